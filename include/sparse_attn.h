@@ -1,0 +1,196 @@
+/*
+ * sparse_attn.h — C ABI of the MI355X (gfx950) block-sparse attention library.
+ *
+ * What it computes.  Multi-head attention in which each head carries a block
+ * mask: rows are Q-blocks, columns are KV-blocks, and only the non-zero
+ * ("dense") entries are computed (db-SP post on load balancing sparse-attention
+ * head and sequence parallelism, scenario 2).  For every live tile the library
+ * runs a flash-attention tile; KV is visited in chunks, each chunk being one
+ * ring-attention step's KV shard, and the per-chunk partial softmax states
+ * (O, m, l) are combined by the online-softmax merge of the 6D-parallel
+ * attention notes, section 2.1.  Work items (one per (batch, head, Q-block))
+ * are ordered by the LPT greedy of the db-SP post so that the persistent
+ * kernel's workgroups carry equal numbers of live tiles.  A second sparsity
+ * kind follows the same notes' section 7.1 (DSA): a rank-r indexer picks the
+ * top-k keys of every query and attention runs over those keys only.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers unless the comment says (host).
+ *  - Q, K, V and O are indexed [b, h, s, d] through the element strides
+ *    sb, sh, ss of sa_problem; d is contiguous (stride 1).  Q, K, V, O share
+ *    one stride set.  bf16 data is IEEE bfloat16, f32 is IEEE binary32.
+ *  - Per-chunk partials are dense fp32: O_part [n][B][H][S][D], m_part and
+ *    l_part [n][B][H][S], where n = chunk_end - chunk_begin.  O_part is the
+ *    UNNORMALISED sum of exp(s - m) v, m is the row max of the scaled scores in
+ *    natural-log units, l = sum exp(s - m).  A row with no live key in a chunk
+ *    gets (O, m, l) = (0, -inf, 0).
+ *  - A row with no live key at all gets O = 0 (and lse = -inf).
+ *  - Every call is asynchronous on the given stream unless stated otherwise;
+ *    no call allocates device memory except sparse_attn_plan.
+ *  - Errors are negative sa_status codes; no C++ exception crosses the ABI.
+ *    Arguments are validated before anything is launched.  On SA_ERR_HIP the
+ *    HIP error text is available from sa_last_error() (thread-local).
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_INVALID = -1,     /* bad pointer, shape, stride or range */
+  SA_ERR_UNSUPPORTED = -2, /* valid request outside the compiled kernel variants */
+  SA_ERR_HIP = -3,         /* a HIP runtime call failed; see sa_last_error() */
+  SA_ERR_NOMEM = -4        /* device or host allocation failed (plan only) */
+} sa_status;
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+typedef enum { SA_ORDER_LPT = 0, SA_ORDER_NAIVE = 1 } sa_order;
+typedef enum { SA_LAYOUT_CONTIGUOUS = 0, SA_LAYOUT_STRIPED = 1 } sa_layout;
+typedef enum { SA_KIND_BLOCK = 0, SA_KIND_TOPK = 1, SA_KIND_INDEX = 2 } sa_kind;
+
+/* Shape of one attention problem (self-attention: Q and KV have length S).
+ *  block     Q-block = KV-block size in tokens.  bf16: 64 or 128; f32: 64.
+ *  D         head dim.  bf16: 64 or 128; f32: 64 or 128.
+ *  n_chunks  number of KV chunks (ring steps).  Contiguous layout: chunk c is
+ *            KV blocks [c*nK/C, (c+1)*nK/C) and nK % C == 0, nK = ceil(S/block);
+ *            the last block may be partial (S % block != 0).  Striped layout
+ *            (striped attention, 6D notes section 2.3): chunk c holds tokens
+ *            j with j % C == c; requires S % (block*C) == 0 and block/C a
+ *            multiple of 32.
+ *  scale     softmax scale; <= 0 selects 1/sqrt(D).
+ *  sb,sh,ss  element strides of the b, h and s axes of Q, K, V and O. */
+typedef struct {
+  int32_t B, H, S, D;
+  int32_t block;
+  int32_t n_chunks;
+  int32_t layout; /* sa_layout */
+  int32_t dtype;  /* sa_dtype */
+  float scale;
+  int32_t pad0;
+  int64_t sb, sh, ss;
+} sa_problem;
+
+/* Sparsity description handed to sparse_attn_plan.
+ *  SA_KIND_BLOCK: mask  uint8 [B][H][nQ][nK], contiguous; non-zero = live.
+ *                 Copied into the plan, so the caller may free it afterwards.
+ *  SA_KIND_TOPK:  q, k  (problem layout and dtype); wq, wk [D][rank] row-major,
+ *                 problem dtype (bf16 only).  The indexer (6D notes, section
+ *                 7.1) computes I = (Q wq)(K wk)^T with the projections rounded
+ *                 to bf16 and fp32 accumulation, and keeps, per query i,
+ *                 min(top_k, #candidates) keys ordered by (I desc, key asc);
+ *                 candidates are j <= i when causal, else all j.  rank == 32.
+ *  SA_KIND_INDEX: idx int32 [B][H][S][top_k] key indices, count int32
+ *                 [B][H][S] (0 <= count <= top_k); copied into the plan.  Every
+ *                 idx[b,h,i,t], t < count, must lie in [0, S) (checked on the
+ *                 host copy; the plan call is synchronous for this kind). */
+typedef struct {
+  int32_t kind; /* sa_kind */
+  int32_t rank, top_k, causal;
+  const uint8_t* mask;
+  const void* q;
+  const void* k;
+  const void* wq;
+  const void* wk;
+  const int32_t* idx;
+  const int32_t* count;
+} sa_sparsity;
+
+typedef struct sa_plan sa_plan; /* opaque; owned by the library */
+
+typedef struct {
+  int32_t kind, num_bins, order, n_chunks;
+  int32_t nQ, nK, n_items, top_k;
+  int64_t total_live;   /* BLOCK: live (Q-block, KV-block) tiles; TOPK/INDEX: selected pairs */
+  int64_t load_sum;     /* sum of the full-range item loads (= total_live for BLOCK) */
+  int64_t makespan;     /* max bin load of the full-range list */
+  int64_t lower_bound;  /* max(max item load, ceil(load_sum / num_bins)) */
+} sa_plan_info;
+
+/* Arrays that sparse_attn_plan_copy can export to host memory. */
+typedef enum {
+  SA_PLAN_ROW = 0,      /* int32 [B][H][nQ]   live tiles per Q-block (mask row sums)      */
+  SA_PLAN_COL = 1,      /* int32 [B][H][nK]   live tiles per KV-block (mask column sums)  */
+  SA_PLAN_CROW = 2,     /* int32 [B][H][C][nQ] per-chunk row counts (striped: = row)      */
+  SA_PLAN_ITEMS = 3,    /* int32 [n_items]    item ids (b*H + h)*nQ + q, bins concatenated */
+  SA_PLAN_BIN_PTR = 4,  /* int32 [num_bins+1] offsets of each bin's list in ITEMS          */
+  SA_PLAN_BIN_LOAD = 5, /* int64 [num_bins]   sum of item loads per bin                    */
+  SA_PLAN_TOPK_IDX = 6, /* int32 [B][H][S][top_k] selected keys (TOPK/INDEX)              */
+  SA_PLAN_TOPK_COUNT = 7 /* int32 [B][H][S]   number of selected keys                     */
+} sa_plan_array;
+
+/* Build a plan.
+ *  BLOCK: counts live tiles per mask row, column and per-chunk row on the GPU
+ *  (row/column sums of the db-SP post, scenario 2), copies the row counts to
+ *  the host and runs the LPT greedy of the same post (longest item to the
+ *  least-loaded bin; ties: lower item id first, lower bin index) — or
+ *  round-robin for SA_ORDER_NAIVE — once over the full chunk range and once
+ *  per chunk; the lists are uploaded for the persistent kernel.  This kind
+ *  synchronises the stream.
+ *  TOPK: runs the indexer and top-k selection on the GPU; asynchronous.
+ *  num_bins: persistent workgroups; 0 picks one per compute unit (two for
+ *  block 64).  out (host): receives the plan.  Returns SA_ERR_NOMEM if the
+ *  plan's device buffers cannot be allocated. */
+sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_t num_bins,
+                           int32_t order, sa_plan** out, hipStream_t stream);
+
+/* Run attention under a plan over KV chunks [chunk_begin, chunk_end).
+ *  Full mode (o != NULL): O = softmax-weighted sum over the live keys of the
+ *  chunk range, normalised, written in the problem dtype through the strides.
+ *  Partial mode (o == NULL): writes one fp32 (O, m, l) partial per chunk of
+ *  the range (see the conventions above); o_part, m_part, l_part must all be
+ *  non-NULL.  This is the ring step's flash_attention of the 6D notes,
+ *  section 2.1.  TOPK/INDEX plans: full mode only, chunk range [0, 1).
+ *  trace (nullable): int64 [n_items_of_list][4] = {start, end, (xcc_id << 32)
+ *  | hw_id, (bin << 32) | item}, timestamps from the 100 MHz real-time clock,
+ *  in list order.  The list is the full-range one, or the chunk's own list
+ *  when the range is a single chunk.  Allocates nothing. */
+sa_status sparse_attn_fwd(const sa_plan* plan, const void* q, const void* k, const void* v,
+                          int32_t chunk_begin, int32_t chunk_end, void* o, float* o_part,
+                          float* m_part, float* l_part, int64_t* trace, hipStream_t stream);
+
+/* Online-softmax merge of n_parts partials (6D notes, section 2.1):
+ *  m_new = max(m_acc, m_p); alpha = exp(m_acc - m_new); beta = exp(m_p - m_new);
+ *  l = alpha*l + beta*l_p; O = alpha*O + beta*O_p; folded in part order, then
+ *  O / l.  Parts with m_p = -inf are the identity and their O_p is not read.
+ *  o_parts, m_parts, l_parts (host arrays of n_parts device pointers): O_p is
+ *  fp32 [rows][D], m_p and l_p fp32 [rows].  o_out: [rows][D] dense in out_dtype.
+ *  lse_out (nullable): fp32 [rows], m + log(l), -inf for empty rows.
+ *  1 <= n_parts <= 64, D in {64, 128}.  Allocates nothing. */
+sa_status chunk_merge(int32_t n_parts, const float* const* o_parts, const float* const* m_parts,
+                      const float* const* l_parts, int64_t rows, int32_t D, void* o_out,
+                      int32_t out_dtype, float* lse_out, hipStream_t stream);
+
+/* Summary of a plan (host output). */
+sa_status sparse_attn_plan_info(const sa_plan* plan, sa_plan_info* out);
+
+/* Copy one of the plan's arrays to host memory dst (n_elems elements of the
+ * array's type).  chunk selects the list for ITEMS / BIN_PTR / BIN_LOAD: -1 is
+ * the full-range list, c in [0, C) the list of chunk c.  Synchronous. */
+sa_status sparse_attn_plan_copy(const sa_plan* plan, int32_t what, int32_t chunk, void* dst,
+                                int64_t n_elems);
+
+/* Host-only LPT / round-robin assignment, the same code the plan uses.
+ *  loads (host) [n] non-negative; items_out (host) [n]; bin_ptr_out (host)
+ *  [m+1]; bin_load_out (host, nullable) [m].  Touches no GPU. */
+sa_status sparse_attn_assign_host(const int64_t* loads, int32_t n, int32_t m, int32_t order,
+                                  int32_t* items_out, int32_t* bin_ptr_out, int64_t* bin_load_out);
+
+/* Free a plan.  Synchronises the device first.  NULL is a no-op. */
+void sparse_attn_plan_destroy(sa_plan* plan);
+
+/* Static description of a status code. */
+const char* sa_status_string(int32_t status);
+
+/* Text of the last error raised on this thread ("" if none). */
+const char* sa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,173 @@
+"""Oracle: block-masked attention, per-chunk partials and the online-softmax merge.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  fp64 numpy, no blocking
+beyond processing one Q-block of rows at a time to bound memory.
+
+Definitions followed:
+
+* Masked attention (the result the block-sparse method must reach exactly):
+  ``O[i] = sum_j softmax_j(s_ij) v_j`` with ``s_ij = scale * <q_i, k_j>`` when
+  ``mask[floor(i / block), floor(j / block)]`` is non-zero and ``-inf``
+  otherwise; ``scale = 1 / sqrt(d)``.  Rows are Q-blocks and columns KV-blocks
+  (db-SP post, scenario 2 bullets).  A row with no live key gets O = 0 and
+  lse = -inf.
+* Per-chunk partial = the ring step's ``flash_attention(Q, K, V) -> (O_step,
+  m_step, l_step)`` of the 6D-parallel notes, section 2.1: ``m`` is the row max
+  of the live scores in the chunk, ``l = sum exp(s - m)`` and ``O`` is the
+  UNNORMALISED ``sum exp(s - m) v`` (the pseudocode marks the accumulator as
+  unnormalised and divides once at the end).  Rows with no live key in the
+  chunk give ``(O, m, l) = (0, -inf, 0)``.
+* Merge = the same section's online-softmax update, folded over the partials
+  in order, with the multiplication signs that the page lost restored:
+  ``m_new = max(m_acc, m_step)``, ``alpha = exp(m_acc - m_new)``,
+  ``beta = exp(m_step - m_new)``, ``l = alpha*l + beta*l_step``,
+  ``O = alpha*O + beta*O_step``; the result is ``O_acc / l_acc``.  The page is
+  silent on rows where both maxima are -inf; there ``alpha = beta = 0`` so the
+  state stays ``(0, -inf, 0)``.
+* Chunk composition: contiguous chunk c holds KV blocks
+  ``[c*nK/C, (c+1)*nK/C)``; striped chunk c holds tokens ``j`` with
+  ``j mod C == c`` (section 2.3's striped attention, "token i -> chunk i mod C").
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def chunk_token_ids(S: int, block: int, n_chunks: int, layout: str, c: int) -> np.ndarray:
+    """KV token indices that form chunk ``c``."""
+    if layout == "contiguous":
+        nK = -(-S // block)
+        per = nK // n_chunks
+        lo = c * per * block
+        hi = min(S, (c + 1) * per * block)
+        return np.arange(lo, hi)
+    if layout == "striped":
+        return np.arange(c, S, n_chunks)
+    raise ValueError(layout)
+
+
+def _key_live(mask_row: np.ndarray, block: int, S: int) -> np.ndarray:
+    """Token-level liveness of every key for one Q-block's mask row."""
+    return np.repeat(mask_row != 0, block)[:S]
+
+
+def masked_attention(q, k, v, mask, block: int, scale: Optional[float] = None,
+                     rows: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """Dense softmax attention with dead (Q-block, KV-block) tiles set to -inf.
+
+    q, k, v: [B, H, S, D]; mask: [B, H, nQ, nK].  Returns ``(O, lse)`` in fp64,
+    shaped [B, H, S, D] / [B, H, S], or [len(rows), D] / [len(rows)] when ``rows``
+    (a list of (b, h, token)) selects individual output rows.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, S, D = q.shape
+    sc = default_scale(D) if scale is None else float(scale)
+    if rows is not None:
+        out = np.zeros((len(rows), D))
+        lse = np.full(len(rows), NEG_INF)
+        for n, (b, h, i) in enumerate(rows):
+            live = _key_live(mask[b, h, i // block], block, S)
+            if not live.any():
+                continue
+            s = sc * (k[b, h][live] @ q[b, h, i])
+            m = s.max()
+            p = np.exp(s - m)
+            out[n] = (p @ v[b, h][live]) / p.sum()
+            lse[n] = m + math.log(p.sum())
+        return out, lse
+    out = np.zeros((B, H, S, D))
+    lse = np.full((B, H, S), NEG_INF)
+    nQ = -(-S // block)
+    for b in range(B):
+        for h in range(H):
+            for qi in range(nQ):
+                r0, r1 = qi * block, min(S, (qi + 1) * block)
+                live = _key_live(mask[b, h, qi], block, S)
+                if not live.any():
+                    continue
+                s = sc * (q[b, h, r0:r1] @ k[b, h][live].T)
+                m = s.max(axis=1, keepdims=True)
+                p = np.exp(s - m)
+                l = p.sum(axis=1, keepdims=True)
+                out[b, h, r0:r1] = (p @ v[b, h][live]) / l
+                lse[b, h, r0:r1] = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def chunk_partial(q, k, v, mask, block: int, n_chunks: int, layout: str, c: int,
+                  scale: Optional[float] = None):
+    """One ring step's partial ``(O_unnormalised, m, l)`` over the KV tokens of chunk ``c``.
+
+    Shapes: O [B, H, S, D], m and l [B, H, S], fp64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, S, D = q.shape
+    sc = default_scale(D) if scale is None else float(scale)
+    toks = chunk_token_ids(S, block, n_chunks, layout, c)
+    O = np.zeros((B, H, S, D))
+    M = np.full((B, H, S), NEG_INF)
+    L = np.zeros((B, H, S))
+    nQ = -(-S // block)
+    for b in range(B):
+        for h in range(H):
+            for qi in range(nQ):
+                r0, r1 = qi * block, min(S, (qi + 1) * block)
+                live = _key_live(mask[b, h, qi], block, S)[toks]
+                if not live.any():
+                    continue
+                kt = toks[live]
+                s = sc * (q[b, h, r0:r1] @ k[b, h, kt].T)
+                m = s.max(axis=1, keepdims=True)
+                p = np.exp(s - m)
+                O[b, h, r0:r1] = p @ v[b, h, kt]
+                M[b, h, r0:r1] = m[:, 0]
+                L[b, h, r0:r1] = p.sum(axis=1)
+    return O, M, L
+
+
+def merge(parts: List[Tuple[np.ndarray, np.ndarray, np.ndarray]]):
+    """Fold per-chunk partials ``[(O, m, l), ...]`` with the online-softmax update.
+
+    O: [..., D]; m, l: [...].  Returns ``(O_normalised, lse)``; rows whose every
+    partial is empty give O = 0 and lse = -inf.
+    """
+    O0, m0, _ = parts[0]
+    O_acc = np.zeros(np.shape(O0))
+    m_acc = np.full(np.shape(m0), NEG_INF)
+    l_acc = np.zeros(np.shape(m0))
+    for O_step, m_step, l_step in parts:
+        O_step, m_step, l_step = _f64(O_step), _f64(m_step), _f64(l_step)
+        m_new = np.maximum(m_acc, m_step)
+        empty = np.isneginf(m_new)  # both sides empty: alpha = beta = 0
+        m_ref = np.where(empty, 0.0, m_new)
+        alpha = np.where(empty, 0.0, np.exp(m_acc - m_ref))  # exp(-inf) = 0
+        beta = np.where(empty, 0.0, np.exp(m_step - m_ref))
+        l_acc = alpha * l_acc + beta * l_step
+        O_acc = alpha[..., None] * O_acc + beta[..., None] * O_step
+        m_acc = m_new
+    pos = l_acc > 0
+    O = np.where(pos[..., None], O_acc / np.where(pos, l_acc, 1.0)[..., None], 0.0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(pos, m_acc + np.log(np.where(pos, l_acc, 1.0)), NEG_INF)
+    return O, lse
+
+
+def chunked_attention(q, k, v, mask, block: int, n_chunks: int, layout: str,
+                      scale: Optional[float] = None):
+    """The ring emulation on one device: every chunk's partial, then the merge."""
+    parts = [chunk_partial(q, k, v, mask, block, n_chunks, layout, c, scale)
+             for c in range(n_chunks)]
+    return merge(parts)

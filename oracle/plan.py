@@ -1,0 +1,130 @@
+"""Oracle: block-mask popcounts, LPT / naive work assignment, brute force, ring step table.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Pure Python / numpy
+integer arithmetic.
+
+Definitions followed (db-SP post, "load balancing of sparse-attention head
+parallelism and sequence parallelism"):
+
+* Scenario 2 bullets: with the block mask's rows as Q-blocks and columns as
+  KV-blocks, a Q-block's work is its row sum and a KV-block's its column sum.
+* LPT paragraph: repeatedly hand the longest remaining job to the machine that
+  is currently least loaded (identical-machines scheduling, makespan
+  objective).  The page leaves ties open; the readings used here are
+  (i) jobs sorted by load descending, then job id ascending; (ii) among
+  equally loaded machines the lowest index wins; (iii) a machine runs its jobs
+  in the order they were given to it.  Reading (ii) is the one the page's own
+  example needs: [8,7,6,5,4] on two machines must print [8+5+4, 7+6], so the
+  final 4 meets a 13/13 tie and goes to machine 0.
+* Per-chunk work ("crow"): a chunk is one ring step's KV shard (6D-parallel
+  notes, section 2.1).  Contiguous chunk c covers KV blocks
+  [c*nK/C, (c+1)*nK/C), so crow counts the row's live blocks in that range.
+  Striped chunk c takes tokens j with j mod C == c (section 2.3), so every KV
+  block lends block/C tokens to every chunk and crow[c] equals the full row
+  count, in units of (block/C)-key groups.
+* Ring step table (section 2.3, causal ring skipping): step (r, c) pairs query
+  shard r with KV chunk c; query shards follow the same layout rule as the KV
+  chunks.  Entry = number of live (query token, key token) pairs.
+"""
+from __future__ import annotations
+
+import itertools
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+
+def popcount(mask: np.ndarray, n_chunks: int, layout: str = "contiguous") -> Dict[str, np.ndarray]:
+    """Row, column and per-chunk row counts of a [B, H, nQ, nK] block mask."""
+    live = (np.asarray(mask) != 0).astype(np.int64)
+    B, H, nQ, nK = live.shape
+    row = live.sum(axis=3)
+    col = live.sum(axis=2)
+    crow = np.zeros((B, H, n_chunks, nQ), dtype=np.int64)
+    if layout == "contiguous":
+        per = nK // n_chunks
+        for c in range(n_chunks):
+            crow[:, :, c, :] = live[:, :, :, c * per:(c + 1) * per].sum(axis=3)
+    elif layout == "striped":
+        for c in range(n_chunks):
+            crow[:, :, c, :] = row
+    else:
+        raise ValueError(layout)
+    return {"row": row, "col": col, "crow": crow, "total": int(live.sum())}
+
+
+def lpt(loads: Sequence[int], m: int) -> Tuple[List[List[int]], List[int]]:
+    """Longest-processing-time-first greedy onto ``m`` identical machines.
+
+    Returns (per-machine job lists in assignment order, per-machine loads).
+    """
+    order = sorted(range(len(loads)), key=lambda i: (-int(loads[i]), i))
+    bins: List[List[int]] = [[] for _ in range(m)]
+    bin_load = [0] * m
+    for job in order:
+        target = 0
+        for b in range(1, m):
+            if bin_load[b] < bin_load[target]:
+                target = b
+        bins[target].append(job)
+        bin_load[target] += int(loads[job])
+    return bins, bin_load
+
+
+def naive(loads: Sequence[int], m: int) -> Tuple[List[List[int]], List[int]]:
+    """Round-robin in job-id order: job i runs on machine i mod m."""
+    bins: List[List[int]] = [[] for _ in range(m)]
+    bin_load = [0] * m
+    for i, p in enumerate(loads):
+        bins[i % m].append(i)
+        bin_load[i % m] += int(p)
+    return bins, bin_load
+
+
+def brute_force_makespan(loads: Sequence[int], m: int) -> Tuple[int, Tuple[int, ...]]:
+    """Optimal makespan by trying every one of the m**n assignments (tiny inputs only)."""
+    best, best_assign = None, None
+    for assign in itertools.product(range(m), repeat=len(loads)):
+        tot = [0] * m
+        for job, b in enumerate(assign):
+            tot[b] += int(loads[job])
+        span = max(tot)
+        if best is None or span < best:
+            best, best_assign = span, assign
+    return best, best_assign
+
+
+def plan_items(row_loads: np.ndarray, m: int, order: str = "lpt") -> Dict[str, np.ndarray]:
+    """Assign every (b, h, q) item (id = (b*H + h)*nQ + q, load = row count) to m bins.
+
+    Returns ``items`` (all bins' lists concatenated), ``bin_ptr`` (m + 1 offsets),
+    ``bin_load`` and ``makespan``.
+    """
+    loads = np.asarray(row_loads, dtype=np.int64).reshape(-1).tolist()
+    bins, bin_load = (lpt if order == "lpt" else naive)(loads, m)
+    items, ptr = [], [0]
+    for b in bins:
+        items.extend(b)
+        ptr.append(len(items))
+    return {"items": np.array(items, dtype=np.int64), "bin_ptr": np.array(ptr, dtype=np.int64),
+            "bin_load": np.array(bin_load, dtype=np.int64), "makespan": int(max(bin_load))}
+
+
+def _tokens_per_block_in_part(S: int, block: int, n_parts: int, layout: str) -> np.ndarray:
+    """[n_parts, nBlocks] count of a block's tokens that fall in each shard / chunk."""
+    nb = -(-S // block)
+    cnt = np.zeros((n_parts, nb), dtype=np.int64)
+    per = nb // n_parts
+    for t in range(S):
+        blk = t // block
+        part = (blk // per) if layout == "contiguous" else (t % n_parts)
+        cnt[part, blk] += 1
+    return cnt
+
+
+def step_table(mask: np.ndarray, S: int, block: int, n_chunks: int, layout: str) -> np.ndarray:
+    """[B, H, C, C] live token pairs of ring step (query shard r, KV chunk c)."""
+    live = (np.asarray(mask) != 0).astype(np.int64)
+    cnt = _tokens_per_block_in_part(S, block, n_chunks, layout)
+    # pairs[r, c] = sum_i sum_j cnt[r, i] * live[i, j] * cnt[c, j]
+    return np.einsum("ri,bhij,cj->bhrc", cnt, live, cnt)

@@ -1,0 +1,159 @@
+"""Pins of oracle.attention against library routines, brute force and invariants.
+
+Independent references used here:
+* torch.nn.functional.scaled_dot_product_attention on the CPU in float64 (a library
+  routine; with an all-ones block mask the masked attention must equal plain dense
+  attention, and with any mask it must equal SDPA under the token mask expanded from
+  the tiles);
+* a pure-Python triple loop with math.exp on tiny inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from sparse_mask_load_amd import workloads as W
+
+
+def _sdpa(q, k, v, token_mask=None, is_causal=False):
+    t = lambda x: torch.from_numpy(np.asarray(x, np.float64))
+    m = None if token_mask is None else torch.from_numpy(token_mask)
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=m, is_causal=is_causal).numpy()
+
+
+def _token_mask(mask_bh, block, S):
+    return np.repeat(np.repeat(mask_bh != 0, block, axis=0), block, axis=1)[:S, :S]
+
+
+def test_all_ones_mask_is_dense_attention():
+    w = W.make_custom(1, 3, 192, 64, block=64, pattern="ones", dtype="f32", seed=5)
+    O, lse = A.masked_attention(w.q, w.k, w.v, w.mask, w.block)
+    ref = _sdpa(w.q, w.k, w.v)
+    assert np.abs(O - ref).max() < 1e-12
+    # lse against logsumexp computed directly
+    s = np.einsum("bhid,bhjd->bhij", w.q.astype(np.float64), w.k.astype(np.float64)) / 8.0
+    mx = s.max(-1)
+    assert np.abs(lse - (mx + np.log(np.exp(s - mx[..., None]).sum(-1)))).max() < 1e-12
+
+
+@pytest.mark.parametrize("pattern,S,block", [("bernoulli", 256, 64), ("causal", 256, 32),
+                                             ("bernoulli", 200, 64)])
+def test_masked_attention_equals_sdpa_with_expanded_mask(pattern, S, block):
+    w = W.make_custom(2, 2, S, 32, block=block, pattern=pattern, density=0.4, dtype="f32", seed=11)
+    O, _ = A.masked_attention(w.q, w.k, w.v, w.mask, w.block)
+    for b in range(2):
+        for h in range(2):
+            tm = _token_mask(w.mask[b, h], block, S)
+            ref = _sdpa(w.q[b, h], w.k[b, h], w.v[b, h], token_mask=tm)
+            assert np.abs(O[b, h] - ref).max() < 1e-12
+
+
+def test_block_causal_equals_token_causal_on_block_diagonal_granularity():
+    # block size 1 turns the block-causal mask into the ordinary token causal mask
+    w = W.make_custom(1, 2, 48, 16, block=1, pattern="causal", dtype="f32", seed=2)
+    O, _ = A.masked_attention(w.q, w.k, w.v, w.mask, 1)
+    ref = _sdpa(w.q, w.k, w.v, is_causal=True)
+    assert np.abs(O - ref).max() < 1e-12
+
+
+def test_pure_python_loops_tiny():
+    w = W.make_custom(1, 2, 24, 4, block=8, pattern="bernoulli", density=0.5, dtype="f32", seed=9)
+    O, lse = A.masked_attention(w.q, w.k, w.v, w.mask, w.block)
+    scale = 1.0 / math.sqrt(4)
+    for h in range(2):
+        for i in range(24):
+            live = [j for j in range(24) if w.mask[0, h, i // 8, j // 8]]
+            s = [scale * sum(float(w.q[0, h, i, d]) * float(w.k[0, h, j, d]) for d in range(4))
+                 for j in live]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            tot = sum(e)
+            for d in range(4):
+                ref = sum(e[n] * float(w.v[0, h, j, d]) for n, j in enumerate(live)) / tot
+                assert abs(O[0, h, i, d] - ref) < 1e-12
+            assert abs(lse[0, h, i] - (m + math.log(tot))) < 1e-12
+
+
+def test_empty_rows_give_zero_output():
+    w = W.make_custom(1, 1, 128, 16, block=32, pattern="empty", dtype="f32")
+    O, lse = A.masked_attention(w.q, w.k, w.v, w.mask, 32)
+    assert (O == 0).all() and np.isneginf(lse).all()
+
+
+def test_mask_sensitivity():
+    w = W.make_custom(1, 1, 256, 32, block=64, pattern="ones", dtype="bf16", seed=4)
+    O, _ = A.masked_attention(w.q, w.k, w.v, w.mask, 64)
+    m2 = w.mask.copy()
+    m2[0, 0, 2, 1] = 0
+    O2, _ = A.masked_attention(w.q, w.k, w.v, m2, 64)
+    assert np.abs(O2[0, 0, 128:192] - O[0, 0, 128:192]).max() > 2e-2
+    assert np.abs(O2[0, 0, :128] - O[0, 0, :128]).max() == 0
+
+
+def test_row_sampling_matches_full():
+    w = W.make_custom(1, 2, 320, 32, block=64, pattern="bernoulli", density=0.3, dtype="f32", seed=1)
+    O, lse = A.masked_attention(w.q, w.k, w.v, w.mask, 64)
+    rows = [(0, 0, 0), (0, 1, 319), (0, 1, 130), (0, 0, 64)]
+    Os, ls = A.masked_attention(w.q, w.k, w.v, w.mask, 64, rows=rows)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.abs(Os[n] - O[b, h, i]).max() < 1e-13 and abs(ls[n] - lse[b, h, i]) < 1e-12
+
+
+@pytest.mark.parametrize("C", [1, 2, 4, 8])
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_chunked_merge_equals_unchunked(C, layout):
+    S = 512
+    w = W.make_custom(1, 2, S, 32, block=32, pattern="bernoulli", density=0.35, dtype="f32",
+                      seed=C, layout=layout)
+    ref, ref_lse = A.masked_attention(w.q, w.k, w.v, w.mask, 32)
+    O, lse = A.chunked_attention(w.q, w.k, w.v, w.mask, 32, C, layout)
+    assert np.abs(O - ref).max() < 1e-12
+    fin = np.isfinite(ref_lse)
+    assert np.abs(lse[fin] - ref_lse[fin]).max() < 1e-12
+
+
+def test_causal_contiguous_chunks_have_empty_rows_and_merge_handles_them():
+    w = W.make_custom(1, 1, 256, 16, block=32, pattern="causal", dtype="f32", seed=3)
+    parts = [A.chunk_partial(w.q, w.k, w.v, w.mask, 32, 4, "contiguous", c) for c in range(4)]
+    # query rows in the first quarter have no key in the last chunk: (0, -inf, 0)
+    O3, m3, l3 = parts[3]
+    assert np.isneginf(m3[0, 0, :64]).all() and (l3[0, 0, :64] == 0).all() and (O3[0, 0, :64] == 0).all()
+    O, _ = A.merge(parts)
+    ref, _ = A.masked_attention(w.q, w.k, w.v, w.mask, 32)
+    assert np.abs(O - ref).max() < 1e-12
+
+
+def test_merge_associative_and_order_free_and_identity():
+    w = W.make_custom(1, 2, 256, 16, block=32, pattern="bernoulli", density=0.5, dtype="f32", seed=8)
+    parts = [A.chunk_partial(w.q, w.k, w.v, w.mask, 32, 4, "contiguous", c) for c in range(4)]
+    full, full_lse = A.merge(parts)
+    # associativity: a normalised result with l = 1 and m = lse is itself a valid partial
+    left, left_lse = A.merge(parts[:2])
+    regrouped = [(left, left_lse, np.where(np.isneginf(left_lse), 0.0, 1.0))] + parts[2:]
+    O2, _ = A.merge(regrouped)
+    assert np.abs(O2 - full).max() < 1e-12
+    O3, _ = A.merge(parts[::-1])
+    assert np.abs(O3 - full).max() < 1e-12
+    empty = (np.zeros_like(parts[0][0]), np.full_like(parts[0][1], -np.inf), np.zeros_like(parts[0][2]))
+    O4, lse4 = A.merge(parts + [empty])
+    assert np.abs(O4 - full).max() == 0 and np.array_equal(lse4, full_lse)
+    O5, lse5 = A.merge([empty, empty])
+    assert (O5 == 0).all() and np.isneginf(lse5).all()
+
+
+def test_striped_equals_contiguous_result():
+    w = W.make_custom(1, 2, 512, 32, block=128, pattern="causal", dtype="f32", seed=6)
+    Oc, _ = A.chunked_attention(w.q, w.k, w.v, w.mask, 128, 4, "contiguous")
+    Os, _ = A.chunked_attention(w.q, w.k, w.v, w.mask, 128, 4, "striped")
+    assert np.abs(Oc - Os).max() < 1e-12
+
+
+def test_chunk_token_sets_partition_the_sequence():
+    for layout in ("contiguous", "striped"):
+        toks = np.concatenate([A.chunk_token_ids(1024, 128, 4, layout, c) for c in range(4)])
+        assert sorted(toks.tolist()) == list(range(1024))
+    assert A.chunk_token_ids(1024, 128, 4, "striped", 1)[:3].tolist() == [1, 5, 9]
+    assert A.chunk_token_ids(1024, 128, 4, "contiguous", 1)[[0, -1]].tolist() == [256, 511]

@@ -1,0 +1,176 @@
+"""Pins of oracle.plan: popcounts, LPT, naive order, brute force, ring step table."""
+import itertools
+import random
+
+import numpy as np
+import pytest
+
+from oracle import plan as P
+from sparse_mask_load_amd import workloads as W
+
+
+def _parse_partition(text):
+    return [sorted((int(x) for x in part.split()), reverse=True) for part in text.split("|")]
+
+
+def test_lpt_counter_example_from_page(golden):
+    g = golden("lpt_counter_example.txt")
+    loads = [int(x) for x in g["loads"].split()]
+    m = int(g["machines"])
+    bins, bin_load = P.lpt(loads, m)
+    got = [sorted((loads[j] for j in b), reverse=True) for b in bins]
+    assert got == _parse_partition(g["lpt_partition"])
+    assert max(bin_load) == int(g["lpt_makespan"])
+    opt, assign = P.brute_force_makespan(loads, m)
+    assert opt == int(g["opt_makespan"])
+    parts = [sorted((loads[j] for j in range(len(loads)) if assign[j] == b), reverse=True)
+             for b in range(m)]
+    assert sorted(parts) == sorted(_parse_partition(g["opt_partition"]))
+
+
+def test_lpt_within_worst_case_bound(golden):
+    g = golden("lpt_bound.txt")
+    assert g["bound_numerator"] == "4m-1" and g["bound_denominator"] == "3m"
+    rng = random.Random(1234)
+    worst = {}
+    for trial in range(400):
+        m = rng.randint(2, 3)
+        n = rng.randint(1, 8 if m == 2 else 7)
+        loads = [rng.randint(0, 12) for _ in range(n)]
+        _, bl = P.lpt(loads, m)
+        opt, _ = P.brute_force_makespan(loads, m)
+        if opt == 0:
+            assert max(bl) == 0
+            continue
+        ratio = max(bl) / opt
+        assert ratio <= (4 * m - 1) / (3 * m) + 1e-12, (loads, m)
+        worst[m] = max(worst.get(m, 1.0), ratio)
+    assert worst[2] >= 1.0
+
+
+@pytest.mark.parametrize("m,loads,lpt_span,opt_span", [
+    # Graham's tight instances for the LPT bound (textbook, Graham 1969): 2m+1 jobs.
+    (2, [3, 3, 2, 2, 2], 7, 6),
+    (3, [5, 5, 4, 4, 3, 3, 3], 11, 9),
+])
+def test_lpt_reaches_bound_on_tight_instances(m, loads, lpt_span, opt_span):
+    _, bl = P.lpt(loads, m)
+    opt, _ = P.brute_force_makespan(loads, m)
+    assert max(bl) == lpt_span and opt == opt_span
+    assert max(bl) * 3 * m == opt * (4 * m - 1)
+
+
+def test_lpt_tie_rules():
+    # equal loads: item ids ascending go to bins 0, 1, 2, ...; then back to the lowest bin
+    bins, bl = P.lpt([5, 5, 5, 5, 5], 3)
+    assert bins == [[0, 3], [1, 4], [2]] and bl == [10, 10, 5]
+    # zero loads are still placed (they go to the least-loaded bins)
+    bins, bl = P.lpt([0, 4, 0], 2)
+    assert bins == [[1], [0, 2]] and bl == [4, 0]
+
+
+def test_lpt_is_list_scheduling_of_sorted_jobs():
+    # Invariant: every job lands on a bin whose load, just before it, was minimal.
+    rng = np.random.default_rng(7)
+    loads = rng.integers(0, 50, size=300).tolist()
+    m = 17
+    bins, bl = P.lpt(loads, m)
+    where = {j: b for b, lst in enumerate(bins) for j in lst}
+    order = sorted(range(len(loads)), key=lambda i: (-loads[i], i))
+    cur = [0] * m
+    for j in order:
+        b = where[j]
+        assert cur[b] == min(cur)
+        assert b == cur.index(min(cur))
+        cur[b] += loads[j]
+    assert cur == bl
+    assert sorted(j for lst in bins for j in lst) == list(range(len(loads)))
+
+
+def test_naive_round_robin():
+    bins, bl = P.naive([1, 2, 3, 4, 5, 6, 7], 3)
+    assert bins == [[0, 3, 6], [1, 4], [2, 5]] and bl == [12, 7, 9]
+
+
+def _brute_counts(mask, n_chunks, layout):
+    B, H, nQ, nK = mask.shape
+    row = np.zeros((B, H, nQ), int)
+    col = np.zeros((B, H, nK), int)
+    crow = np.zeros((B, H, n_chunks, nQ), int)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nQ):
+                for j in range(nK):
+                    if mask[b, h, i, j]:
+                        row[b, h, i] += 1
+                        col[b, h, j] += 1
+                        if layout == "contiguous":
+                            crow[b, h, j // (nK // n_chunks), i] += 1
+                        else:
+                            for c in range(n_chunks):
+                                crow[b, h, c, i] += 1
+    return row, col, crow
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_popcount_brute_force(layout):
+    rng = np.random.default_rng(3)
+    mask = (rng.random((2, 3, 8, 8)) < 0.4).astype(np.uint8) * rng.integers(1, 255, (2, 3, 8, 8)).astype(np.uint8)
+    cnt = P.popcount(mask, 4, layout)
+    row, col, crow = _brute_counts(mask, 4, layout)
+    assert (cnt["row"] == row).all() and (cnt["col"] == col).all() and (cnt["crow"] == crow).all()
+    assert cnt["total"] == row.sum() == col.sum()
+
+
+def test_popcount_row_and_column_sums_4x4():
+    # db-SP scenario 2 uses a 4x4 mask: Q-block load = row sum, KV-block load = column sum
+    # (values below counted by hand).
+    mask = np.array([[[[1, 0, 0, 0], [1, 1, 0, 0], [0, 1, 1, 0], [1, 1, 1, 1]]]], np.uint8)
+    cnt = P.popcount(mask, 2)
+    assert cnt["row"][0, 0].tolist() == [1, 2, 2, 4]
+    assert cnt["col"][0, 0].tolist() == [3, 3, 2, 1]
+    assert cnt["crow"][0, 0].tolist() == [[1, 2, 1, 2], [0, 0, 1, 2]]
+
+
+def test_workload_tile_counts():
+    w2 = W.make(2, with_data=False)
+    cnt = P.popcount(w2.mask, 4)
+    # frame band: 4 rows per frame x (14 frames x 12 live blocks + 2 edge frames x 8) = 736
+    assert (cnt["row"][0, :12].sum(axis=1) == 736).all()
+    assert (np.diagonal(w2.mask[0, 12:], axis1=1, axis2=2) == 1).all()
+    w3 = W.make(3, with_data=False)
+    cnt3 = P.popcount(w3.mask, 4)
+    assert (cnt3["row"].sum(axis=2) == 128 * 129 // 2).all() and cnt3["total"] == 132096
+    # per-chunk work of contiguous causal chunks: 3600 / 2576 / 1552 / 528 tiles per head
+    assert cnt3["crow"][0, 0].sum(axis=1).tolist() == [3600, 2576, 1552, 528]
+
+
+def test_ring_step_table_matches_page(golden):
+    g = golden("causal_ring_steps.txt")
+    cp = int(g["cp"])
+    w3 = W.make(3, with_data=False)
+    tab = P.step_table(w3.mask[:, :1], w3.S, w3.block, cp, "contiguous")[0, 0]
+    nonzero = tab > 0
+    assert nonzero.size == int(g["steps_total"])
+    assert int(nonzero.sum()) == int(g["steps_with_work"])
+    assert nonzero.sum(axis=1).tolist() == [int(x) for x in g["steps_per_gpu"].split()]
+    assert 100.0 * nonzero.sum() / nonzero.size == float(g["fraction_percent"])
+    assert 100.0 - 100.0 * nonzero.sum() / nonzero.size == float(g["saved_percent"])
+    # striped: every step has work and the causal work is balanced
+    tab_s = P.step_table(w3.mask[:, :1], w3.S, w3.block, cp, "striped")[0, 0]
+    assert (tab_s > 0).all()
+    assert len(set(tab_s.ravel().tolist())) == 1
+    assert tab_s.sum() == tab.sum() == 8256 * 128 * 128
+    # imbalance of the contiguous per-GPU work vs the striped one
+    assert tab.sum(axis=1).max() > tab.sum(axis=1).min() * 2
+    assert tab_s.sum(axis=1).max() == tab_s.sum(axis=1).min()
+
+
+def test_plan_items_ids_and_ptrs():
+    row = np.array([[[3, 1, 2], [0, 5, 1]]])  # B=1, H=2, nQ=3
+    out = P.plan_items(row, 2, "lpt")
+    assert out["bin_ptr"].tolist()[0] == 0 and out["bin_ptr"][-1] == 6
+    assert sorted(out["items"].tolist()) == list(range(6))
+    assert out["makespan"] == max(out["bin_load"]) == 6
+    # item id = (b*H + h)*nQ + q; LPT order: 4(5), 0(3), 2(2), 1(1), 5(1), 3(0)
+    assert out["items"].tolist() == [4, 1, 3, 0, 2, 5]
