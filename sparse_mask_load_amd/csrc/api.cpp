@@ -1,0 +1,425 @@
+// Host side of the C ABI: validation, the plan object, launches, error mapping.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "sparse_attn.h"
+
+struct sa_plan {
+  sa_problem prob{};
+  int32_t kind = SA_KIND_BLOCK;
+  int32_t num_bins = 0;
+  int32_t order = SA_ORDER_LPT;
+  int32_t nQ = 0, nK = 0, n_items = 0, top_k = 0, rank = 0, causal = 0;
+  int device = 0;
+  // BLOCK
+  uint8_t* d_mask = nullptr;         // [B][H][nQ][nK] copy of the caller's mask
+  int32_t* d_row = nullptr;          // [B*H*nQ]
+  int32_t* d_col = nullptr;          // [B*H*nK]
+  int32_t* d_crow = nullptr;         // [B*H*C*nQ]
+  unsigned long long* d_total = nullptr;
+  int32_t* d_items = nullptr;        // [(C+1)][n_items]: list 0 = full range, list 1+c = chunk c
+  int32_t* d_bin_ptr = nullptr;      // [(C+1)][num_bins+1]
+  std::vector<int32_t> h_items, h_bin_ptr;
+  std::vector<int64_t> h_bin_load;   // [(C+1)][num_bins]
+  int64_t total_live = 0, load_sum = 0, makespan = 0, lower_bound = 0;
+  // TOPK / INDEX
+  int32_t* d_idx = nullptr;          // [B][H][S][top_k]
+  int32_t* d_count = nullptr;        // [B][H][S]
+  __bf16* d_qp = nullptr;            // [B][H][S][rank]
+  __bf16* d_kp = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sa_status fail(sa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sa_status hip_fail(hipError_t e, const char* what) {
+  return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define SA_HIP(call)                                   \
+  do {                                                 \
+    hipError_t e_ = (call);                            \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);  \
+  } while (0)
+
+int max_tiles_per_row(int block) { return block >= 128 ? sa::kMaxTilesPerRow : sa::kMaxTilesPerRow / 2; }
+
+sa_status validate_problem(const sa_problem* p, bool block_kind) {
+  if (!p) return fail(SA_ERR_INVALID, "problem is NULL");
+  if (p->B <= 0 || p->H <= 0 || p->S <= 0 || p->D <= 0)
+    return fail(SA_ERR_INVALID, "B, H, S, D must be positive (got %d, %d, %d, %d)", p->B, p->H, p->S, p->D);
+  if (p->dtype != SA_F32 && p->dtype != SA_BF16) return fail(SA_ERR_INVALID, "unknown dtype %d", p->dtype);
+  if (p->D != 64 && p->D != 128) return fail(SA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", p->D);
+  if (p->sb <= 0 || p->sh <= 0 || p->ss < p->D)
+    return fail(SA_ERR_INVALID, "strides must be positive with ss >= D (got %lld, %lld, %lld)",
+                (long long)p->sb, (long long)p->sh, (long long)p->ss);
+  if ((p->ss % 8) || (p->sh % 8) || (p->sb % 8))
+    return fail(SA_ERR_UNSUPPORTED, "strides must be multiples of 8 elements (16-byte rows)");
+  if (!block_kind) return SA_OK;
+  if (p->dtype == SA_BF16 && p->block != 64 && p->block != 128)
+    return fail(SA_ERR_UNSUPPORTED, "bf16 block %d (supported: 64, 128)", p->block);
+  if (p->dtype == SA_F32 && p->block != 64)
+    return fail(SA_ERR_UNSUPPORTED, "f32 block %d (supported: 64)", p->block);
+  const int nK = (p->S + p->block - 1) / p->block;
+  if (nK > max_tiles_per_row(p->block))
+    return fail(SA_ERR_UNSUPPORTED, "S/block = %d exceeds %d tiles per row", nK, max_tiles_per_row(p->block));
+  if (p->n_chunks < 1 || p->n_chunks > sa::kMaxChunks)
+    return fail(SA_ERR_INVALID, "n_chunks %d outside [1, %d]", p->n_chunks, sa::kMaxChunks);
+  if (nK % p->n_chunks) return fail(SA_ERR_INVALID, "nK = %d not divisible by n_chunks %d", nK, p->n_chunks);
+  if (p->layout == SA_LAYOUT_STRIPED) {
+    if (p->S % (p->block * p->n_chunks))
+      return fail(SA_ERR_INVALID, "striped layout needs S %% (block * n_chunks) == 0");
+    if ((p->block / p->n_chunks) % 32 || p->block % p->n_chunks)
+      return fail(SA_ERR_UNSUPPORTED, "striped layout needs block / n_chunks to be a multiple of 32");
+  } else if (p->layout != SA_LAYOUT_CONTIGUOUS) {
+    return fail(SA_ERR_INVALID, "unknown layout %d", p->layout);
+  }
+  return SA_OK;
+}
+
+float effective_scale(const sa_problem& p) { return p.scale > 0.f ? p.scale : 1.f / std::sqrt((float)p.D); }
+
+template <typename T>
+sa_status dalloc(T** ptr, size_t n) {
+  *ptr = nullptr;
+  if (n == 0) n = 1;
+  hipError_t e = hipMalloc((void**)ptr, n * sizeof(T));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *ptr = nullptr;
+    return fail(SA_ERR_NOMEM, "hipMalloc of %zu bytes failed: %s", n * sizeof(T), hipGetErrorString(e));
+  }
+  return SA_OK;
+}
+
+void free_plan(sa_plan* p) {
+  if (!p) return;
+  (void)hipDeviceSynchronize();
+  void* ptrs[] = {p->d_mask, p->d_row, p->d_col, p->d_crow, p->d_total, p->d_items,
+                  p->d_bin_ptr, p->d_idx, p->d_count, p->d_qp, p->d_kp};
+  for (void* q : ptrs)
+    if (q) (void)hipFree(q);
+  delete p;
+}
+
+int default_bins(int block, int device) {
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
+    cus = 256;
+  return block >= 128 ? cus : 2 * cus;
+}
+
+sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
+  const sa_problem& pr = P->prob;
+  const int BH = pr.B * pr.H, C = pr.n_chunks;
+  P->nQ = P->nK = (pr.S + pr.block - 1) / pr.block;
+  const int nQ = P->nQ, nK = P->nK;
+  P->n_items = BH * nQ;
+  if (!sp->mask) return fail(SA_ERR_INVALID, "mask is NULL");
+  const size_t mask_bytes = (size_t)BH * nQ * nK;
+  sa_status st;
+  if ((st = dalloc(&P->d_mask, mask_bytes)) || (st = dalloc(&P->d_row, (size_t)BH * nQ)) ||
+      (st = dalloc(&P->d_col, (size_t)BH * nK)) || (st = dalloc(&P->d_crow, (size_t)BH * C * nQ)) ||
+      (st = dalloc(&P->d_total, 1)) || (st = dalloc(&P->d_items, (size_t)(C + 1) * P->n_items)) ||
+      (st = dalloc(&P->d_bin_ptr, (size_t)(C + 1) * (P->num_bins + 1))))
+    return st;
+  SA_HIP(hipMemcpyAsync(P->d_mask, sp->mask, mask_bytes, hipMemcpyDeviceToDevice, stream));
+  SA_HIP(sa::launch_popcount(P->d_mask, BH, nQ, nK, C, pr.layout, P->d_row, P->d_col, P->d_crow, P->d_total,
+                             stream));
+  std::vector<int32_t> row((size_t)BH * nQ), crow((size_t)BH * C * nQ);
+  unsigned long long total = 0;
+  SA_HIP(hipMemcpyAsync(row.data(), P->d_row, row.size() * 4, hipMemcpyDeviceToHost, stream));
+  SA_HIP(hipMemcpyAsync(crow.data(), P->d_crow, crow.size() * 4, hipMemcpyDeviceToHost, stream));
+  SA_HIP(hipMemcpyAsync(&total, P->d_total, sizeof(total), hipMemcpyDeviceToHost, stream));
+  SA_HIP(hipStreamSynchronize(stream));
+  P->total_live = (int64_t)total;
+
+  const int m = P->num_bins, n = P->n_items;
+  P->h_items.assign((size_t)(C + 1) * n, 0);
+  P->h_bin_ptr.assign((size_t)(C + 1) * (m + 1), 0);
+  P->h_bin_load.assign((size_t)(C + 1) * m, 0);
+  std::vector<int64_t> loads(n);
+  for (int list = 0; list <= C; ++list) {
+    if (list == 0) {
+      for (int i = 0; i < n; ++i) loads[i] = row[i];
+    } else {
+      const int c = list - 1;
+      for (int i = 0; i < n; ++i) {
+        const int bh = i / nQ, q = i % nQ;
+        loads[i] = crow[((size_t)bh * C + c) * nQ + q];
+      }
+    }
+    sa::assign(loads.data(), n, m, P->order, P->h_items.data() + (size_t)list * n,
+               P->h_bin_ptr.data() + (size_t)list * (m + 1), P->h_bin_load.data() + (size_t)list * m);
+  }
+  int64_t sum = 0, pmax = 0;
+  for (int i = 0; i < n; ++i) {
+    sum += row[i];
+    pmax = std::max<int64_t>(pmax, row[i]);
+  }
+  P->load_sum = sum;
+  P->makespan = *std::max_element(P->h_bin_load.begin(), P->h_bin_load.begin() + m);
+  P->lower_bound = std::max<int64_t>(pmax, (sum + m - 1) / m);
+  SA_HIP(hipMemcpyAsync(P->d_items, P->h_items.data(), P->h_items.size() * 4, hipMemcpyHostToDevice, stream));
+  SA_HIP(hipMemcpyAsync(P->d_bin_ptr, P->h_bin_ptr.data(), P->h_bin_ptr.size() * 4, hipMemcpyHostToDevice,
+                        stream));
+  SA_HIP(hipStreamSynchronize(stream));
+  return SA_OK;
+}
+
+sa_status plan_topk(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
+  const sa_problem& pr = P->prob;
+  if (pr.dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "top-k kinds are bf16 only");
+  if (sp->top_k <= 0 || sp->top_k > 2048) return fail(SA_ERR_UNSUPPORTED, "top_k %d outside [1, 2048]", sp->top_k);
+  P->top_k = sp->top_k;
+  P->causal = sp->causal ? 1 : 0;
+  const size_t rows = (size_t)pr.B * pr.H * pr.S;
+  P->n_items = (int32_t)rows;
+  sa_status st;
+  if ((st = dalloc(&P->d_idx, rows * P->top_k)) || (st = dalloc(&P->d_count, rows))) return st;
+  if (P->kind == SA_KIND_INDEX) {
+    if (!sp->idx || !sp->count) return fail(SA_ERR_INVALID, "idx or count is NULL");
+    std::vector<int32_t> idx(rows * P->top_k), cnt(rows);
+    SA_HIP(hipMemcpyAsync(idx.data(), sp->idx, idx.size() * 4, hipMemcpyDeviceToHost, stream));
+    SA_HIP(hipMemcpyAsync(cnt.data(), sp->count, cnt.size() * 4, hipMemcpyDeviceToHost, stream));
+    SA_HIP(hipStreamSynchronize(stream));
+    int64_t tot = 0;
+    for (size_t r = 0; r < rows; ++r) {
+      if (cnt[r] < 0 || cnt[r] > P->top_k) return fail(SA_ERR_INVALID, "count[%zu] = %d outside [0, top_k]", r, cnt[r]);
+      for (int t = 0; t < cnt[r]; ++t) {
+        const int32_t j = idx[r * P->top_k + t];
+        if (j < 0 || j >= pr.S) return fail(SA_ERR_INVALID, "idx[%zu][%d] = %d outside [0, S)", r, t, j);
+      }
+      tot += cnt[r];
+    }
+    P->total_live = P->load_sum = tot;
+    SA_HIP(hipMemcpyAsync(P->d_idx, sp->idx, idx.size() * 4, hipMemcpyDeviceToDevice, stream));
+    SA_HIP(hipMemcpyAsync(P->d_count, sp->count, cnt.size() * 4, hipMemcpyDeviceToDevice, stream));
+    SA_HIP(hipStreamSynchronize(stream));
+    return SA_OK;
+  }
+  if (!sp->q || !sp->k || !sp->wq || !sp->wk) return fail(SA_ERR_INVALID, "q, k, wq or wk is NULL");
+  if (sp->rank != 32) return fail(SA_ERR_UNSUPPORTED, "indexer rank %d (supported: 32)", sp->rank);
+  P->rank = sp->rank;
+  if ((st = dalloc(&P->d_qp, rows * P->rank)) || (st = dalloc(&P->d_kp, rows * P->rank))) return st;
+  sa::IndexerArgs a{};
+  a.q = sp->q; a.k = sp->k; a.wq = sp->wq; a.wk = sp->wk;
+  a.qp = P->d_qp; a.kp = P->d_kp; a.idx = P->d_idx; a.count = P->d_count;
+  a.B = pr.B; a.H = pr.H; a.S = pr.S; a.D = pr.D; a.rank = P->rank; a.top_k = P->top_k; a.causal = P->causal;
+  a.sb = pr.sb; a.sh = pr.sh; a.ss = pr.ss;
+  SA_HIP(sa::launch_indexer(a, stream));
+  // selected pairs are known in closed form: min(top_k, #candidates) per query
+  int64_t tot = 0;
+  for (int i = 0; i < pr.S; ++i) tot += std::min<int64_t>(P->top_k, P->causal ? i + 1 : pr.S);
+  P->total_live = P->load_sum = tot * pr.B * pr.H;
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_t num_bins, int32_t order,
+                           sa_plan** out, hipStream_t stream) {
+  if (!out) return fail(SA_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!sp) return fail(SA_ERR_INVALID, "sparsity is NULL");
+  if (sp->kind != SA_KIND_BLOCK && sp->kind != SA_KIND_TOPK && sp->kind != SA_KIND_INDEX)
+    return fail(SA_ERR_INVALID, "unknown sparsity kind %d", sp->kind);
+  sa_status st = validate_problem(prob, sp->kind == SA_KIND_BLOCK);
+  if (st) return st;
+  if (order != SA_ORDER_LPT && order != SA_ORDER_NAIVE) return fail(SA_ERR_INVALID, "unknown order %d", order);
+  if (num_bins < 0) return fail(SA_ERR_INVALID, "num_bins %d < 0", num_bins);
+  sa_plan* P = new (std::nothrow) sa_plan();
+  if (!P) return fail(SA_ERR_NOMEM, "host allocation of the plan failed");
+  P->prob = *prob;
+  P->kind = sp->kind;
+  P->order = order;
+  if (hipGetDevice(&P->device) != hipSuccess) {
+    delete P;
+    return fail(SA_ERR_HIP, "hipGetDevice failed");
+  }
+  P->num_bins = num_bins ? num_bins : default_bins(prob->block, P->device);
+  st = sp->kind == SA_KIND_BLOCK ? plan_block(P, sp, stream) : plan_topk(P, sp, stream);
+  if (st) {
+    std::string keep = g_last_error;
+    free_plan(P);
+    g_last_error = keep;
+    return st;
+  }
+  *out = P;
+  return SA_OK;
+}
+
+sa_status sparse_attn_fwd(const sa_plan* P, const void* q, const void* k, const void* v, int32_t chunk_begin,
+                          int32_t chunk_end, void* o, float* o_part, float* m_part, float* l_part, int64_t* trace,
+                          hipStream_t stream) {
+  if (!P) return fail(SA_ERR_INVALID, "plan is NULL");
+  if (!q || !k || !v) return fail(SA_ERR_INVALID, "q, k or v is NULL");
+  const sa_problem& pr = P->prob;
+  if (P->kind != SA_KIND_BLOCK) {
+    if (!o) return fail(SA_ERR_INVALID, "top-k plans support full mode only (o must be non-NULL)");
+    if (chunk_begin != 0 || chunk_end != 1) return fail(SA_ERR_INVALID, "top-k plans take the chunk range [0, 1)");
+    sa::GatherArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.idx = P->d_idx; a.count = P->d_count;
+    a.B = pr.B; a.H = pr.H; a.S = pr.S; a.D = pr.D; a.top_k = P->top_k;
+    a.sb = pr.sb; a.sh = pr.sh; a.ss = pr.ss;
+    a.scale_log2 = effective_scale(pr) * 1.4426950408889634f;
+    SA_HIP(sa::launch_gather_attn(a, stream));
+    return SA_OK;
+  }
+  if (chunk_begin < 0 || chunk_end > pr.n_chunks || chunk_begin >= chunk_end)
+    return fail(SA_ERR_INVALID, "chunk range [%d, %d) not inside [0, %d)", chunk_begin, chunk_end, pr.n_chunks);
+  if (!o && (!o_part || !m_part || !l_part))
+    return fail(SA_ERR_INVALID, "partial mode needs o_part, m_part and l_part");
+  const int list = (chunk_end - chunk_begin == 1) ? 1 + chunk_begin : 0;
+  sa::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.o_part = o ? nullptr : o_part;
+  a.m_part = o ? nullptr : m_part;
+  a.l_part = o ? nullptr : l_part;
+  a.mask = P->d_mask;
+  a.items = P->d_items + (size_t)list * P->n_items;
+  a.bin_ptr = P->d_bin_ptr + (size_t)list * (P->num_bins + 1);
+  a.trace = trace;
+  a.B = pr.B; a.H = pr.H; a.S = pr.S; a.nQ = P->nQ; a.nK = P->nK; a.n_chunks = pr.n_chunks;
+  a.layout = pr.layout; a.c0 = chunk_begin; a.c1 = chunk_end; a.num_bins = P->num_bins;
+  a.sb = pr.sb; a.sh = pr.sh; a.ss = pr.ss;
+  a.scale = effective_scale(pr);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  hipError_t e = pr.dtype == SA_BF16 ? sa::launch_attn_bf16(a, pr.D, pr.block, stream)
+                                     : sa::launch_attn_f32(a, pr.D, pr.block, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return SA_OK;
+}
+
+sa_status chunk_merge(int32_t n_parts, const float* const* o_parts, const float* const* m_parts,
+                      const float* const* l_parts, int64_t rows, int32_t D, void* o_out, int32_t out_dtype,
+                      float* lse_out, hipStream_t stream) {
+  if (n_parts < 1 || n_parts > sa::kMaxMergeParts)
+    return fail(SA_ERR_INVALID, "n_parts %d outside [1, %d]", n_parts, sa::kMaxMergeParts);
+  if (!o_parts || !m_parts || !l_parts || !o_out) return fail(SA_ERR_INVALID, "NULL pointer argument");
+  if (rows < 0) return fail(SA_ERR_INVALID, "rows %lld < 0", (long long)rows);
+  if (D != 64 && D != 128) return fail(SA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", D);
+  if (out_dtype != SA_F32 && out_dtype != SA_BF16) return fail(SA_ERR_INVALID, "unknown dtype %d", out_dtype);
+  if (rows == 0) return SA_OK;
+  sa::MergeArgs a{};
+  for (int p = 0; p < n_parts; ++p) {
+    if (!o_parts[p] || !m_parts[p] || !l_parts[p]) return fail(SA_ERR_INVALID, "part %d has a NULL pointer", p);
+    a.o[p] = o_parts[p];
+    a.m[p] = m_parts[p];
+    a.l[p] = l_parts[p];
+  }
+  a.out = o_out;
+  a.lse = lse_out;
+  a.rows = rows;
+  a.n_parts = n_parts;
+  SA_HIP(sa::launch_merge(a, D, out_dtype, stream));
+  return SA_OK;
+}
+
+sa_status sparse_attn_plan_info(const sa_plan* P, sa_plan_info* out) {
+  if (!P || !out) return fail(SA_ERR_INVALID, "NULL argument");
+  std::memset(out, 0, sizeof(*out));
+  out->kind = P->kind;
+  out->num_bins = P->num_bins;
+  out->order = P->order;
+  out->n_chunks = P->prob.n_chunks;
+  out->nQ = P->nQ;
+  out->nK = P->nK;
+  out->n_items = P->n_items;
+  out->top_k = P->top_k;
+  out->total_live = P->total_live;
+  out->load_sum = P->load_sum;
+  out->makespan = P->makespan;
+  out->lower_bound = P->lower_bound;
+  return SA_OK;
+}
+
+sa_status sparse_attn_plan_copy(const sa_plan* P, int32_t what, int32_t chunk, void* dst, int64_t n_elems) {
+  if (!P || !dst) return fail(SA_ERR_INVALID, "NULL argument");
+  const sa_problem& pr = P->prob;
+  const int C = pr.n_chunks;
+  const int64_t BH = (int64_t)pr.B * pr.H;
+  const bool block = P->kind == SA_KIND_BLOCK;
+  if (what == SA_PLAN_ITEMS || what == SA_PLAN_BIN_PTR || what == SA_PLAN_BIN_LOAD) {
+    if (!block) return fail(SA_ERR_INVALID, "work lists exist only for block plans");
+    if (chunk < -1 || chunk >= C) return fail(SA_ERR_INVALID, "chunk %d outside [-1, %d)", chunk, C);
+  }
+  const int list = chunk + 1;
+  const void* src = nullptr;
+  bool device = true;
+  int64_t count = 0;
+  size_t esize = 4;
+  switch (what) {
+    case SA_PLAN_ROW: src = P->d_row; count = block ? BH * P->nQ : 0; break;
+    case SA_PLAN_COL: src = P->d_col; count = block ? BH * P->nK : 0; break;
+    case SA_PLAN_CROW: src = P->d_crow; count = block ? BH * C * P->nQ : 0; break;
+    case SA_PLAN_ITEMS: src = P->h_items.data() + (size_t)list * P->n_items; count = P->n_items; device = false; break;
+    case SA_PLAN_BIN_PTR:
+      src = P->h_bin_ptr.data() + (size_t)list * (P->num_bins + 1); count = P->num_bins + 1; device = false; break;
+    case SA_PLAN_BIN_LOAD:
+      src = P->h_bin_load.data() + (size_t)list * P->num_bins; count = P->num_bins; device = false; esize = 8; break;
+    case SA_PLAN_TOPK_IDX: src = P->d_idx; count = block ? 0 : BH * pr.S * P->top_k; break;
+    case SA_PLAN_TOPK_COUNT: src = P->d_count; count = block ? 0 : BH * pr.S; break;
+    default: return fail(SA_ERR_INVALID, "unknown plan array %d", what);
+  }
+  if (count == 0 || !src) return fail(SA_ERR_INVALID, "array %d does not exist for this plan kind", what);
+  if (n_elems != count) return fail(SA_ERR_INVALID, "array %d has %lld elements, caller asked for %lld", what,
+                                    (long long)count, (long long)n_elems);
+  if (device) {
+    SA_HIP(hipDeviceSynchronize());
+    SA_HIP(hipMemcpy(dst, src, (size_t)count * esize, hipMemcpyDeviceToHost));
+  } else {
+    std::memcpy(dst, src, (size_t)count * esize);
+  }
+  return SA_OK;
+}
+
+sa_status sparse_attn_assign_host(const int64_t* loads, int32_t n, int32_t m, int32_t order, int32_t* items_out,
+                                  int32_t* bin_ptr_out, int64_t* bin_load_out) {
+  if (n < 0 || m <= 0) return fail(SA_ERR_INVALID, "need n >= 0 and m > 0 (got %d, %d)", n, m);
+  if ((n > 0 && (!loads || !items_out)) || !bin_ptr_out) return fail(SA_ERR_INVALID, "NULL argument");
+  if (order != SA_ORDER_LPT && order != SA_ORDER_NAIVE) return fail(SA_ERR_INVALID, "unknown order %d", order);
+  for (int i = 0; i < n; ++i)
+    if (loads[i] < 0) return fail(SA_ERR_INVALID, "loads[%d] = %lld < 0", i, (long long)loads[i]);
+  sa::assign(loads, n, m, order, items_out, bin_ptr_out, bin_load_out);
+  return SA_OK;
+}
+
+void sparse_attn_plan_destroy(sa_plan* P) { free_plan(P); }
+
+const char* sa_status_string(int32_t status) {
+  switch (status) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_INVALID: return "SA_ERR_INVALID: invalid argument";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED: outside the compiled kernel variants";
+    case SA_ERR_HIP: return "SA_ERR_HIP: HIP runtime error";
+    case SA_ERR_NOMEM: return "SA_ERR_NOMEM: allocation failed";
+    default: return "unknown sa_status";
+  }
+}
+
+const char* sa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

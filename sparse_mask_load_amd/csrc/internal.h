@@ -1,0 +1,97 @@
+// Internal declarations shared by the host runtime and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "sparse_attn.h"
+
+namespace sa {
+
+// Limits of the compiled kernels (checked before any launch).
+constexpr int kMaxTilesPerRow = 4096;  // nK <= 4096: per-item tile list lives in LDS
+constexpr int kMaxChunks = 64;
+constexpr int kMaxMergeParts = 64;
+
+// Tile descriptor packed in an int32 (per-item tile list):
+//   bits  0..19 tile index (contiguous: KV block j; striped: compacted tile t)
+//   bits 20..23 live 32-key-group code (striped; all ones for contiguous)
+//   bits 24..29 chunk index
+constexpr int kDescCodeShift = 20;
+constexpr int kDescChunkShift = 24;
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;        // full mode output (problem dtype), nullptr in partial mode
+  float* o_part;  // partial mode: [n][B][H][S][D]
+  float* m_part;  // [n][B][H][S]
+  float* l_part;
+  const uint8_t* mask;    // [B][H][nQ][nK]
+  const int32_t* items;   // work list of this launch
+  const int32_t* bin_ptr; // [num_bins + 1]
+  int64_t* trace;         // nullable
+  int32_t B, H, S, nQ, nK, n_chunks, layout, c0, c1;
+  int32_t num_bins;
+  int64_t sb, sh, ss;
+  float scale;        // natural-log softmax scale
+  float scale_log2;   // scale * log2(e)
+};
+
+struct GatherArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int32_t* idx;    // [B][H][S][top_k]
+  const int32_t* count;  // [B][H][S]
+  int32_t B, H, S, D, top_k;
+  int64_t sb, sh, ss;
+  float scale_log2;
+};
+
+struct IndexerArgs {
+  const void* q;
+  const void* k;
+  const void* wq;  // [D][rank] bf16
+  const void* wk;
+  __bf16* qp;      // [B][H][S][rank] projections (plan scratch)
+  __bf16* kp;
+  int32_t* idx;    // [B][H][S][top_k]
+  int32_t* count;  // [B][H][S]
+  int32_t B, H, S, D, rank, top_k, causal;
+  int64_t sb, sh, ss;
+};
+
+struct MergeArgs {
+  const float* o[kMaxMergeParts];
+  const float* m[kMaxMergeParts];
+  const float* l[kMaxMergeParts];
+  void* out;
+  float* lse;
+  int64_t rows;
+  int32_t n_parts;
+};
+
+// Kernel launchers (defined in the .hip files).  Return hipSuccess or the launch error.
+hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_chunks, int layout,
+                           int32_t* row, int32_t* col, int32_t* crow, unsigned long long* total,
+                           hipStream_t stream);
+hipError_t launch_attn_bf16(const FwdArgs& a, int D, int block, hipStream_t stream);
+hipError_t launch_attn_f32(const FwdArgs& a, int D, int block, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int D, int out_dtype, hipStream_t stream);
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
+hipError_t launch_gather_attn(const GatherArgs& a, hipStream_t stream);
+
+// Host LPT / round-robin (lpt.cpp).  Items are 0..n-1 with loads[i] >= 0.
+//   LPT: sort by (load desc, id asc); each item goes to the least-loaded bin,
+//   ties to the lowest bin index; each bin keeps assignment order.
+//   NAIVE: item i goes to bin i mod m, in id order.
+void assign(const int64_t* loads, int n, int m, int order, int32_t* items_out, int32_t* bin_ptr_out,
+            int64_t* bin_load_out);
+
+}  // namespace sa

@@ -1,0 +1,63 @@
+// Device helpers shared by the block-sparse attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace sa {
+
+// Builds the ordered list of live KV tiles of one work item (one Q-block row of
+// the block mask) for chunks [c0, c1), using one wavefront.  Chunk c of the
+// contiguous layout covers KV blocks [c*nK/C, (c+1)*nK/C); a descriptor carries
+// the block index and a full group code.  Chunk c of the striped layout
+// (striped attention: token j belongs to chunk j mod C) is cut into compacted
+// tiles of `block` tokens; compacted tile t of chunk c spans original blocks
+// C*t .. C*t+C-1, each contributing block/C consecutive compacted keys, so its
+// liveness is the C-bit code of those mask entries.  Order: chunk, then tile.
+// Returns the number of descriptors written to `list` (valid in every lane).
+__device__ inline int build_tile_list(const uint8_t* __restrict__ mrow, int nK, int n_chunks,
+                                      int layout, int c0, int c1, int* list) {
+  const int lane = threadIdx.x & 63;
+  const int per_chunk = nK / n_chunks;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int count = 0;
+  for (int c = c0; c < c1; ++c) {
+    if (layout == SA_LAYOUT_CONTIGUOUS) {
+      const int j0 = c * per_chunk, j1 = j0 + per_chunk;
+      for (int base = j0; base < j1; base += 64) {
+        const int j = base + lane;
+        const bool live = j < j1 && mrow[j] != 0;
+        const uint64_t bits = __ballot(live);
+        if (live)
+          list[count + __popcll(bits & below)] = j | (0xF << kDescCodeShift) | (c << kDescChunkShift);
+        count += __popcll(bits);
+      }
+    } else {
+      for (int base = 0; base < per_chunk; base += 64) {
+        const int t = base + lane;
+        int code = 0;
+        if (t < per_chunk)
+          for (int g = 0; g < n_chunks; ++g) code |= (mrow[n_chunks * t + g] != 0 ? 1 : 0) << g;
+        const bool live = code != 0;
+        const uint64_t bits = __ballot(live);
+        if (live)
+          list[count + __popcll(bits & below)] = t | (code << kDescCodeShift) | (c << kDescChunkShift);
+        count += __popcll(bits);
+      }
+    }
+  }
+  return count;
+}
+
+__device__ inline int64_t realtime_now() { return (int64_t)__builtin_amdgcn_s_memrealtime(); }
+
+// (XCC_ID << 32) | HW_ID of the executing wave: identifies the compute unit.
+__device__ inline int64_t hw_location() {
+  const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_REG_HW_ID
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // HW_REG_XCC_ID
+  return ((int64_t)xcc << 32) | (int64_t)hw;
+}
+
+}  // namespace sa

@@ -1,0 +1,70 @@
+// Online-softmax merge of per-chunk partials (6D-parallel notes, section 2.1):
+// per row, fold the parts in order with m_new = max(m_acc, m_p),
+// alpha = exp(m_acc - m_new), beta = exp(m_p - m_new), l = alpha*l + beta*l_p,
+// O = alpha*O + beta*O_p, then divide by l.  A part with m_p = -inf is the
+// identity of the fold (alpha = 1, beta = 0), so it is skipped and its O_p is
+// never read; a row whose every part is empty yields O = 0, lse = -inf.
+//
+// HBM-bound: D/4 threads per row, each folding one 16-byte fp32 vector per part.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace sa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void chunk_merge_kernel(MergeArgs a) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (row >= a.rows) return;
+  const int dq = (threadIdx.x % TPR) * 4;
+  float m_acc = kNegInf, l_acc = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < a.n_parts; ++p) {
+    const float mp = a.m[p][row];
+    if (mp == kNegInf) continue;
+    const float lp = a.l[p][row];
+    const float m_new = fmaxf(m_acc, mp);
+    const float alpha = expf(m_acc - m_new);
+    const float beta = expf(mp - m_new);
+    const f32x4 op = *(const f32x4*)(a.o[p] + row * D + dq);
+    o = alpha * o + beta * op;
+    l_acc = alpha * l_acc + beta * lp;
+    m_acc = m_new;
+  }
+  const float inv = l_acc > 0.f ? 1.f / l_acc : 0.f;
+  OutT* out = (OutT*)a.out + row * D + dq;
+  if constexpr (sizeof(OutT) == 2) {
+    const bf16x4 v = {(__bf16)(o[0] * inv), (__bf16)(o[1] * inv), (__bf16)(o[2] * inv), (__bf16)(o[3] * inv)};
+    *(bf16x4*)out = v;
+  } else {
+    *(f32x4*)out = o * inv;
+  }
+  if (a.lse && dq == 0) a.lse[row] = l_acc > 0.f ? m_acc + logf(l_acc) : kNegInf;
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a, int D, int out_dtype, hipStream_t stream) {
+  const int rpb = 256 / (D / 4);
+  const unsigned grid = (unsigned)((a.rows + rpb - 1) / rpb);
+  if (D == 128 && out_dtype == SA_BF16)
+    hipLaunchKernelGGL((chunk_merge_kernel<128, __bf16>), dim3(grid), dim3(256), 0, stream, a);
+  else if (D == 128 && out_dtype == SA_F32)
+    hipLaunchKernelGGL((chunk_merge_kernel<128, float>), dim3(grid), dim3(256), 0, stream, a);
+  else if (D == 64 && out_dtype == SA_BF16)
+    hipLaunchKernelGGL((chunk_merge_kernel<64, __bf16>), dim3(grid), dim3(256), 0, stream, a);
+  else if (D == 64 && out_dtype == SA_F32)
+    hipLaunchKernelGGL((chunk_merge_kernel<64, float>), dim3(grid), dim3(256), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,125 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry point, its host
+LPT planner is bit-exact against the oracle, and argument errors are reported before any
+GPU work.  No kernel is launched here."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import plan as P
+from sparse_mask_load_amd import binding as bd
+from sparse_mask_load_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "sparse_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:sa_status|void|const char\s*\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"sparse_attn_plan", "sparse_attn_fwd", "chunk_merge"} <= set(names)
+    lib = bd.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(bd._SIGNATURES)
+
+
+def test_status_strings():
+    assert bd.sa_status_string(0) == "SA_OK"
+    for st in (-1, -2, -3, -4):
+        assert bd.sa_status_string(st).startswith("SA_ERR")
+
+
+def _oracle_lists(loads, m, order):
+    bins, bl = (P.lpt if order == "lpt" else P.naive)(list(loads), m)
+    items = [j for b in bins for j in b]
+    ptr = np.cumsum([0] + [len(b) for b in bins])
+    return np.array(items), ptr, np.array(bl)
+
+
+@pytest.mark.parametrize("order", ["lpt", "naive"])
+def test_host_assign_bit_exact_random(order):
+    rng = np.random.default_rng(0)
+    for trial in range(40):
+        n = int(rng.integers(0, 400))
+        m = int(rng.integers(1, 40))
+        loads = rng.integers(0, int(rng.integers(1, 60)), size=n)
+        items, ptr, bl = bd.sparse_attn_assign_host(loads, m, order)
+        oi, op, ob = _oracle_lists(loads, m, order)
+        assert np.array_equal(items, oi) and np.array_equal(ptr, op) and np.array_equal(bl, ob)
+
+
+def test_host_assign_page_example():
+    items, ptr, bl = bd.sparse_attn_assign_host([8, 7, 6, 5, 4], 2)
+    assert items.tolist() == [0, 3, 4, 1, 2] and ptr.tolist() == [0, 3, 5] and bl.tolist() == [17, 13]
+
+
+@pytest.mark.parametrize("cfg,m", [(2, 512), (3, 256), (4, 256)])
+def test_host_assign_bit_exact_on_workload_rows(cfg, m):
+    w = W.make(cfg, with_data=False)
+    cnt = P.popcount(w.mask, w.n_chunks)
+    for order in ("lpt", "naive"):
+        loads = cnt["row"].reshape(-1)
+        items, ptr, bl = bd.sparse_attn_assign_host(loads, m, order)
+        ref = P.plan_items(cnt["row"], m, order)
+        assert np.array_equal(items, ref["items"]) and np.array_equal(ptr, ref["bin_ptr"])
+        assert np.array_equal(bl, ref["bin_load"])
+    if cfg == 3:
+        # causal block mask over 256 workgroups: LPT reaches the lower bound exactly
+        ref = P.plan_items(cnt["row"], 256, "lpt")
+        assert ref["makespan"] == 516 == -(-cnt["total"] // 256)
+        naive = P.plan_items(cnt["row"], 256, "naive")
+        assert naive["makespan"] / (cnt["total"] / 256) > 1.9
+
+
+def test_host_assign_errors():
+    with pytest.raises(bd.SparseAttnError) as e:
+        bd.sparse_attn_assign_host([1, 2], 0)
+    assert e.value.status == bd.SA_ERR_INVALID
+    with pytest.raises(bd.SparseAttnError) as e:
+        bd.sparse_attn_assign_host([1, -2], 3)
+    assert e.value.status == bd.SA_ERR_INVALID and "loads[1]" in str(e.value)
+
+
+def _problem(**kw):
+    base = dict(B=1, H=2, S=256, D=64, block=64, n_chunks=2, layout=0, dtype=bd.SA_BF16, scale=0.0, pad0=0,
+                sb=2 * 256 * 64, sh=256 * 64, ss=64)
+    base.update(kw)
+    return bd.sa_problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), bd.SA_ERR_UNSUPPORTED),
+    (dict(block=32), bd.SA_ERR_UNSUPPORTED),
+    (dict(B=0), bd.SA_ERR_INVALID),
+    (dict(n_chunks=3), bd.SA_ERR_INVALID),
+    (dict(n_chunks=0), bd.SA_ERR_INVALID),
+    (dict(ss=32), bd.SA_ERR_INVALID),
+    (dict(layout=1, n_chunks=4), bd.SA_ERR_UNSUPPORTED),  # block/C = 16 keys < 32
+    (dict(layout=7), bd.SA_ERR_INVALID),
+    (dict(dtype=bd.SA_F32, block=128), bd.SA_ERR_UNSUPPORTED),
+])
+def test_plan_rejects_bad_problems_before_touching_the_gpu(kw, status):
+    import ctypes
+    prob = _problem(**kw)
+    sp = bd.sa_sparsity(bd.SA_KIND_BLOCK, 0, 0, 0, 1, None, None, None, None, None, None)
+    out = ctypes.c_void_p()
+    st = bd.lib().sparse_attn_plan(ctypes.byref(prob), ctypes.byref(sp), 0, 0, ctypes.byref(out), None)
+    assert st == status, bd.sa_last_error()
+    assert out.value is None
+
+
+def test_fwd_and_merge_argument_errors():
+    lib = bd.lib()
+    assert lib.sparse_attn_fwd(None, 1, 1, 1, 0, 1, 1, None, None, None, None, None) == bd.SA_ERR_INVALID
+    assert "plan is NULL" in bd.sa_last_error()
+    arr = (bd._P * 1)(1)
+    assert lib.chunk_merge(0, arr, arr, arr, 10, 64, 1, 0, None, None) == bd.SA_ERR_INVALID
+    assert lib.chunk_merge(1, arr, arr, arr, 10, 96, 1, 0, None, None) == bd.SA_ERR_UNSUPPORTED
+    assert lib.chunk_merge(1, arr, arr, arr, 0, 64, 1, 0, None, None) == bd.SA_OK  # nothing to do
+    lib.sparse_attn_plan_destroy(None)  # no-op
