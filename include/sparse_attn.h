@@ -56,6 +56,7 @@ typedef enum { SA_KIND_BLOCK = 0, SA_KIND_TOPK = 1, SA_KIND_INDEX = 2 } sa_kind;
 
 /* Shape of one attention problem (self-attention: Q and KV have length S).
  *  block     Q-block = KV-block size in tokens.  bf16: 64 or 128; f32: 64.
+ *            nK = ceil(S/block) <= 2048.
  *  D         head dim.  bf16: 64 or 128; f32: 64 or 128.
  *  n_chunks  number of KV chunks (ring steps).  Contiguous layout: chunk c is
  *            KV blocks [c*nK/C, (c+1)*nK/C) and nK % C == 0, nK = ceil(S/block);
@@ -133,8 +134,8 @@ typedef enum {
  *  per chunk; the lists are uploaded for the persistent kernel.  This kind
  *  synchronises the stream.
  *  TOPK: runs the indexer and top-k selection on the GPU; asynchronous.
- *  num_bins: persistent workgroups; 0 picks one per compute unit (two for
- *  block 64).  out (host): receives the plan.  Returns SA_ERR_NOMEM if the
+ *  num_bins: persistent workgroups; 0 picks one per resident workgroup slot
+ *  (bf16: 2 per compute unit for block 128, 4 for block 64; f32: 1).  out (host): receives the plan.  Returns SA_ERR_NOMEM if the
  *  plan's device buffers cannot be allocated. */
 sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_t num_bins,
                            int32_t order, sa_plan** out, hipStream_t stream);

@@ -62,7 +62,7 @@ sa_status hip_fail(hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(e_, #call);  \
   } while (0)
 
-int max_tiles_per_row(int block) { return block >= 128 ? sa::kMaxTilesPerRow : sa::kMaxTilesPerRow / 2; }
+int max_tiles_per_row(int) { return sa::kMaxTilesPerRow; }
 
 sa_status validate_problem(const sa_problem* p, bool block_kind) {
   if (!p) return fail(SA_ERR_INVALID, "problem is NULL");
@@ -122,11 +122,12 @@ void free_plan(sa_plan* p) {
   delete p;
 }
 
-int default_bins(int block, int device) {
+int default_bins(const sa_problem& p, int device) {
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
     cus = 256;
-  return block >= 128 ? cus : 2 * cus;
+  // one bin per resident workgroup: the bf16 kernel keeps 2 (block 128) or 4 (block 64) per CU
+  return p.dtype == SA_BF16 ? cus * sa::attn_bf16_wg_per_cu(p.block) : cus;
 }
 
 sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
@@ -259,7 +260,7 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
     delete P;
     return fail(SA_ERR_HIP, "hipGetDevice failed");
   }
-  P->num_bins = num_bins ? num_bins : default_bins(prob->block, P->device);
+  P->num_bins = num_bins ? num_bins : default_bins(*prob, P->device);
   st = sp->kind == SA_KIND_BLOCK ? plan_block(P, sp, stream) : plan_topk(P, sp, stream);
   if (st) {
     std::string keep = g_last_error;

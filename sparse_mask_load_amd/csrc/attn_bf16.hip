@@ -23,12 +23,19 @@
 //    two ds_read_b64_tr_b16 transposed reads of the row-major V tile.  O^T's
 //    accumulator again gives a lane one query column, so the alpha rescale is
 //    in-lane too.
-//  * K and V tiles are double-buffered in LDS and filled by
-//    global_load_lds_dwordx4 (no VGPR staging); tile t+1 streams in while
-//    tile t is computed.  16-byte chunks are XOR-swizzled per row so the
-//    operand reads above are free of bank conflicts.
-//  * exp is exp2 on scores pre-multiplied by scale*log2(e); the exported m is
-//    converted back to natural-log units.
+//  * One K and one V tile live in LDS (72 KiB with the tile list), so two
+//    workgroups share a compute unit and every SIMD holds two waves: one
+//    wave's softmax (VALU) runs while the other's MFMAs execute.  Tiles are
+//    filled by global_load_lds_dwordx4 (no VGPR staging) on a two-barrier
+//    schedule: K of tile t+1 streams in during the softmax and P V of tile t,
+//    V of tile t+1 during S of tile t+1.  16-byte chunks are XOR-swizzled per
+//    row so the operand reads above are free of bank conflicts.
+//  * exp is exp2 on scores pre-multiplied by scale*log2(e).  The reference max
+//    used in the exponent only moves when a row's max grows by more than 2^8
+//    (the result O/l does not depend on the reference), so O is rarely
+//    rescaled; the true row max is tracked and the exported partial is
+//    converted to it, in natural-log units.  The row sum adds the bf16-rounded
+//    P values that also feed P V (v_dot2c_f32_bf16).
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -40,12 +47,26 @@ namespace {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units: P values stay below 2^8
+
+template <int D, int BLK>
+struct Shape {
+  static constexpr int NW = BLK / 32;    // waves per workgroup
+  static constexpr int NKB = BLK / 32;   // 32-key blocks per tile
+  static constexpr int ND = D / 32;      // 32-wide head-dim blocks
+  static constexpr int NKS = D / 16;     // k-steps of S^T
+  static constexpr int TILE = BLK * D;
+  static constexpr int CPR = D / 8;      // 16-byte chunks per row
+  static constexpr int IPW = BLK * CPR / (64 * NW);  // load instructions per wave per tile
+  static constexpr int WG_PER_CU = BLK >= 128 ? 2 : 4;
+};
 
 // Row-dependent XOR applied to the 16-byte chunk index of a tile row in LDS.
 template <int D>
@@ -63,57 +84,167 @@ __device__ __forceinline__ float other_half(float x) {
   return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-// Issue the global->LDS loads of one K and one V tile (this wave's share).
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Issue the global->LDS loads of one K or V tile (this wave's share).
 template <int D, int BLK>
-__device__ __forceinline__ void load_tile(const bf16* __restrict__ gK, const bf16* __restrict__ gV,
-                                          int64_t bh_base, int64_t ss, int S, int layout, int n_chunks,
-                                          int desc, bf16* sK, bf16* sV) {
-  constexpr int NW = BLK / 32;
-  constexpr int CPR = D / 8;                      // 16-byte chunks per row
-  constexpr int IPW = BLK * CPR / (64 * NW);      // load instructions per wave per tensor
+__device__ __forceinline__ void load_tile(const bf16* __restrict__ g, int64_t bh_base, int64_t ss, int S,
+                                          int layout, int n_chunks, int desc, bf16* lds) {
+  using SH = Shape<D, BLK>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int idx = desc & 0xFFFFF;
   const int c = (desc >> kDescChunkShift) & 63;
 #pragma unroll
-  for (int n = 0; n < IPW; ++n) {
-    const int slot0 = (wave * IPW + n) * 64;
+  for (int n = 0; n < SH::IPW; ++n) {
+    const int slot0 = (wave * SH::IPW + n) * 64;
     const int slot = slot0 + lane;
-    const int r = slot / CPR;
-    const int p = slot % CPR;
-    const int lc = p ^ chunk_swizzle<D>(r);
+    const int r = slot / SH::CPR;
+    const int lc = (slot % SH::CPR) ^ chunk_swizzle<D>(r);
     int64_t pos;
-    if (layout == SA_LAYOUT_CONTIGUOUS) {
+    if (layout == SA_LAYOUT_CONTIGUOUS)
       pos = min(idx * BLK + r, S - 1);
-    } else {
+    else
       pos = c + (int64_t)n_chunks * ((int64_t)idx * BLK + r);
-    }
-    const int64_t g = bh_base + pos * ss + lc * 8;
-    __builtin_amdgcn_global_load_lds(gK + g, LDS_PTR(void, sK + slot0 * 8), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(gV + g, LDS_PTR(void, sV + slot0 * 8), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g + bh_base + pos * ss + lc * 8, LDS_PTR(void, lds + slot0 * 8), 16, 0, 0);
   }
 }
 
-template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(FwdArgs a) {
-  constexpr int NKB = BLK / 32;  // 32-key blocks per tile
-  constexpr int ND = D / 32;     // 32-wide head-dim blocks
-  constexpr int NKS = D / 16;    // k-steps of S^T
-  constexpr int TILE = BLK * D;
-  constexpr int MAXT = BLK >= 128 ? kMaxTilesPerRow : kMaxTilesPerRow / 2;
+// Online-softmax state of one wave (32 query rows; a lane owns row l % 32).
+template <int ND>
+struct RowState {
+  f32x16 acc[ND];  // O^T (unnormalised, relative to m_ref)
+  float m_ref;     // reference max used in the exponent (log2 units)
+  float m_true;    // true running max (log2 units)
+  float l;         // this lane's share of the row sum (relative to m_ref)
+};
 
-  __shared__ __attribute__((aligned(1024))) bf16 sK[2][TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[2][TILE];
-  __shared__ int sList[MAXT];
-  __shared__ int sCount;
+template <int ND>
+__device__ __forceinline__ void reset(RowState<ND>& st) {
+#pragma unroll
+  for (int d = 0; d < ND; ++d) st.acc[d] = f32x16{};
+  st.m_ref = kNegInf;
+  st.m_true = kNegInf;
+  st.l = 0.f;
+}
+
+// One live tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// live_kb: bit kb set when 32-key block kb of the tile holds live keys.
+// ragged: keys at or beyond S (last, partial block) are masked to -inf.
+template <int D, int BLK>
+__device__ __forceinline__ void tile_step(const bf16* __restrict__ Kt, const bf16* __restrict__ Vt,
+                                          const bf16x8 (&qf)[D / 16], RowState<D / 32>& st, int live_kb,
+                                          bool ragged, int key0, float sl2, int k_off, int k_swz,
+                                          const int (&v_off)[2], const int (&v_swz)[2], int v_chunk, int h2,
+                                          bool last, const FwdArgs& a, int64_t bh_base, int next_desc, bf16* kbuf,
+                                          bf16* vbuf) {
+  using SH = Shape<D, BLK>;
+  f32x16 s[SH::NKB];
+#pragma unroll
+  for (int kb = 0; kb < SH::NKB; ++kb) {
+    s[kb] = f32x16{};
+    if ((live_kb >> kb) & 1) {
+      const bf16* kp = Kt + kb * 32 * D + k_off;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 kf[SH::NKS / 2];
+#pragma unroll
+        for (int i = 0; i < SH::NKS / 2; ++i) {
+          const int ks = half * (SH::NKS / 2) + i;
+          kf[i] = *(const bf16x8*)(kp + (((2 * ks + h2) ^ k_swz) << 3));
+        }
+#pragma unroll
+        for (int i = 0; i < SH::NKS / 2; ++i)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[half * (SH::NKS / 2) + i], s[kb], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Barrier A: every wave is done reading K of this tile and V of this tile has landed.
+  wait_vm();
+  __syncthreads();
+  if (!last) load_tile<D, BLK>((const bf16*)a.k, bh_base, a.ss, a.S, a.layout, a.n_chunks, next_desc, kbuf);
+
+  if (ragged) {
+#pragma unroll
+    for (int kb = 0; kb < SH::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (key0 + kb * 32 + 16 * (r >> 3) + 8 * h2 + (r & 7) >= a.S) s[kb][r] = kNegInf;
+  }
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < SH::NKB; ++kb) {
+    if (!((live_kb >> kb) & 1)) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  }
+  mx = fmaxf(mx, other_half(mx)) * sl2;
+  st.m_true = fmaxf(st.m_true, mx);
+  if (__builtin_amdgcn_ballot_w64(mx > st.m_ref + kRescaleSlack)) {
+    const float m_new = (mx > st.m_ref + kRescaleSlack) ? st.m_true : st.m_ref;
+    const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);
+    st.m_ref = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int d = 0; d < SH::ND; ++d) st.acc[d] *= alpha;
+  }
+  const float m_ref = st.m_ref;
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  float lsum0 = 0.f, lsum1 = 0.f;
+
+#pragma unroll
+  for (int kb = 0; kb < SH::NKB; ++kb) {
+    if ((live_kb >> kb) & 1) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -m_ref));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lsum0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0][2 * e], pb[0][2 * e + 1]}, ones, lsum0, false);
+        lsum1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][2 * e], pb[1][2 * e + 1]}, ones, lsum1, false);
+      }
+#pragma unroll
+      for (int stp = 0; stp < 2; ++stp) {
+        const bf16* vp = Vt + (kb * 32 + 16 * stp) * D;
+        bf16x8 va[SH::ND];
+#pragma unroll
+        for (int d = 0; d < SH::ND; ++d) {
+          const int ch = 4 * d + v_chunk;
+          const bf16x4 lo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_off[0] + ((ch ^ v_swz[0]) << 3)));
+          const bf16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_off[1] + ((ch ^ v_swz[1]) << 3)));
+          va[d] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int d = 0; d < SH::ND; ++d)
+          st.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[d], pb[stp], st.acc[d], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l += lsum0 + lsum1;
+
+  // Barrier B: every wave is done reading V of this tile and K of the next tile has landed.
+  wait_vm();
+  __syncthreads();
+  if (!last) load_tile<D, BLK>((const bf16*)a.v, bh_base, a.ss, a.S, a.layout, a.n_chunks, next_desc, vbuf);
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(FwdArgs a) {
+  using SH = Shape<D, BLK>;
+  __shared__ __attribute__((aligned(1024))) bf16 sK[SH::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[SH::TILE];
+  __shared__ int sList[kMaxTilesPerRow];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h2 = lane >> 5, l32 = lane & 31;
   const bool full = a.o != nullptr;
   const bool striped = a.layout == SA_LAYOUT_STRIPED;
-  const int kb_div = striped ? NKB / a.n_chunks : NKB;  // key blocks per liveness group
+  const int kb_div = striped ? SH::NKB / a.n_chunks : SH::NKB;  // key blocks per liveness group
   const bf16* __restrict__ gQ = (const bf16*)a.q;
-  const bf16* __restrict__ gK = (const bf16*)a.k;
-  const bf16* __restrict__ gV = (const bf16*)a.v;
 
   // Per-lane LDS operand offsets (independent of tile, key block and step).
   const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);  // bits 2,3 swapped
@@ -143,154 +274,88 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(FwdArgs a) {
     // Q^T operand of this wave's 32 rows: lane holds row q0 + l32, dims 16*ks + 8*h2 .. +7.
     const int qrow = qb * BLK + wave * 32 + l32;
     const int qrow_c = min(qrow, a.S - 1);
-    bf16x8 qf[NKS];
+    bf16x8 qf[SH::NKS];
     {
       const bf16* qp = gQ + bh_base + (int64_t)qrow_c * a.ss + 8 * h2;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
+      for (int ks = 0; ks < SH::NKS; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
     }
 
     __syncthreads();  // every wave is done with the previous item's list and tiles
-    if (wave == 0) {
-      const int n = build_tile_list(a.mask + (int64_t)item * a.nK, a.nK, a.n_chunks, a.layout, a.c0,
-                                    a.c1, sList);
-      if (lane == 0) sCount = n;
-    }
+    // every wave counts the live tiles; wave 0 also writes the list
+    const int n_tiles = build_tile_list(a.mask + (int64_t)item * a.nK, a.nK, a.n_chunks, a.layout, a.c0, a.c1,
+                                        sList, wave == 0);
     __syncthreads();
-    const int n_tiles = sCount;
+    const int* list = sList;
 
-    f32x16 acc[ND];
-#pragma unroll
-    for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
-    float m_run = kNegInf, l_run = 0.f;
+    RowState<SH::ND> st;
+    reset(st);
     int cur_chunk = a.c0;
 
     auto flush_partial = [&](int chunk) {
-      const float l_tot = l_run + other_half(l_run);
+      const bool any = st.m_true != kNegInf;
+      const float corr = any ? __builtin_amdgcn_exp2f(st.m_ref - st.m_true) : 0.f;
+      const float l_tot = (st.l + other_half(st.l)) * corr;
       if (qrow < a.S) {
         const int64_t prow = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + qrow;
         float* op = a.o_part + prow * D;
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
+        for (int d = 0; d < SH::ND; ++d)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const f32x4 v4 = {acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]};
+            const f32x4 v4 = {st.acc[d][4 * g] * corr, st.acc[d][4 * g + 1] * corr, st.acc[d][4 * g + 2] * corr,
+                              st.acc[d][4 * g + 3] * corr};
             *(f32x4*)(op + d * 32 + 8 * g + 4 * h2) = v4;
           }
         if (h2 == 0) {
-          a.m_part[prow] = m_run * kLn2;
+          a.m_part[prow] = any ? st.m_true * kLn2 : kNegInf;
           a.l_part[prow] = l_tot;
         }
       }
-#pragma unroll
-      for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
-      m_run = kNegInf;
-      l_run = 0.f;
+      reset(st);
     };
 
-    if (n_tiles > 0)
-      load_tile<D, BLK>(gK, gV, bh_base, a.ss, a.S, a.layout, a.n_chunks, sList[0], sK[0], sV[0]);
+    if (n_tiles > 0) {
+      const int d0 = __builtin_amdgcn_readfirstlane(list[0]);
+      load_tile<D, BLK>((const bf16*)a.k, bh_base, a.ss, a.S, a.layout, a.n_chunks, d0, sK);
+      load_tile<D, BLK>((const bf16*)a.v, bh_base, a.ss, a.S, a.layout, a.n_chunks, d0, sV);
+      wait_vm();
+      __syncthreads();
+    }
 
     for (int t = 0; t < n_tiles; ++t) {
-      const int desc = __builtin_amdgcn_readfirstlane(sList[t]);
+      const int desc = __builtin_amdgcn_readfirstlane(list[t]);
+      const bool last = t + 1 == n_tiles;
+      const int next_desc = last ? 0 : __builtin_amdgcn_readfirstlane(list[t + 1]);
       const int tchunk = (desc >> kDescChunkShift) & 63;
       if (!full)
         while (cur_chunk < tchunk) flush_partial(cur_chunk++);
-
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // tile t is in LDS; tile t-1's buffer is free
-      if (t + 1 < n_tiles)
-        load_tile<D, BLK>(gK, gV, bh_base, a.ss, a.S, a.layout, a.n_chunks,
-                          __builtin_amdgcn_readfirstlane(sList[t + 1]), sK[(t + 1) & 1], sV[(t + 1) & 1]);
-
-      const bf16* Kt = sK[t & 1];
-      const bf16* Vt = sV[t & 1];
       const int code = (desc >> kDescCodeShift) & 15;
       const int tidx = desc & 0xFFFFF;
-      const bool ragged = !striped && (tidx + 1) * BLK > a.S;
       const int key0 = tidx * BLK;
-
-      // S^T = K Q^T for the live 32-key blocks.
-      f32x16 s[NKB];
+      int live_kb = (1 << SH::NKB) - 1;
+      if (striped) {
+        live_kb = 0;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
-        if (!((code >> (kb / kb_div)) & 1)) continue;
-        const bf16* kp = Kt + kb * 32 * D + k_off;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 kv = *(const bf16x8*)(kp + (((2 * ks + h2) ^ k_swz) << 3));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qf[ks], s[kb], 0, 0, 0);
-        }
+        for (int kb = 0; kb < SH::NKB; ++kb) live_kb |= ((code >> (kb / kb_div)) & 1) << kb;
       }
-
-      // Online softmax (row = this lane's query column).
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        if (!((code >> (kb / kb_div)) & 1)) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r];
-          if (ragged) {
-            const int key = key0 + kb * 32 + 16 * (r >> 3) + 8 * h2 + (r & 7);
-            if (key >= a.S) x = kNegInf;
-            s[kb][r] = x;
-          }
-          mx = fmaxf(mx, x);
-        }
-      }
-      mx = fmaxf(mx, other_half(mx));
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < ND; ++d) acc[d] *= alpha;
-
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        if (!((code >> (kb / kb_div)) & 1)) continue;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -m_new));
-          lsum += p;
-          pb[r >> 3][r & 7] = (bf16)p;
-        }
-        // O^T += V^T P^T over this block's two 16-key steps.
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const bf16* vp = Vt + (kb * 32 + 16 * st) * D;
-#pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            const int ch = 4 * d + v_chunk;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                LDS_PTR(bf16x4, vp + v_off[0] + ((ch ^ v_swz[0]) << 3)));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                LDS_PTR(bf16x4, vp + v_off[1] + ((ch ^ v_swz[1]) << 3)));
-            const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st], acc[d], 0, 0, 0);
-          }
-        }
-      }
-      l_run += lsum;
+      tile_step<D, BLK>(sK, sV, qf, st, live_kb, !striped && key0 + BLK > a.S, key0, sl2, k_off, k_swz, v_off,
+                        v_swz, v_chunk, h2, last, a, bh_base, next_desc, sK, sV);
     }
 
     if (!full) {
       while (cur_chunk < a.c1) flush_partial(cur_chunk++);
     } else {
-      const float l_tot = l_run + other_half(l_run);
+      const float l_tot = st.l + other_half(st.l);
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       if (qrow < a.S) {
         bf16* op = (bf16*)a.o + bh_base + (int64_t)qrow * a.ss;
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
+        for (int d = 0; d < SH::ND; ++d)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const bf16x4 v4 = {(bf16)(acc[d][4 * g] * inv), (bf16)(acc[d][4 * g + 1] * inv),
-                               (bf16)(acc[d][4 * g + 2] * inv), (bf16)(acc[d][4 * g + 3] * inv)};
+            const bf16x4 v4 = {(bf16)(st.acc[d][4 * g] * inv), (bf16)(st.acc[d][4 * g + 1] * inv),
+                               (bf16)(st.acc[d][4 * g + 2] * inv), (bf16)(st.acc[d][4 * g + 3] * inv)};
             *(bf16x4*)(op + d * 32 + 8 * g + 4 * h2) = v4;
           }
       }
@@ -306,6 +371,8 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(FwdArgs a) {
 }
 
 }  // namespace
+
+int attn_bf16_wg_per_cu(int block) { return block >= 128 ? 2 : 4; }
 
 hipError_t launch_attn_bf16(const FwdArgs& a, int D, int block, hipStream_t stream) {
   if (D == 128 && block == 128)

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(FwdArgs a) {
   __shared__ float sK[BLK][D + 1];
   __shared__ float sV[BLK][D];
   __shared__ float sP[BLK][BLK + 1];
-  __shared__ int sList[kMaxTilesPerRow / 2];
+  __shared__ int sList[kMaxTilesPerRow];
   __shared__ int sCount;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -12,7 +12,7 @@
 namespace sa {
 
 // Limits of the compiled kernels (checked before any launch).
-constexpr int kMaxTilesPerRow = 4096;  // nK <= 4096: per-item tile list lives in LDS
+constexpr int kMaxTilesPerRow = 2048;  // nK <= 2048: per-item tile list lives in LDS
 constexpr int kMaxChunks = 64;
 constexpr int kMaxMergeParts = 64;
 
@@ -82,6 +82,7 @@ hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_ch
                            int32_t* row, int32_t* col, int32_t* crow, unsigned long long* total,
                            hipStream_t stream);
 hipError_t launch_attn_bf16(const FwdArgs& a, int D, int block, hipStream_t stream);
+int attn_bf16_wg_per_cu(int block);  // workgroups the bf16 kernel keeps resident per CU
 hipError_t launch_attn_f32(const FwdArgs& a, int D, int block, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int D, int out_dtype, hipStream_t stream);
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);

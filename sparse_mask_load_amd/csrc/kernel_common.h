@@ -16,9 +16,10 @@ namespace sa {
 // tiles of `block` tokens; compacted tile t of chunk c spans original blocks
 // C*t .. C*t+C-1, each contributing block/C consecutive compacted keys, so its
 // liveness is the C-bit code of those mask entries.  Order: chunk, then tile.
-// Returns the number of descriptors written to `list` (valid in every lane).
+// Returns the number of descriptors (valid in every lane); only writes `list`
+// when `write` is set, so every wave can count while one wave fills the list.
 __device__ inline int build_tile_list(const uint8_t* __restrict__ mrow, int nK, int n_chunks,
-                                      int layout, int c0, int c1, int* list) {
+                                      int layout, int c0, int c1, int* list, bool write = true) {
   const int lane = threadIdx.x & 63;
   const int per_chunk = nK / n_chunks;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -30,7 +31,7 @@ __device__ inline int build_tile_list(const uint8_t* __restrict__ mrow, int nK, 
         const int j = base + lane;
         const bool live = j < j1 && mrow[j] != 0;
         const uint64_t bits = __ballot(live);
-        if (live)
+        if (write && live)
           list[count + __popcll(bits & below)] = j | (0xF << kDescCodeShift) | (c << kDescChunkShift);
         count += __popcll(bits);
       }
@@ -42,7 +43,7 @@ __device__ inline int build_tile_list(const uint8_t* __restrict__ mrow, int nK, 
           for (int g = 0; g < n_chunks; ++g) code |= (mrow[n_chunks * t + g] != 0 ? 1 : 0) << g;
         const bool live = code != 0;
         const uint64_t bits = __ballot(live);
-        if (live)
+        if (write && live)
           list[count + __popcll(bits & below)] = t | (code << kDescCodeShift) | (c << kDescChunkShift);
         count += __popcll(bits);
       }
