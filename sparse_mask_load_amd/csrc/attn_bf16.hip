@@ -86,28 +86,67 @@ __device__ __forceinline__ float other_half(float x) {
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Issue the global->LDS loads of one K or V tile (this wave's share).
-template <int D, int BLK>
-__device__ __forceinline__ void load_tile(const bf16* __restrict__ g, int64_t bh_base, int64_t ss, int S,
-                                          int layout, int n_chunks, int desc, bf16* lds) {
-  using SH = Shape<D, BLK>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Where the rows of one K/V tile live in global memory: row r of the tile is
+// element base + r * row_stride; rows at or beyond `rows` repeat the last
+// valid row (the partial last block of a ragged sequence).
+struct TileSrc {
+  int64_t base;
+  int row_stride;
+  int rows;
+};
+
+__device__ __forceinline__ TileSrc tile_source(int desc, int64_t bh_base, int64_t ss, int S, int layout,
+                                               int n_chunks, int BLK) {
   const int idx = desc & 0xFFFFF;
   const int c = (desc >> kDescChunkShift) & 63;
-#pragma unroll
-  for (int n = 0; n < SH::IPW; ++n) {
-    const int slot0 = (wave * SH::IPW + n) * 64;
-    const int slot = slot0 + lane;
-    const int r = slot / SH::CPR;
-    const int lc = (slot % SH::CPR) ^ chunk_swizzle<D>(r);
-    int64_t pos;
-    if (layout == SA_LAYOUT_CONTIGUOUS)
-      pos = min(idx * BLK + r, S - 1);
-    else
-      pos = c + (int64_t)n_chunks * ((int64_t)idx * BLK + r);
-    __builtin_amdgcn_global_load_lds(g + bh_base + pos * ss + lc * 8, LDS_PTR(void, lds + slot0 * 8), 16, 0, 0);
+  TileSrc t;
+  if (layout == SA_LAYOUT_CONTIGUOUS) {
+    t.base = bh_base + (int64_t)idx * BLK * ss;
+    t.row_stride = (int)ss;
+    t.rows = min(BLK, S - idx * BLK);
+  } else {  // compacted position p of chunk c is token c + n_chunks * p
+    t.base = bh_base + ((int64_t)c + (int64_t)n_chunks * idx * BLK) * ss;
+    t.row_stride = (int)(ss * n_chunks);
+    t.rows = BLK;
   }
+  return t;
 }
+
+// Per-lane part of the tile loads.  Load instruction n of a wave writes the
+// 64 consecutive 16-byte LDS slots (wave*IPW + n)*64 + lane; slot s holds row
+// s / CPR, physical chunk s % CPR, i.e. logical chunk (s % CPR) ^ swizzle(row).
+// For the shapes here the swizzle of row lane_row + n*RPI is the lane's base
+// swizzle XOR a constant of n, so one XOR per instruction finds the chunk.
+template <int D, int BLK>
+struct TileLoader {
+  int lane_row;    // tile row of this lane's slot in instruction 0
+  int lane_chunk;  // logical chunk of that slot, before the per-instruction constant
+  __device__ __forceinline__ void init(int wave, int lane) {
+    using SH = Shape<D, BLK>;
+    constexpr int RPI = 64 / SH::CPR;
+    lane_row = wave * SH::IPW * RPI + lane / SH::CPR;
+    lane_chunk = (lane % SH::CPR) ^ chunk_swizzle<D>(lane_row);
+  }
+  static __device__ __forceinline__ constexpr int chunk_xor(int n) {
+    // swizzle(row + n*RPI) ^ swizzle(row) for rows with bits 0-1 from the lane and IPW % 4 == 0
+    return D == 128 ? (((n >> 1) & 1) | (8 * (n & 1))) : (n & 1);
+  }
+  template <bool MAY_CLAMP>
+  __device__ __forceinline__ void issue(const bf16* __restrict__ g, const TileSrc& src, bf16* lds, int wave) const {
+    using SH = Shape<D, BLK>;
+    constexpr int RPI = 64 / SH::CPR;
+    static_assert(SH::IPW % 4 == 0 || D == 64, "row bits 2-3 of a load instruction must come from n");
+    const bf16* gt = g + src.base;
+    const bool clamp = MAY_CLAMP && src.rows < BLK;
+#pragma unroll
+    for (int n = 0; n < SH::IPW; ++n) {
+      int r = lane_row + n * RPI;
+      if (clamp) r = min(r, src.rows - 1);
+      const uint32_t off = (uint32_t)(r * src.row_stride + ((lane_chunk ^ chunk_xor(n)) << 3));
+      __builtin_amdgcn_global_load_lds(gt + off, LDS_PTR(void, lds + (wave * SH::IPW + n) * 64 * 8), 16, 0, 0);
+    }
+  }
+};
 
 // Online-softmax state of one wave (32 query rows; a lane owns row l % 32).
 template <int ND>
@@ -127,45 +166,54 @@ __device__ __forceinline__ void reset(RowState<ND>& st) {
   st.l = 0.f;
 }
 
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 // One live tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// live_kb: bit kb set when 32-key block kb of the tile holds live keys.
-// ragged: keys at or beyond S (last, partial block) are masked to -inf.
-template <int D, int BLK>
+// GENERAL = false: every 32-key block is live and no key lies beyond S (the
+// common case, straight-line code).  GENERAL = true: live_kb has bit kb set
+// when key block kb holds live keys (striped layout) and `ragged` masks keys
+// at or beyond S (the last, partial block).
+// LDS operand reads are issued two MFMAs ahead of their use.
+template <int D, int BLK, bool GENERAL>
 __device__ __forceinline__ void tile_step(const bf16* __restrict__ Kt, const bf16* __restrict__ Vt,
                                           const bf16x8 (&qf)[D / 16], RowState<D / 32>& st, int live_kb,
                                           bool ragged, int key0, float sl2, int k_off, int k_swz,
                                           const int (&v_off)[2], const int (&v_swz)[2], int v_chunk, int h2,
-                                          bool last, const FwdArgs& a, int64_t bh_base, int next_desc, bf16* kbuf,
-                                          bf16* vbuf) {
+                                          bool last, const FwdArgs& a, const TileLoader<D, BLK>& loader,
+                                          const TileSrc& next, int wave, bf16* kbuf, bf16* vbuf) {
   using SH = Shape<D, BLK>;
+  auto kb_live = [&](int kb) { return !GENERAL || ((live_kb >> kb) & 1); };
+
   f32x16 s[SH::NKB];
 #pragma unroll
   for (int kb = 0; kb < SH::NKB; ++kb) {
-    s[kb] = f32x16{};
-    if ((live_kb >> kb) & 1) {
-      const bf16* kp = Kt + kb * 32 * D + k_off;
+    if (!kb_live(kb)) continue;
+    const bf16* kp = Kt + kb * 32 * D + k_off;
+    bf16x8 kf[SH::NKS];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 kf[SH::NKS / 2];
+    for (int ks = 0; ks < SH::NKS; ++ks) kf[ks] = *(const bf16x8*)(kp + (((2 * ks + h2) ^ k_swz) << 3));
+    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < SH::NKS / 2; ++i) {
-          const int ks = half * (SH::NKS / 2) + i;
-          kf[i] = *(const bf16x8*)(kp + (((2 * ks + h2) ^ k_swz) << 3));
-        }
+    for (int ks = 1; ks < SH::NKS; ++ks) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s[kb], 0, 0, 0);
+    SCHED_GROUP(kSchedDsRead, 2);
 #pragma unroll
-        for (int i = 0; i < SH::NKS / 2; ++i)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[half * (SH::NKS / 2) + i], s[kb], 0, 0, 0);
-      }
+    for (int ks = 0; ks < SH::NKS - 2; ++ks) {
+      SCHED_GROUP(kSchedMfma, 1);
+      SCHED_GROUP(kSchedDsRead, 1);
     }
+    SCHED_GROUP(kSchedMfma, 2);
     __builtin_amdgcn_sched_barrier(0);
   }
 
   // Barrier A: every wave is done reading K of this tile and V of this tile has landed.
   wait_vm();
   __syncthreads();
-  if (!last) load_tile<D, BLK>((const bf16*)a.k, bh_base, a.ss, a.S, a.layout, a.n_chunks, next_desc, kbuf);
+  if (!last) loader.template issue<GENERAL>((const bf16*)a.k, next, kbuf, wave);
 
-  if (ragged) {
+  if (GENERAL && ragged) {
 #pragma unroll
     for (int kb = 0; kb < SH::NKB; ++kb)
 #pragma unroll
@@ -175,9 +223,9 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ Kt, const bf1
   float mx = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < SH::NKB; ++kb) {
-    if (!((live_kb >> kb) & 1)) continue;
+    if (!kb_live(kb)) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
   }
   mx = fmaxf(mx, other_half(mx)) * sl2;
   st.m_true = fmaxf(st.m_true, mx);
@@ -195,55 +243,68 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ Kt, const bf1
 
 #pragma unroll
   for (int kb = 0; kb < SH::NKB; ++kb) {
-    if ((live_kb >> kb) & 1) {
-      bf16x8 pb[2];
+    if (!kb_live(kb)) continue;
+    bf16x8 pb[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -m_ref));
+    for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -m_ref));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lsum0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0][2 * e], pb[0][2 * e + 1]}, ones, lsum0, false);
-        lsum1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][2 * e], pb[1][2 * e + 1]}, ones, lsum1, false);
-      }
+    for (int e = 0; e < 4; ++e) {
+      lsum0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0][2 * e], pb[0][2 * e + 1]}, ones, lsum0, false);
+      lsum1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][2 * e], pb[1][2 * e + 1]}, ones, lsum1, false);
+    }
+    bf16x8 va[2][SH::ND];
 #pragma unroll
-      for (int stp = 0; stp < 2; ++stp) {
-        const bf16* vp = Vt + (kb * 32 + 16 * stp) * D;
-        bf16x8 va[SH::ND];
+    for (int stp = 0; stp < 2; ++stp) {
+      const bf16* vp = Vt + (kb * 32 + 16 * stp) * D;
 #pragma unroll
-        for (int d = 0; d < SH::ND; ++d) {
-          const int ch = 4 * d + v_chunk;
-          const bf16x4 lo =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_off[0] + ((ch ^ v_swz[0]) << 3)));
-          const bf16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_off[1] + ((ch ^ v_swz[1]) << 3)));
-          va[d] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int d = 0; d < SH::ND; ++d)
-          st.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[d], pb[stp], st.acc[d], 0, 0, 0);
+      for (int d = 0; d < SH::ND; ++d) {
+        const int ch = 4 * d + v_chunk;
+        const bf16x4 lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_off[0] + ((ch ^ v_swz[0]) << 3)));
+        const bf16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_off[1] + ((ch ^ v_swz[1]) << 3)));
+        va[stp][d] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int stp = 0; stp < 2; ++stp)
+#pragma unroll
+      for (int d = 0; d < SH::ND; ++d)
+        st.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[stp][d], pb[stp], st.acc[d], 0, 0, 0);
+    // two transposed reads per MFMA operand, issued one operand ahead
+    SCHED_GROUP(kSchedDsRead, 4);
+#pragma unroll
+    for (int i = 0; i < 2 * SH::ND - 2; ++i) {
+      SCHED_GROUP(kSchedMfma, 1);
+      SCHED_GROUP(kSchedDsRead, 2);
+    }
+    SCHED_GROUP(kSchedMfma, 2);
   }
   st.l += lsum0 + lsum1;
 
   // Barrier B: every wave is done reading V of this tile and K of the next tile has landed.
   wait_vm();
   __syncthreads();
-  if (!last) load_tile<D, BLK>((const bf16*)a.v, bh_base, a.ss, a.S, a.layout, a.n_chunks, next_desc, vbuf);
+  if (!last) loader.template issue<GENERAL>((const bf16*)a.v, next, vbuf, wave);
 }
 
-template <int D, int BLK>
+// GENERAL: the problem has striped chunks or a partial last block, so a tile
+// may have dead 32-key groups or keys beyond S; otherwise every tile is full.
+template <int D, int BLK, bool GENERAL>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(FwdArgs a) {
   using SH = Shape<D, BLK>;
   __shared__ __attribute__((aligned(1024))) bf16 sK[SH::TILE];
   __shared__ __attribute__((aligned(1024))) bf16 sV[SH::TILE];
   __shared__ int sList[kMaxTilesPerRow];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
   const bool full = a.o != nullptr;
   const bool striped = a.layout == SA_LAYOUT_STRIPED;
-  const int kb_div = striped ? SH::NKB / a.n_chunks : SH::NKB;  // key blocks per liveness group
+  const int kb_div = striped ? SH::NKB / a.n_chunks : SH::NKB;
+  TileLoader<D, BLK> loader;
+  loader.init(wave, lane);  // key blocks per liveness group
   const bf16* __restrict__ gQ = (const bf16*)a.q;
 
   // Per-lane LDS operand offsets (independent of tile, key block and step).
@@ -316,9 +377,10 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
     };
 
     if (n_tiles > 0) {
-      const int d0 = __builtin_amdgcn_readfirstlane(list[0]);
-      load_tile<D, BLK>((const bf16*)a.k, bh_base, a.ss, a.S, a.layout, a.n_chunks, d0, sK);
-      load_tile<D, BLK>((const bf16*)a.v, bh_base, a.ss, a.S, a.layout, a.n_chunks, d0, sV);
+      const TileSrc src0 = tile_source(__builtin_amdgcn_readfirstlane(list[0]), bh_base, a.ss, a.S, a.layout,
+                                       a.n_chunks, BLK);
+      loader.template issue<GENERAL>((const bf16*)a.k, src0, sK, wave);
+      loader.template issue<GENERAL>((const bf16*)a.v, src0, sV, wave);
       wait_vm();
       __syncthreads();
     }
@@ -339,8 +401,10 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int kb = 0; kb < SH::NKB; ++kb) live_kb |= ((code >> (kb / kb_div)) & 1) << kb;
       }
-      tile_step<D, BLK>(sK, sV, qf, st, live_kb, !striped && key0 + BLK > a.S, key0, sl2, k_off, k_swz, v_off,
-                        v_swz, v_chunk, h2, last, a, bh_base, next_desc, sK, sV);
+      const bool ragged = !striped && key0 + BLK > a.S;
+      const TileSrc next = tile_source(next_desc, bh_base, a.ss, a.S, a.layout, a.n_chunks, BLK);
+      tile_step<D, BLK, GENERAL>(sK, sV, qf, st, live_kb, ragged, key0, sl2, k_off, k_swz, v_off, v_swz, v_chunk,
+                                 h2, last, a, loader, next, wave, sK, sV);
     }
 
     if (!full) {
@@ -374,18 +438,22 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 int attn_bf16_wg_per_cu(int block) { return block >= 128 ? 2 : 4; }
 
-hipError_t launch_attn_bf16(const FwdArgs& a, int D, int block, hipStream_t stream) {
-  if (D == 128 && block == 128)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 128>), dim3(a.num_bins), dim3(256), 0, stream, a);
-  else if (D == 64 && block == 128)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 128>), dim3(a.num_bins), dim3(256), 0, stream, a);
-  else if (D == 128 && block == 64)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 64>), dim3(a.num_bins), dim3(128), 0, stream, a);
-  else if (D == 64 && block == 64)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 64>), dim3(a.num_bins), dim3(128), 0, stream, a);
+template <int D, int BLK>
+hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
+  const bool general = a.layout == SA_LAYOUT_STRIPED || a.S % BLK != 0;
+  if (general)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, true>), dim3(a.num_bins), dim3(BLK * 2), 0, stream, a);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false>), dim3(a.num_bins), dim3(BLK * 2), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const FwdArgs& a, int D, int block, hipStream_t stream) {
+  if (D == 128 && block == 128) return launch_variant<128, 128>(a, stream);
+  if (D == 64 && block == 128) return launch_variant<64, 128>(a, stream);
+  if (D == 128 && block == 64) return launch_variant<128, 64>(a, stream);
+  if (D == 64 && block == 64) return launch_variant<64, 64>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sa
