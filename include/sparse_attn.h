@@ -135,8 +135,9 @@ typedef enum {
  *  synchronises the stream.
  *  TOPK: runs the indexer and top-k selection on the GPU; asynchronous.
  *  num_bins: persistent workgroups; 0 picks one per resident workgroup slot
- *  (bf16: 2 per compute unit for block 128, 4 for block 64; f32: 1).  out (host): receives the plan.  Returns SA_ERR_NOMEM if the
- *  plan's device buffers cannot be allocated. */
+ *  (bf16: 1 per compute unit for block 128, 2 for block 64; f32: 1).
+ *  out (host): receives the plan.  Returns SA_ERR_NOMEM if the plan's device
+ *  buffers cannot be allocated. */
 sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_t num_bins,
                            int32_t order, sa_plan** out, hipStream_t stream);
 

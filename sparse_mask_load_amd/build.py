@@ -39,9 +39,18 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP toolchain is required to build libsparse_attn.so")
 
 
+# Per-source code-generation options.
+EXTRA = {
+    # matrix-core results land in ordinary vector registers, where the softmax reads the scores
+    # and from where the output is written; without this the compiler picks the accumulator
+    # file and copies every score tile across
+    "attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = (res.stdout + res.stderr).strip()
     # the host pass does not know the device-only feature flag; that warning is expected

@@ -10,12 +10,14 @@
 // range into one state and writes O / l; partial mode writes each chunk's
 // (O unnormalised, m, l) and resets the state (the ring step's output).
 //
-// gfx950 mapping (one wave = 32 query rows, BLOCK/32 waves per workgroup):
-//  * The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows are
-//    the A operand read from LDS, Q^T the B operand kept in registers for the
-//    whole item.  In the accumulator layout a lane then owns one query column
-//    and 16 keys per 32-key block, so the row max and row sum are in-lane
-//    reductions plus one v_permlane32_swap between the two half-waves.
+// gfx950 mapping (a wave owns 32 query rows and one half of the keys of every
+// tile; two waves per SIMD, so the matrix cores run one wave's MFMAs while the
+// other wave does its softmax arithmetic):
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows are the A operand read
+//    from LDS, Q^T the B operand kept in registers for the whole item.  In the
+//    accumulator layout a lane owns one query column and 16 keys per 32-key
+//    block, so the row max and row sum are in-lane reductions plus one
+//    v_permlane32_swap between the two half-waves.
 //  * K rows are loaded permuted within each 32-key block (row bits 2 and 3
 //    swapped) so that accumulator register r of half h holds key
 //    16*(r/8) + 8*h + r%8: each lane's 8 consecutive P values are then a
@@ -23,13 +25,19 @@
 //    two ds_read_b64_tr_b16 transposed reads of the row-major V tile.  O^T's
 //    accumulator again gives a lane one query column, so the alpha rescale is
 //    in-lane too.
-//  * One K and one V tile live in LDS (72 KiB with the tile list), so two
-//    workgroups share a compute unit and every SIMD holds two waves: one
-//    wave's softmax (VALU) runs while the other's MFMAs execute.  Tiles are
-//    filled by global_load_lds_dwordx4 (no VGPR staging) on a two-barrier
-//    schedule: K of tile t+1 streams in during the softmax and P V of tile t,
-//    V of tile t+1 during S of tile t+1.  16-byte chunks are XOR-swizzled per
-//    row so the operand reads above are free of bank conflicts.
+//  * The two key halves of a row keep separate online-softmax states (each is
+//    a flash-attention pass over a disjoint key subset) and are merged through
+//    LDS with the same rule that merges chunks, when a chunk is flushed and at
+//    the end of the item.
+//  * Each wave is also software-pipelined: per 32-key block it exponentiates
+//    block kb of tile t, issues the S MFMAs of block kb of tile t+1 and the
+//    P V MFMAs of block kb of tile t, all in one basic block.
+//  * K and V tiles are double-buffered in LDS (128 KiB for 128-key tiles, four
+//    separate arrays so that the compiler can tell operand reads from loads in
+//    flight) and filled by global_load_lds_dwordx4 (no VGPR staging) one tile
+//    ahead, in slices spread over the key blocks, with one workgroup barrier
+//    per tile.  16-byte chunks are XOR-swizzled per row so that the operand
+//    reads are free of bank conflicts.
 //  * exp is exp2 on scores pre-multiplied by scale*log2(e).  The reference max
 //    used in the exponent only moves when a row's max grows by more than 2^8
 //    (the result O/l does not depend on the reference), so O is rarely
@@ -37,6 +45,8 @@
 //    converted to it, in natural-log units.  The row sum adds the bf16-rounded
 //    P values that also feed P V (v_dot2c_f32_bf16).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "internal.h"
 #include "kernel_common.h"
@@ -58,23 +68,42 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units: P values stay below 2^8
 
 template <int D, int BLK>
 struct Shape {
-  static constexpr int NW = BLK / 32;    // waves per workgroup
+  static constexpr int NRG = BLK / 32;   // 32-row groups of a Q block
+  static constexpr int NW = 2 * NRG;     // waves per workgroup: row group x key half
   static constexpr int NKB = BLK / 32;   // 32-key blocks per tile
+  static constexpr int NKBW = NKB / 2;   // key blocks of one wave (its half of the tile)
   static constexpr int ND = D / 32;      // 32-wide head-dim blocks
   static constexpr int NKS = D / 16;     // k-steps of S^T
   static constexpr int TILE = BLK * D;
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int IPW = BLK * CPR / (64 * NW);  // load instructions per wave per tile
-  static constexpr int WG_PER_CU = BLK >= 128 ? 2 : 4;
+  static constexpr int WG_PER_CU = 8 / NW;           // two waves per SIMD
+  static constexpr int RB = ND / 2;                  // head-dim blocks per merge round
 };
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time loop).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 // Row-dependent XOR applied to the 16-byte chunk index of a tile row in LDS.
+// The LDS serves 256 bytes (64 banks) per clock: 16 lanes of a ds_read_b128 or
+// 32 lanes of a ds_read_b64_tr_b16.  The K-operand read touches 16 different
+// rows (bits 0-3 of the row index all vary) at one logical chunk, so the XOR
+// must be a bijection on row % 16; the V^T read touches 4 consecutive rows
+// (4*i .. 4*i+3) at 4 consecutive chunks, so those rows need different chunk
+// bits 2-3 (D = 128; for D = 64 two rows share a 256-byte bank line, so rows of
+// equal parity need different chunk bit 2).
 template <int D>
 __device__ __forceinline__ int chunk_swizzle(int row) {
   if constexpr (D == 128)
-    return 2 * (row & 3) + ((row >> 3) & 1) + 8 * ((row >> 2) & 1);
+    return 4 * (row & 3) + ((row >> 2) & 3);
   else
-    return 2 * (row & 3) + ((row >> 3) & 1);
+    return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
 }
 
 // Value held by lane l ^ 32.
@@ -116,34 +145,47 @@ __device__ __forceinline__ TileSrc tile_source(int desc, int64_t bh_base, int64_
 // 64 consecutive 16-byte LDS slots (wave*IPW + n)*64 + lane; slot s holds row
 // s / CPR, physical chunk s % CPR, i.e. logical chunk (s % CPR) ^ swizzle(row).
 // For the shapes here the swizzle of row lane_row + n*RPI is the lane's base
-// swizzle XOR a constant of n, so one XOR per instruction finds the chunk.
+// swizzle XOR a constant of n, so the byte offset of every slot in the tile
+// depends only on the row stride and is computed once per item.  The loads
+// are buffer loads through a per-tile resource whose base is the tile's first
+// row, so no vector address arithmetic is left per tile.
 template <int D, int BLK>
 struct TileLoader {
+  static constexpr int IPW = Shape<D, BLK>::IPW;
+  static constexpr int RPI = 64 / Shape<D, BLK>::CPR;  // rows per load instruction
   int lane_row;    // tile row of this lane's slot in instruction 0
   int lane_chunk;  // logical chunk of that slot, before the per-instruction constant
+  uint32_t voff[IPW];
   __device__ __forceinline__ void init(int wave, int lane) {
-    using SH = Shape<D, BLK>;
-    constexpr int RPI = 64 / SH::CPR;
-    lane_row = wave * SH::IPW * RPI + lane / SH::CPR;
-    lane_chunk = (lane % SH::CPR) ^ chunk_swizzle<D>(lane_row);
+    lane_row = wave * IPW * RPI + lane / Shape<D, BLK>::CPR;
+    lane_chunk = (lane % Shape<D, BLK>::CPR) ^ chunk_swizzle<D>(lane_row);
   }
   static __device__ __forceinline__ constexpr int chunk_xor(int n) {
-    // swizzle(row + n*RPI) ^ swizzle(row) for rows with bits 0-1 from the lane and IPW % 4 == 0
-    return D == 128 ? (((n >> 1) & 1) | (8 * (n & 1))) : (n & 1);
+    // swizzle(lane_row + n*RPI) ^ swizzle(lane_row): row bits below log2(RPI) come from the lane,
+    // the bits above from wave*IPW + n, whose low bits are those of n (IPW is a multiple of 4
+    // for D = 128 and of 2 for D = 64, the bits the swizzle reads)
+    return D == 128 ? (n & 3) : 2 * (n & 1);
   }
-  template <bool MAY_CLAMP>
+  __device__ __forceinline__ uint32_t slot_offset(int row, int n, int row_stride) const {
+    return (uint32_t)(row * row_stride + ((lane_chunk ^ chunk_xor(n)) << 3)) * 2u;
+  }
+  // Per-item byte offsets of this lane's slots (rows are row_stride elements apart).
+  __device__ __forceinline__ void set_stride(int row_stride) {
+    static_assert(IPW % (D == 128 ? 4 : 2) == 0, "row bits of a load instruction above the lane bits must come from n");
+#pragma unroll
+    for (int n = 0; n < IPW; ++n) voff[n] = slot_offset(lane_row + n * RPI, n, row_stride);
+  }
+  // Issues load instructions n0 .. n1-1 of this wave (all of them by default).
+  // Rows at or beyond src.rows (partial last block) repeat the last valid row.
+  template <bool MAY_CLAMP, int N0 = 0, int N1 = IPW>
   __device__ __forceinline__ void issue(const bf16* __restrict__ g, const TileSrc& src, bf16* lds, int wave) const {
-    using SH = Shape<D, BLK>;
-    constexpr int RPI = 64 / SH::CPR;
-    static_assert(SH::IPW % 4 == 0 || D == 64, "row bits 2-3 of a load instruction must come from n");
-    const bf16* gt = g + src.base;
+    const uint32_t bytes = (uint32_t)((src.rows - 1) * src.row_stride + D) * 2u;  // extent of the valid rows
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(g + src.base), 0, bytes, 0x00020000);
     const bool clamp = MAY_CLAMP && src.rows < BLK;
 #pragma unroll
-    for (int n = 0; n < SH::IPW; ++n) {
-      int r = lane_row + n * RPI;
-      if (clamp) r = min(r, src.rows - 1);
-      const uint32_t off = (uint32_t)(r * src.row_stride + ((lane_chunk ^ chunk_xor(n)) << 3));
-      __builtin_amdgcn_global_load_lds(gt + off, LDS_PTR(void, lds + (wave * SH::IPW + n) * 64 * 8), 16, 0, 0);
+    for (int n = N0; n < N1; ++n) {
+      const uint32_t off = clamp ? slot_offset(min(lane_row + n * RPI, src.rows - 1), n, src.row_stride) : voff[n];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, lds + (wave * IPW + n) * 64 * 8), 16, off, 0, 0, 0);
     }
   }
 };
@@ -166,66 +208,88 @@ __device__ __forceinline__ void reset(RowState<ND>& st) {
   st.l = 0.f;
 }
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
-
-// One live tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// GENERAL = false: every 32-key block is live and no key lies beyond S (the
-// common case, straight-line code).  GENERAL = true: live_kb has bit kb set
-// when key block kb holds live keys (striped layout) and `ragged` masks keys
-// at or beyond S (the last, partial block).
-// LDS operand reads are issued two MFMAs ahead of their use.
-template <int D, int BLK, bool GENERAL>
-__device__ __forceinline__ void tile_step(const bf16* __restrict__ Kt, const bf16* __restrict__ Vt,
-                                          const bf16x8 (&qf)[D / 16], RowState<D / 32>& st, int live_kb,
-                                          bool ragged, int key0, float sl2, int k_off, int k_swz,
-                                          const int (&v_off)[2], const int (&v_swz)[2], int v_chunk, int h2,
-                                          bool last, const FwdArgs& a, const TileLoader<D, BLK>& loader,
-                                          const TileSrc& next, int wave, bf16* kbuf, bf16* vbuf) {
-  using SH = Shape<D, BLK>;
-  auto kb_live = [&](int kb) { return !GENERAL || ((live_kb >> kb) & 1); };
-
-  f32x16 s[SH::NKB];
+// Per-lane LDS operand geometry (independent of tile, key block and step);
+// key block j of a wave is block kb0 + j of the tile.
+template <int D>
+struct OperandLanes {
+  int k_off, k_swz, h2;
+  int v_off[2], v_swz[2], v_chunk;
+  __device__ __forceinline__ void init(int lane, int kb0) {
+    h2 = lane >> 5;
+    const int l32 = lane & 31;
+    const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);  // bits 2,3 swapped
+    k_off = (kb0 * 32 + krow) * D;
+    k_swz = chunk_swizzle<D>(krow);
 #pragma unroll
-  for (int kb = 0; kb < SH::NKB; ++kb) {
-    if (!kb_live(kb)) continue;
-    const bf16* kp = Kt + kb * 32 * D + k_off;
-    bf16x8 kf[SH::NKS];
-#pragma unroll
-    for (int ks = 0; ks < SH::NKS; ++ks) kf[ks] = *(const bf16x8*)(kp + (((2 * ks + h2) ^ k_swz) << 3));
-    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], f32x16{}, 0, 0, 0);
-#pragma unroll
-    for (int ks = 1; ks < SH::NKS; ++ks) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s[kb], 0, 0, 0);
-    SCHED_GROUP(kSchedDsRead, 2);
-#pragma unroll
-    for (int ks = 0; ks < SH::NKS - 2; ++ks) {
-      SCHED_GROUP(kSchedMfma, 1);
-      SCHED_GROUP(kSchedDsRead, 1);
+    for (int rr = 0; rr < 2; ++rr) {
+      const int vrow = 8 * h2 + 4 * rr + ((lane & 15) >> 2);
+      v_off[rr] = (kb0 * 32 + vrow) * D + 4 * (lane & 1);
+      v_swz[rr] = chunk_swizzle<D>(vrow);
     }
-    SCHED_GROUP(kSchedMfma, 2);
-    __builtin_amdgcn_sched_barrier(0);
+    v_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   }
+  // K rows of 32-key block kb at k-step ks (A operand of S^T).
+  __device__ __forceinline__ bf16x8 k_frag(const bf16* Kt, int kb, int ks) const {
+    return *(const bf16x8*)(Kt + kb * 32 * D + k_off + (((2 * ks + h2) ^ k_swz) << 3));
+  }
+  // V^T rows of head-dim block d for the 16-key step `half` of key block kb (A operand of O^T).
+  __device__ __forceinline__ bf16x8 v_frag(const bf16* Vt, int kb, int half, int d) const {
+    const bf16* vp = Vt + (kb * 32 + 16 * half) * D;
+    const int ch = 4 * d + v_chunk;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_off[0] + ((ch ^ v_swz[0]) << 3)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_off[1] + ((ch ^ v_swz[1]) << 3)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
 
-  // Barrier A: every wave is done reading K of this tile and V of this tile has landed.
-  wait_vm();
-  __syncthreads();
-  if (!last) loader.template issue<GENERAL>((const bf16*)a.k, next, kbuf, wave);
+// S^T = K Q^T of the wave's key blocks of one tile, k-step major: one MFMA per
+// live 32-key block per step, the K fragments of the next step read while the
+// current MFMAs run.
+template <int D, int BLK, bool GENERAL>
+__device__ __forceinline__ void tile_scores(const bf16* __restrict__ Kt, const bf16x8 (&qf)[D / 16],
+                                            const OperandLanes<D>& ol, int live_w, f32x16 (&s)[BLK / 64]) {
+  using SH = Shape<D, BLK>;
+  constexpr int NB = SH::NKBW, NKS = SH::NKS;
+  auto live = [&](int j) { return !GENERAL || ((live_w >> j) & 1); };
+  bf16x8 kf[2][NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    if (live(j)) kf[0][j] = ol.k_frag(Kt, j, 0);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (ks + 1 < NKS) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        if (live(j)) kf[(ks + 1) & 1][j] = ol.k_frag(Kt, j, ks + 1);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (live(j))
+        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks & 1][j], qf[ks], ks == 0 ? f32x16{} : s[j], 0, 0, 0);
+  }
+}
 
+// Row max of the wave's tile scores (after masking keys beyond S on a ragged
+// tile) and the lazy move of the exponent's reference max.  key0 is the first
+// key of the wave's first block.  Returns the reference to use.
+template <int D, int BLK, bool GENERAL>
+__device__ __forceinline__ float tile_max(f32x16 (&s)[BLK / 64], RowState<D / 32>& st, int live_w, bool ragged,
+                                          int key0, int S, int h2, float sl2) {
+  using SH = Shape<D, BLK>;
+  auto live = [&](int j) { return !GENERAL || ((live_w >> j) & 1); };
   if (GENERAL && ragged) {
 #pragma unroll
-    for (int kb = 0; kb < SH::NKB; ++kb)
+    for (int j = 0; j < SH::NKBW; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (key0 + kb * 32 + 16 * (r >> 3) + 8 * h2 + (r & 7) >= a.S) s[kb][r] = kNegInf;
+        if (key0 + j * 32 + 16 * (r >> 3) + 8 * h2 + (r & 7) >= S) s[j][r] = kNegInf;
   }
   float mx = kNegInf;
 #pragma unroll
-  for (int kb = 0; kb < SH::NKB; ++kb) {
-    if (!kb_live(kb)) continue;
+  for (int j = 0; j < SH::NKBW; ++j) {
+    if (!live(j)) continue;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[j][r], s[j][r + 1]));
   }
   mx = fmaxf(mx, other_half(mx)) * sl2;
   st.m_true = fmaxf(st.m_true, mx);
@@ -237,89 +301,115 @@ __device__ __forceinline__ void tile_step(const bf16* __restrict__ Kt, const bf1
 #pragma unroll
     for (int d = 0; d < SH::ND; ++d) st.acc[d] *= alpha;
   }
-  const float m_ref = st.m_ref;
+  return st.m_ref;
+}
+
+// P of one key block as two bf16x8 B operands (keys 16*half + 8*h2 + 0..7),
+// accumulating the row sum of the rounded values.
+__device__ __forceinline__ void tile_probs(const f32x16& s, float sl2, float m_ref, bf16x8 (&pb)[2], float& lsum0,
+                                           float& lsum1) {
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  float lsum0 = 0.f, lsum1 = 0.f;
-
 #pragma unroll
-  for (int kb = 0; kb < SH::NKB; ++kb) {
-    if (!kb_live(kb)) continue;
-    bf16x8 pb[2];
+  for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[r], sl2, -m_ref));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -m_ref));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      lsum0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0][2 * e], pb[0][2 * e + 1]}, ones, lsum0, false);
-      lsum1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][2 * e], pb[1][2 * e + 1]}, ones, lsum1, false);
-    }
-    bf16x8 va[2][SH::ND];
-#pragma unroll
-    for (int stp = 0; stp < 2; ++stp) {
-      const bf16* vp = Vt + (kb * 32 + 16 * stp) * D;
-#pragma unroll
-      for (int d = 0; d < SH::ND; ++d) {
-        const int ch = 4 * d + v_chunk;
-        const bf16x4 lo =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_off[0] + ((ch ^ v_swz[0]) << 3)));
-        const bf16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_off[1] + ((ch ^ v_swz[1]) << 3)));
-        va[stp][d] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-    }
-#pragma unroll
-    for (int stp = 0; stp < 2; ++stp)
-#pragma unroll
-      for (int d = 0; d < SH::ND; ++d)
-        st.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[stp][d], pb[stp], st.acc[d], 0, 0, 0);
-    // two transposed reads per MFMA operand, issued one operand ahead
-    SCHED_GROUP(kSchedDsRead, 4);
-#pragma unroll
-    for (int i = 0; i < 2 * SH::ND - 2; ++i) {
-      SCHED_GROUP(kSchedMfma, 1);
-      SCHED_GROUP(kSchedDsRead, 2);
-    }
-    SCHED_GROUP(kSchedMfma, 2);
+  for (int e = 0; e < 4; ++e) {
+    lsum0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0][2 * e], pb[0][2 * e + 1]}, ones, lsum0, false);
+    lsum1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][2 * e], pb[1][2 * e + 1]}, ones, lsum1, false);
   }
-  st.l += lsum0 + lsum1;
+}
 
-  // Barrier B: every wave is done reading V of this tile and K of the next tile has landed.
-  wait_vm();
-  __syncthreads();
-  if (!last) loader.template issue<GENERAL>((const bf16*)a.v, next, vbuf, wave);
+// Folds the key-half-1 state of every row group into the key-half-0 wave of the
+// same rows (the merge rule of two partials over disjoint keys).  Called by all
+// waves of the workgroup at the same point (it has barriers); kscr and mscr are
+// LDS buffers that no wave reads or loads into meanwhile.  On return the
+// half-0 wave holds, in the true-max basis, acc (unnormalised O^T), m (true row
+// max, log2 units, -inf for a row without keys) and l_row (full row sum).
+template <int D, int BLK>
+__device__ __forceinline__ void merge_halves(RowState<D / 32>& st, float& m, float& l_row, float* kscr, float* mscr,
+                                             int rg, int kh, int lane) {
+  using SH = Shape<D, BLK>;
+  constexpr int ND = SH::ND, RB = SH::RB;
+  const bool any = st.m_true != kNegInf;
+  const float corr = any ? __builtin_amdgcn_exp2f(st.m_ref - st.m_true) : 0.f;
+  m = st.m_true;
+  l_row = (st.l + other_half(st.l)) * corr;
+#pragma unroll
+  for (int d = 0; d < ND; ++d) st.acc[d] *= corr;
+  const int l32 = lane & 31;
+  float fa = 1.f, fb = 0.f;
+#pragma unroll
+  for (int round = 0; round < ND / RB; ++round) {
+    // kscr layout: [row group][block i of the round][group g of 4 registers][lane] f32x4
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v4 = {st.acc[round * RB + i][4 * g], st.acc[round * RB + i][4 * g + 1],
+                            st.acc[round * RB + i][4 * g + 2], st.acc[round * RB + i][4 * g + 3]};
+          *(f32x4*)(kscr + (((rg * RB + i) * 4 + g) * 64 + lane) * 4) = v4;
+        }
+      if (round == 0) mscr[rg * 64 + lane] = lane < 32 ? m : l_row;
+    }
+    __syncthreads();
+    if (kh == 0) {
+      if (round == 0) {
+        const float mo = mscr[rg * 64 + l32], lo = mscr[rg * 64 + 32 + l32];
+        const float mn = fmaxf(m, mo);
+        fa = mn == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        fb = mn == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+        l_row = l_row * fa + lo * fb;
+        m = mn;
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v4 = *(const f32x4*)(kscr + (((rg * RB + i) * 4 + g) * 64 + lane) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            st.acc[round * RB + i][4 * g + e] = st.acc[round * RB + i][4 * g + e] * fa + v4[e] * fb;
+        }
+    }
+    __syncthreads();
+  }
 }
 
 // GENERAL: the problem has striped chunks or a partial last block, so a tile
 // may have dead 32-key groups or keys beyond S; otherwise every tile is full.
 template <int D, int BLK, bool GENERAL>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_kernel(FwdArgs a) {
   using SH = Shape<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) bf16 sK[SH::TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[SH::TILE];
+  static_assert(SH::NW * 64 == BLK * 4, "launch bounds");
+  constexpr int NKB = SH::NKB, NB = SH::NKBW, ND = SH::ND, NKS = SH::NKS, NRG = SH::NRG;
+  static_assert(SH::TILE * 2 >= NRG * SH::RB * 4096, "merge round must fit in a K buffer");
+  static_assert(SH::TILE * 2 >= NRG * 64 * 4, "merge statistics must fit in a V buffer");
+  // Four separate LDS arrays (not one indexed array): the compiler can then
+  // prove that operand reads of one buffer do not alias the tile loads in
+  // flight into another, and need not wait for those loads to land.
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[SH::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[SH::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[SH::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[SH::TILE];
   __shared__ int sList[kMaxTilesPerRow];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave % NRG, kh = wave / NRG;  // row group, key half
+  const int kb0 = kh * NB;                     // first key block of this wave
   const int h2 = lane >> 5, l32 = lane & 31;
   const bool full = a.o != nullptr;
   const bool striped = a.layout == SA_LAYOUT_STRIPED;
-  const int kb_div = striped ? SH::NKB / a.n_chunks : SH::NKB;
+  const int kb_div = striped ? NKB / a.n_chunks : NKB;  // key blocks per liveness group
   TileLoader<D, BLK> loader;
-  loader.init(wave, lane);  // key blocks per liveness group
+  loader.init(wave, lane);
+  loader.set_stride(striped ? (int)(a.ss * a.n_chunks) : (int)a.ss);
+  OperandLanes<D> ol;
+  ol.init(lane, kb0);
   const bf16* __restrict__ gQ = (const bf16*)a.q;
-
-  // Per-lane LDS operand offsets (independent of tile, key block and step).
-  const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);  // bits 2,3 swapped
-  const int k_off = krow * D;
-  const int k_swz = chunk_swizzle<D>(krow);
-  int v_off[2], v_swz[2];
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int vrow = 8 * h2 + 4 * rr + ((lane & 15) >> 2);
-    v_off[rr] = vrow * D + 4 * (lane & 1);
-    v_swz[rr] = chunk_swizzle<D>(vrow);
-  }
-  const int v_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-
+  const bf16* __restrict__ gK = (const bf16*)a.k;
+  const bf16* __restrict__ gV = (const bf16*)a.v;
   const int bin = blockIdx.x;
   const int p_begin = a.bin_ptr[bin], p_end = a.bin_ptr[bin + 1];
   const float sl2 = a.scale_log2;
@@ -333,89 +423,161 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int64_t bh_base = (int64_t)b * a.sb + (int64_t)h * a.sh;
 
     // Q^T operand of this wave's 32 rows: lane holds row q0 + l32, dims 16*ks + 8*h2 .. +7.
-    const int qrow = qb * BLK + wave * 32 + l32;
+    const int qrow = qb * BLK + rg * 32 + l32;
     const int qrow_c = min(qrow, a.S - 1);
-    bf16x8 qf[SH::NKS];
+    bf16x8 qf[NKS];
     {
       const bf16* qp = gQ + bh_base + (int64_t)qrow_c * a.ss + 8 * h2;
 #pragma unroll
-      for (int ks = 0; ks < SH::NKS; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
     }
 
-    __syncthreads();  // every wave is done with the previous item's list and tiles
+    __syncthreads();  // every wave is done with the previous item's list, tiles and merge buffers
     // every wave counts the live tiles; wave 0 also writes the list
     const int n_tiles = build_tile_list(a.mask + (int64_t)item * a.nK, a.nK, a.n_chunks, a.layout, a.c0, a.c1,
                                         sList, wave == 0);
     __syncthreads();
-    const int* list = sList;
 
-    RowState<SH::ND> st;
+    RowState<ND> st;
     reset(st);
     int cur_chunk = a.c0;
 
-    auto flush_partial = [&](int chunk) {
-      const bool any = st.m_true != kNegInf;
-      const float corr = any ? __builtin_amdgcn_exp2f(st.m_ref - st.m_true) : 0.f;
-      const float l_tot = (st.l + other_half(st.l)) * corr;
-      if (qrow < a.S) {
+    // Merges the two key halves and writes chunk `chunk`'s partial (O in the
+    // true-max basis, m in natural-log units, l), then resets the state.
+    auto flush_partial = [&](int chunk, float* kscr, float* mscr) {
+      float m, l_row;
+      merge_halves<D, BLK>(st, m, l_row, kscr, mscr, rg, kh, lane);
+      if (kh == 0 && qrow < a.S) {
         const int64_t prow = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + qrow;
         float* op = a.o_part + prow * D;
 #pragma unroll
-        for (int d = 0; d < SH::ND; ++d)
+        for (int d = 0; d < ND; ++d)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const f32x4 v4 = {st.acc[d][4 * g] * corr, st.acc[d][4 * g + 1] * corr, st.acc[d][4 * g + 2] * corr,
-                              st.acc[d][4 * g + 3] * corr};
+            const f32x4 v4 = {st.acc[d][4 * g], st.acc[d][4 * g + 1], st.acc[d][4 * g + 2], st.acc[d][4 * g + 3]};
             *(f32x4*)(op + d * 32 + 8 * g + 4 * h2) = v4;
           }
         if (h2 == 0) {
-          a.m_part[prow] = any ? st.m_true * kLn2 : kNegInf;
-          a.l_part[prow] = l_tot;
+          a.m_part[prow] = m == kNegInf ? kNegInf : m * kLn2;
+          a.l_part[prow] = l_row;
         }
       }
       reset(st);
     };
+    // live bits of this wave's key blocks of a tile
+    auto live_of = [&](int desc) {
+      int live = (1 << NB) - 1;
+      if (striped) {
+        const int code = (desc >> kDescCodeShift) & 15;
+        live = 0;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) live |= ((code >> ((kb0 + j) / kb_div)) & 1) << j;
+      }
+      return live;
+    };
+    auto src_of = [&](int desc) { return tile_source(desc, bh_base, a.ss, a.S, a.layout, a.n_chunks, BLK); };
 
+    // Prologue: K and V of tile 0, K of tile 1; S of tile 0.
+    f32x16 s[NB];
     if (n_tiles > 0) {
-      const TileSrc src0 = tile_source(__builtin_amdgcn_readfirstlane(list[0]), bh_base, a.ss, a.S, a.layout,
-                                       a.n_chunks, BLK);
-      loader.template issue<GENERAL>((const bf16*)a.k, src0, sK, wave);
-      loader.template issue<GENERAL>((const bf16*)a.v, src0, sV, wave);
+      const int d0 = __builtin_amdgcn_readfirstlane(sList[0]);
+      loader.template issue<GENERAL>(gK, src_of(d0), sK0, wave);
+      loader.template issue<GENERAL>(gV, src_of(d0), sV0, wave);
+      if (n_tiles > 1)
+        loader.template issue<GENERAL>(gK, src_of(__builtin_amdgcn_readfirstlane(sList[1])), sK1, wave);
       wait_vm();
       __syncthreads();
+      tile_scores<D, BLK, GENERAL>(sK0, qf, ol, live_of(d0), s);
     }
 
-    for (int t = 0; t < n_tiles; ++t) {
-      const int desc = __builtin_amdgcn_readfirstlane(list[t]);
-      const bool last = t + 1 == n_tiles;
-      const int next_desc = last ? 0 : __builtin_amdgcn_readfirstlane(list[t + 1]);
-      const int tchunk = (desc >> kDescChunkShift) & 63;
-      if (!full)
-        while (cur_chunk < tchunk) flush_partial(cur_chunk++);
-      const int code = (desc >> kDescCodeShift) & 15;
-      const int tidx = desc & 0xFFFFF;
-      const int key0 = tidx * BLK;
-      int live_kb = (1 << SH::NKB) - 1;
-      if (striped) {
-        live_kb = 0;
-#pragma unroll
-        for (int kb = 0; kb < SH::NKB; ++kb) live_kb |= ((code >> (kb / kb_div)) & 1) << kb;
+    // One tile per call; the parity P = t & 1 selects the buffers at compile
+    // time (tile t reads K of tile t+1 and V of tile t, and loads K of tile t+2
+    // and V of tile t+1).
+    auto tile = [&](int t, auto parity) {
+      constexpr int P = decltype(parity)::value;
+      bf16* const kfree = P ? sK1 : sK0;  // K of tile t: consumed, refilled below
+      bf16* const vfree = P ? sV0 : sV1;  // V of tile t-1: consumed, refilled below
+      const bf16* const Kt1 = P ? sK0 : sK1;  // K of tile t+1
+      const bf16* const Vt = P ? sV1 : sV0;   // V of tile t
+      const int desc = __builtin_amdgcn_readfirstlane(sList[t]);
+      const bool has_next = t + 1 < n_tiles;
+      // the fast variant always computes "next" scores (discarded after the last tile) so that
+      // the S MFMAs and the exponentials share one basic block
+      const int desc1 = has_next ? __builtin_amdgcn_readfirstlane(sList[t + 1]) : desc;
+      const int live_w = live_of(desc);
+      const int key0 = (desc & 0xFFFFF) * BLK + kb0 * 32;
+      const bool ragged = !striped && (desc & 0xFFFFF) * BLK + BLK > a.S;
+
+      // K of tile t+1 and V of tile t have landed; K of tile t and V of tile t-1 are free.
+      wait_vm();
+      __syncthreads();
+      if (!full) {
+        const int tchunk = (desc >> kDescChunkShift) & 63;
+        while (cur_chunk < tchunk) flush_partial(cur_chunk++, (float*)kfree, (float*)vfree);
       }
-      const bool ragged = !striped && key0 + BLK > a.S;
-      const TileSrc next = tile_source(next_desc, bh_base, a.ss, a.S, a.layout, a.n_chunks, BLK);
-      tile_step<D, BLK, GENERAL>(sK, sV, qf, st, live_kb, ragged, key0, sl2, k_off, k_swz, v_off, v_swz, v_chunk,
-                                 h2, last, a, loader, next, wave, sK, sV);
+      // K of tile t+2 and V of tile t+1 are loaded in slices, one per key block,
+      // so that no wave stalls on a full memory-request queue.  Near the end of
+      // the list the slices reload the last tile into a buffer that is free
+      // (this keeps the loop body branch-free; the loads are drained below).
+      const TileSrc srcK = src_of(__builtin_amdgcn_readfirstlane(sList[min(t + 2, n_tiles - 1)]));
+      const TileSrc srcV = src_of(desc1);
+
+      // Rolling pipeline over the wave's 32-key blocks j of tile t: the
+      // exponentials of block j of tile t (VALU), the S MFMAs of block j of
+      // tile t+1 and the P V MFMAs of block j of tile t all issue in one basic
+      // block; block j of the scores is overwritten by tile t+1 once its
+      // probabilities are formed.
+      const float m_ref = tile_max<D, BLK, GENERAL>(s, st, live_w, ragged, key0, a.S, h2, sl2);
+      const int live_next = live_of(desc1);
+      float lsum0 = 0.f, lsum1 = 0.f;
+      constexpr int LPB = SH::IPW / NB;  // load instructions per tensor per key block
+      static_assert(SH::IPW % NB == 0, "loads must split evenly over the key blocks");
+      static_for<NB>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        loader.template issue<GENERAL, j * LPB, (j + 1) * LPB>(gK, srcK, kfree, wave);
+        loader.template issue<GENERAL, j * LPB, (j + 1) * LPB>(gV, srcV, vfree, wave);
+        bf16x8 pb[2];
+        const bool live_now = !GENERAL || ((live_w >> j) & 1);
+        if (live_now) tile_probs(s[j], sl2, m_ref, pb, lsum0, lsum1);
+        if (!GENERAL || (has_next && ((live_next >> j) & 1))) {
+          bf16x8 kf[NKS];
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) kf[ks] = ol.k_frag(Kt1, j, ks);
+          s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+          for (int ks = 1; ks < NKS; ++ks)
+            s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s[j], 0, 0, 0);
+        }
+        if (!live_now) return;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          bf16x8 va[ND];
+#pragma unroll
+          for (int d = 0; d < ND; ++d) va[d] = ol.v_frag(Vt, j, half, d);
+#pragma unroll
+          for (int d = 0; d < ND; ++d)
+            st.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[d], pb[half], st.acc[d], 0, 0, 0);
+        }
+      });
+      st.l += lsum0 + lsum1;
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+      tile(t, std::integral_constant<int, 0>{});
+      if (t + 1 < n_tiles) tile(t + 1, std::integral_constant<int, 1>{});
     }
 
+    wait_vm();  // no tile load may still be in flight when the merge buffers are used
+    __syncthreads();
     if (!full) {
-      while (cur_chunk < a.c1) flush_partial(cur_chunk++);
+      while (cur_chunk < a.c1) flush_partial(cur_chunk++, (float*)sK0, (float*)sV0);
     } else {
-      const float l_tot = st.l + other_half(st.l);
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      if (qrow < a.S) {
+      float m, l_row;
+      merge_halves<D, BLK>(st, m, l_row, (float*)sK0, (float*)sV0, rg, kh, lane);
+      const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+      if (kh == 0 && qrow < a.S) {
         bf16* op = (bf16*)a.o + bh_base + (int64_t)qrow * a.ss;
 #pragma unroll
-        for (int d = 0; d < SH::ND; ++d)
+        for (int d = 0; d < ND; ++d)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const bf16x4 v4 = {(bf16)(st.acc[d][4 * g] * inv), (bf16)(st.acc[d][4 * g + 1] * inv),
@@ -434,19 +596,20 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-}  // namespace
-
-int attn_bf16_wg_per_cu(int block) { return block >= 128 ? 2 : 4; }
-
 template <int D, int BLK>
 hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
   const bool general = a.layout == SA_LAYOUT_STRIPED || a.S % BLK != 0;
   if (general)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, true>), dim3(a.num_bins), dim3(BLK * 2), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, true>), dim3(a.num_bins), dim3(Shape<D, BLK>::NW * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false>), dim3(a.num_bins), dim3(BLK * 2), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false>), dim3(a.num_bins), dim3(Shape<D, BLK>::NW * 64), 0, stream,
+                       a);
   return hipGetLastError();
 }
+
+}  // namespace
+
+int attn_bf16_wg_per_cu(int block) { return block >= 128 ? Shape<128, 128>::WG_PER_CU : Shape<128, 64>::WG_PER_CU; }
 
 hipError_t launch_attn_bf16(const FwdArgs& a, int D, int block, hipStream_t stream) {
   if (D == 128 && block == 128) return launch_variant<128, 128>(a, stream);
