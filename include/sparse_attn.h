@@ -84,8 +84,10 @@ typedef struct {
  *                 problem dtype (bf16 only).  The indexer (6D notes, section
  *                 7.1) computes I = (Q wq)(K wk)^T with the projections rounded
  *                 to bf16 and fp32 accumulation, and keeps, per query i,
- *                 min(top_k, #candidates) keys ordered by (I desc, key asc);
- *                 candidates are j <= i when causal, else all j.  rank == 32.
+ *                 the min(top_k, #candidates) keys that come first in the
+ *                 order (I desc, key asc); candidates are j <= i when causal,
+ *                 else all j.  rank == 32, top_k <= 512, S <= 65536.  The
+ *                 order of the keys within a query's list is unspecified.
  *  SA_KIND_INDEX: idx int32 [B][H][S][top_k] key indices, count int32
  *                 [B][H][S] (0 <= count <= top_k); copied into the plan.  Every
  *                 idx[b,h,i,t], t < count, must lie in [0, S) (checked on the

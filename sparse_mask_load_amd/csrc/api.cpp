@@ -221,6 +221,9 @@ sa_status plan_topk(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   }
   if (!sp->q || !sp->k || !sp->wq || !sp->wk) return fail(SA_ERR_INVALID, "q, k, wq or wk is NULL");
   if (sp->rank != 32) return fail(SA_ERR_UNSUPPORTED, "indexer rank %d (supported: 32)", sp->rank);
+  if (P->top_k > sa::kIndexerMaxTopK)
+    return fail(SA_ERR_UNSUPPORTED, "indexer top_k %d above %d", P->top_k, sa::kIndexerMaxTopK);
+  if (pr.S > 65536) return fail(SA_ERR_UNSUPPORTED, "indexer sequence length %d above 65536", pr.S);
   P->rank = sp->rank;
   if ((st = dalloc(&P->d_qp, rows * P->rank)) || (st = dalloc(&P->d_kp, rows * P->rank))) return st;
   sa::IndexerArgs a{};

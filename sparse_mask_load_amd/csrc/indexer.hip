@@ -1,11 +1,357 @@
-// DSA-style indexer (6D-parallel notes, section 7.1): placeholder until the
-// top-k selection kernel lands; the plan reports SA_ERR_HIP (not supported).
+// Top-k indexer of DeepSeek Sparse Attention (6D-parallel notes, section 7.1):
+// a low-rank importance I[i, j] = <Q'_i, K'_j> with Q' = Q Wq and K' = K Wk
+// (rank 32), and per query the top_k keys by importance (ties to the lower key
+// index; with a causal mask the candidates of query i are j <= i and a query
+// with fewer candidates than top_k takes all of them).
+//
+// 1. proj_kernel: Q' and K' in bf16 (fp32 sums over the head dimension in
+//    index order, rounded to nearest-even), the precision the selection is
+//    defined in.
+// 2. select_kernel: one workgroup per 32 consecutive queries of a (batch,
+//    head).  Importance tiles of 32 keys x 32 queries come from two
+//    v_mfma_f32_32x32x16_bf16 (fp32 accumulate; the bf16 products are exact).
+//    Each row's selection is a threshold K on a unique 64-bit key
+//    key(j) = ord(I[i, j]) << 32 | (0xFFFF - j), ord being the order-preserving
+//    map of fp32 onto uint32, so "larger key" means "higher importance, then
+//    lower index" and exactly top_k keys lie above the right threshold.  A
+//    counting pass streams all candidate keys of the 32 rows and appends those
+//    above each row's threshold to the row's LDS buffer (kCap entries); the
+//    common case rejects a 16-score group with one max and one compare.  The
+//    threshold is first estimated from the mean and deviation of the row's
+//    first kFirstLook importances (a normal quantile, Abramowitz & Stegun
+//    26.2.23); a pass that collects fewer than top_k or more than kCap keys
+//    moves it (deviation steps, then bisection of the key space, which ends
+//    because one more unit of the threshold removes at most one key).  Finally
+//    a wave per row picks the exact top_k from its buffer by bisection on the
+//    importance bits and, for ties, on the key index.  The order of the
+//    indices within a row's list is unspecified.
 #include <hip/hip_runtime.h>
+
+#include <stdint.h>
 
 #include "internal.h"
 
 namespace sa {
+namespace {
 
-hipError_t launch_indexer(const IndexerArgs&, hipStream_t) { return hipErrorNotSupported; }
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kRank = 32;
+constexpr int kRows = 32;          // queries per workgroup
+constexpr int kWaves = 4;
+constexpr int kCap = 704;          // candidate buffer entries per row
+constexpr int kFirstLook = 2048;   // keys of the threshold estimate
+constexpr int kMaxPasses = 80;     // 4 deviation steps + at most 64 bisections suffice
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ uint32_t ord_of(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_of_ord(uint32_t o) {
+  return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+// Threshold that keeps exactly the importances strictly above t.
+__device__ __forceinline__ uint64_t key_above(float t) { return ((uint64_t)ord_of(t) << 32) | 0xFFFFFFFFull; }
+
+// Upper-tail normal quantile: z with P(N(0,1) > z) = p (Abramowitz & Stegun 26.2.23, |error| < 4.5e-4).
+__device__ float normal_upper_quantile(float p) {
+  const bool lower = p > 0.5f;
+  const float pp = lower ? 1.f - p : p;
+  const float t = sqrtf(-2.f * logf(fmaxf(pp, 1e-30f)));
+  const float z = t - (2.515517f + t * (0.802853f + t * 0.010328f)) /
+                          (1.f + t * (1.432788f + t * (0.189269f + t * 0.001308f)));
+  return lower ? -z : z;
+}
+
+// ---------------------------------------------------------------------------
+// Projections: Xp[row][r] = bf16(sum_d X[row][d] * W[d][r]); 8 rows per block,
+// 32 threads per row.
+__global__ __launch_bounds__(256) void proj_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W,
+                                                   bf16* __restrict__ Xp, int B, int H, int S, int D, int64_t sb,
+                                                   int64_t sh, int64_t ss) {
+  const int64_t row = (int64_t)blockIdx.x * 8 + threadIdx.x / 32;
+  const int r = threadIdx.x & 31;
+  if (row >= (int64_t)B * H * S) return;
+  const int i = (int)(row % S);
+  const int bh = (int)(row / S);
+  const bf16* x = X + (int64_t)(bh / H) * sb + (int64_t)(bh % H) * sh + (int64_t)i * ss;
+  float acc = 0.f;
+  for (int d = 0; d < D; d += 8) {
+    const bf16x8 xv = *(const bf16x8*)(x + d);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)xv[e], (float)W[(d + e) * kRank + r], acc);
+  }
+  Xp[row * kRank + r] = (bf16)acc;
+}
+
+// ---------------------------------------------------------------------------
+struct RowCtl {
+  uint64_t K, lo, hi;  // threshold; largest known with too many keys above; smallest known with too few
+  float mean, sd, step;
+  int n, need, done, found;  // candidates, keys to select, finished, keys in the buffer once finished
+};
+
+struct SelShared {
+  float score[kRows][kCap];
+  uint16_t key[kRows][kCap];
+  int cnt[kRows];
+  RowCtl ctl[kRows];
+  float red[kWaves][kRows][3];
+  int active;
+};
+
+// Importance tile of key block kb for this wave's lanes: element r holds key
+// kb*32 + 8*(r/4) + 4*(lane/32) + r%4 of query i0 + lane%32; invalid pairs
+// (beyond S, or above the diagonal when causal) are -inf.
+__device__ __forceinline__ f32x16 tile_scores(const bf16* __restrict__ kp, int kb, int S, int i, bool causal,
+                                              const bf16x8 (&qf)[2], int lane) {
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int jrow = min(kb * 32 + l32, S - 1);
+  const bf16* p = kp + (int64_t)jrow * kRank + 8 * h2;
+  const bf16x8 k0 = *(const bf16x8*)p;
+  const bf16x8 k1 = *(const bf16x8*)(p + 16);
+  f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], f32x16{}, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[1], acc, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+    if (j >= S || i >= S || (causal && j > i)) acc[r] = kNegInf;
+  }
+  return acc;
+}
+
+__device__ __forceinline__ int wave_count(bool pred) { return __builtin_popcountll(__ballot(pred)); }
+
+__global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int blocks_per_bh = (a.S + kRows - 1) / kRows;
+  const int bh = blockIdx.x / blocks_per_bh;
+  const int i0 = (blockIdx.x % blocks_per_bh) * kRows;
+  const bool causal = a.causal != 0;
+  const bf16* qp = a.qp + (int64_t)bh * a.S * kRank;
+  const bf16* kp = a.kp + (int64_t)bh * a.S * kRank;
+  const int i = i0 + l32;  // this lane's query
+
+  // Q'^T operand: lane holds Q'[i][8*h2 .. +7] (k-step 0) and Q'[i][16 + 8*h2 .. +7] (k-step 1).
+  bf16x8 qf[2];
+  {
+    const bf16* p = qp + (int64_t)min(i, a.S - 1) * kRank + 8 * h2;
+    qf[0] = *(const bf16x8*)p;
+    qf[1] = *(const bf16x8*)(p + 16);
+  }
+  const int i_last = min(i0 + kRows - 1, a.S - 1);
+  const int n_max = causal ? i_last + 1 : a.S;  // most candidates of any row of the block
+  const int nkb = (n_max + 31) / 32;
+
+  if (tid < kRows) {
+    const int ir = i0 + tid;
+    RowCtl& c = sh.ctl[tid];
+    c.n = ir < a.S ? (causal ? ir + 1 : a.S) : 0;
+    c.need = min(a.top_k, c.n);
+    c.lo = 0;
+    c.hi = ~0ull;
+    c.K = 0;  // every candidate is above key 0
+    c.done = c.n == 0;
+    c.found = 0;
+    c.mean = 0.f;
+    c.sd = 0.f;
+    c.step = 0.5f;
+  }
+
+  // Threshold estimate for rows with more candidates than the buffer holds.
+  if (n_max > kCap) {
+    float s1 = 0.f, s2 = 0.f, s0 = 0.f;
+    const int n_fl = min(n_max, kFirstLook);
+    const int nfl_kb = (n_fl + 31) / 32;
+    const int my_n = i < a.S ? min(causal ? i + 1 : a.S, kFirstLook) : 0;
+    for (int kb = wave; kb < nfl_kb; kb += kWaves) {
+      const f32x16 sc = tile_scores(kp, kb, a.S, i, causal, qf, lane);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        if (j < my_n) {
+          s0 += 1.f;
+          s1 += sc[r];
+          s2 = fmaf(sc[r], sc[r], s2);
+        }
+      }
+    }
+    // fold the two half-waves (same query, different keys)
+    s0 += __shfl_xor(s0, 32);
+    s1 += __shfl_xor(s1, 32);
+    s2 += __shfl_xor(s2, 32);
+    if (h2 == 0) {
+      sh.red[wave][l32][0] = s0;
+      sh.red[wave][l32][1] = s1;
+      sh.red[wave][l32][2] = s2;
+    }
+    __syncthreads();
+    if (tid < kRows) {
+      RowCtl& c = sh.ctl[tid];
+      float t0 = 0.f, t1 = 0.f, t2 = 0.f;
+      for (int w = 0; w < kWaves; ++w) {
+        t0 += sh.red[w][tid][0];
+        t1 += sh.red[w][tid][1];
+        t2 += sh.red[w][tid][2];
+      }
+      c.mean = t0 > 0.f ? t1 / t0 : 0.f;
+      c.sd = t0 > 0.f ? sqrtf(fmaxf(t2 / t0 - c.mean * c.mean, 0.f)) : 0.f;
+      if (c.n > kCap) {
+        const float target = 0.5f * (float)(c.need + kCap);
+        c.K = key_above(c.mean + c.sd * normal_upper_quantile(target / (float)c.n));
+      }
+    }
+  }
+  __syncthreads();
+
+  // Counting passes until every row has between need and kCap keys above its threshold.
+  for (int pass = 0; pass < kMaxPasses; ++pass) {
+    if (tid < kRows) {
+      if (!sh.ctl[tid].done) sh.cnt[tid] = 0;
+      if (tid == 0) sh.active = 0;
+    }
+    __syncthreads();
+    const RowCtl& c = sh.ctl[l32];
+    const bool live = !c.done;
+    const uint64_t K = live ? c.K : ~0ull;
+    const uint32_t k_hi = (uint32_t)(K >> 32);
+    const float t_filter = !live ? __builtin_huge_valf() : (k_hi == 0 ? kNegInf : float_of_ord(k_hi));
+    for (int kb = wave; kb < nkb; kb += kWaves) {
+      const f32x16 sc = tile_scores(kp, kb, a.S, i, causal, qf, lane);
+      float m = sc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) m = fmaxf(m, sc[r]);
+      const bool maybe = m != kNegInf && m >= t_filter;
+      if (__ballot(maybe)) {
+        if (maybe) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            const uint64_t key = ((uint64_t)ord_of(sc[r]) << 32) | (uint32_t)(0xFFFF - j);
+            if (sc[r] != kNegInf && key > K) {
+              const int pos = atomicAdd(&sh.cnt[l32], 1);
+              if (pos < kCap) {
+                sh.score[l32][pos] = sc[r];
+                sh.key[l32][pos] = (uint16_t)j;
+              }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < kRows) {
+      RowCtl& cc = sh.ctl[tid];
+      if (!cc.done) {
+        const int n = sh.cnt[tid];
+        if (n >= cc.need && n <= kCap) {
+          cc.done = 1;
+          cc.found = n;
+        } else {
+          if (n > kCap)
+            cc.lo = cc.K;
+          else
+            cc.hi = cc.K;
+          uint64_t next = cc.lo + (cc.hi - cc.lo) / 2;
+          if (pass < 4 && cc.sd > 0.f) {
+            // deviation steps first: usually one step from the estimate reaches the window
+            const float t = float_of_ord((uint32_t)(cc.K >> 32));
+            const uint64_t kk = key_above(n > kCap ? t + cc.step * cc.sd : t - cc.step * cc.sd);
+            cc.step *= 2.f;
+            if (kk > cc.lo && kk < cc.hi) next = kk;
+          }
+          cc.K = next;
+          atomicAdd(&sh.active, 1);
+        }
+      }
+    }
+    __syncthreads();
+    const int still_active = sh.active;
+    __syncthreads();  // everyone has read it before the next pass resets it
+    if (still_active == 0) break;
+  }
+
+  // Exact top-need of each row's buffer: wave w takes rows w, w + 4, ...
+  constexpr int kPer = (kCap + 63) / 64;
+  for (int row = wave; row < kRows; row += kWaves) {
+    const int ir = i0 + row;
+    if (ir >= a.S) break;
+    const int n = sh.ctl[row].found;
+    const int need = sh.ctl[row].need;
+    uint32_t o[kPer];
+    int jj[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int p = e * 64 + lane;
+      o[e] = p < n ? ord_of(sh.score[row][p]) : 0u;
+      jj[e] = p < n ? (int)sh.key[row][p] : 0x7FFFFFFF;
+    }
+    auto count_if = [&](auto pred) {
+      int c = 0;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) c += wave_count(e * 64 + lane < n && pred(o[e], jj[e]));
+      return c;
+    };
+    uint32_t t_ord = 0;   // selected: ord > t_ord, plus ord == t_ord with index <= t_j
+    int t_j = -1;
+    if (n > need) {
+      // smallest h with fewer than need importances above it: the need-th largest has ord h
+      uint32_t lo = 0, hi = 0xFFFFFFFFu;
+      while (hi - lo > 1) {
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if (count_if([&](uint32_t ov, int) { return ov > mid; }) >= need)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      t_ord = hi;
+      const int above = count_if([&](uint32_t ov, int) { return ov > hi; });
+      const int ties_needed = need - above;
+      // smallest index bound taking ties_needed of the tied keys (lowest indices first)
+      int jlo = -1, jhi = 0xFFFF;
+      while (jhi - jlo > 1) {
+        const int mid = (jlo + jhi) / 2;
+        if (count_if([&](uint32_t ov, int jv) { return ov == hi && jv <= mid; }) >= ties_needed)
+          jhi = mid;
+        else
+          jlo = mid;
+      }
+      t_j = jhi;
+    }
+    int32_t* out = a.idx + ((int64_t)bh * a.S + ir) * a.top_k;
+    int base = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const bool sel = e * 64 + lane < n && (n <= need || o[e] > t_ord || (o[e] == t_ord && jj[e] <= t_j));
+      const uint64_t bits = __ballot(sel);
+      const int pos = base + __builtin_popcountll(bits & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+      if (sel && pos < a.top_k) out[pos] = jj[e];
+      base += __builtin_popcountll(bits);
+    }
+    if (lane == 0) a.count[(int64_t)bh * a.S + ir] = min(base, need);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
+  if (a.rank != kRank || a.top_k < 1 || a.top_k > kIndexerMaxTopK || a.S > 65536 || a.D % 8 != 0)
+    return hipErrorInvalidValue;
+  const int64_t rows = (int64_t)a.B * a.H * a.S;
+  const dim3 pg((unsigned)((rows + 7) / 8));
+  hipLaunchKernelGGL(proj_kernel, pg, dim3(256), 0, stream, (const bf16*)a.q, (const bf16*)a.wq, a.qp, a.B, a.H, a.S,
+                     a.D, a.sb, a.sh, a.ss);
+  hipLaunchKernelGGL(proj_kernel, pg, dim3(256), 0, stream, (const bf16*)a.k, (const bf16*)a.wk, a.kp, a.B, a.H, a.S,
+                     a.D, a.sb, a.sh, a.ss);
+  const int blocks = a.B * a.H * ((a.S + kRows - 1) / kRows);
+  hipLaunchKernelGGL(select_kernel, dim3(blocks), dim3(kWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
 
 }  // namespace sa

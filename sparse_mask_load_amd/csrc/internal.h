@@ -54,6 +54,9 @@ struct GatherArgs {
   float scale_log2;
 };
 
+// The indexer's per-row candidate buffer leaves room above the selection size.
+constexpr int kIndexerMaxTopK = 512;
+
 struct IndexerArgs {
   const void* q;
   const void* k;

@@ -95,6 +95,7 @@ def assert_close(got, ref, tol, what=""):
 def sample_rows(w, n=96, seed=0):
     """Seeded sample of (b, h, token) rows plus the first/last rows of edge blocks and heads."""
     rng = np.random.default_rng(seed)
+    n = min(n, w.B * w.H * w.S)  # there are only that many distinct rows
     rows = {(0, 0, 0), (0, w.H - 1, w.S - 1), (0, 0, w.S - 1), (0, w.H - 1, 0)}
     if w.block:
         rows |= {(0, w.H // 2, w.block - 1), (0, w.H // 2, w.block), (0, 1 % w.H, w.S - w.block)}
