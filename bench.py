@@ -11,6 +11,10 @@ chunks, LPT over one bin per compute unit):
 
 value = live-block FLOP per step (4 * 128^3 per live tile) / measured step time.
 
+The untimed extras also run the token top-k path on its own workload (B1 H16 n32768 d128,
+rank-32 indexer, top-k 512, causal): the TOPK plan (projections + importance + per-query
+top-k) and the gather attention over the selected keys, reported as times and rates.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode merged|fused]
        [--workload causal|video|skewed|tiny] [--no-cpu-baseline] [--calibrate-copy MiB]
 Prints one JSON line.  Only one GPU is used: --gpus > 1 exits with a message.
@@ -105,6 +109,52 @@ def per_cu_balance(trace: np.ndarray):
             "measured_bin_max_over_mean": float(bins.max() / bins.mean())}
 
 
+def topk_path(bd, W, torch, dev, reps: int = 5) -> dict:
+    """Times the top-k path (indexer + selection, gather attention) on the 16x32768 workload."""
+    w = W.make(5)
+    q, k, v = (torch.from_numpy(x).to(dev, torch.bfloat16) for x in (w.q, w.k, w.v))
+    wq, wk = (torch.from_numpy(np.ascontiguousarray(x)).to(dev, torch.bfloat16) for x in (w.wq, w.wk))
+    prob = bd.make_problem(q, 0, 1, "contiguous")
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def plan():
+        return bd.sparse_attn_plan(prob, "topk", q=q, k=k, wq=wq, wk=wk, rank=w.rank, top_k=w.top_k, causal=True)
+
+    p = plan()
+    bd.sparse_attn_fwd(p, q, k, v, 0, 1, o=out)
+    torch.cuda.synchronize()
+    info = bd.sparse_attn_plan_info(p)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    t_idx, t_att = [], []
+    for _ in range(reps):
+        e[0].record(stream)
+        p2 = plan()
+        e[1].record(stream)
+        e[2].record(stream)
+        bd.sparse_attn_fwd(p2, q, k, v, 0, 1, o=out)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        p2.close()
+        t_idx.append(e[0].elapsed_time(e[1]))
+        t_att.append(e[2].elapsed_time(e[3]))
+    p.close()
+    B, H, S, D = q.shape
+    cand = B * H * S * (S + 1) // 2  # causal candidate pairs
+    pairs = int(info["total_live"])
+    idx_ms, att_ms = float(np.median(t_idx)), float(np.median(t_att))
+    return {
+        "workload": f"top-k token-sparse attention B{B} H{H} n{S} d{D}, rank {w.rank} indexer, top-k {w.top_k}, causal",
+        "indexer_ms": round(idx_ms, 4), "candidates": cand,
+        "indexer_gcand_per_s": round(cand / idx_ms / 1e6, 1),
+        "indexer_mfma_tflops": round(2.0 * w.rank * cand / idx_ms / 1e9, 2),
+        "gather_attention_ms": round(att_ms, 4), "selected_pairs": pairs,
+        "gather_attention_tflops": round(4.0 * D * pairs / att_ms / 1e9, 2),
+        "gather_kv_gbs": round(2 * D * 2 * pairs / att_ms / 1e6, 1),
+        "path_ms": round(idx_ms + att_ms, 4),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +167,7 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the untimed breakdown runs")
+    ap.add_argument("--no-topk", action="store_true", help="skip the token top-k path measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -265,6 +316,11 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = 4 * n
+
+    if not args.no_extras and not args.no_topk:
+        del q, k, v, o_part, m_part, l_part, out
+        torch.cuda.empty_cache()
+        result["topk_path"] = topk_path(bd, W, torch, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.H))

@@ -20,8 +20,9 @@
 //    threshold is first estimated from the mean and deviation of the row's
 //    first kFirstLook importances (a normal quantile, Abramowitz & Stegun
 //    26.2.23); a pass that collects fewer than top_k or more than kCap keys
-//    moves it (deviation steps, then bisection of the key space, which ends
-//    because one more unit of the threshold removes at most one key).  Finally
+//    moves it (by the normal-model distance between the observed and the
+//    target count, then by bisection of the key space, which ends because one
+//    more unit of the threshold removes at most one key).  Finally
 //    a wave per row picks the exact top_k from its buffer by bisection on the
 //    importance bits and, for ties, on the key index.  The order of the
 //    indices within a row's list is unspecified.
@@ -40,10 +41,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kRank = 32;
 constexpr int kRows = 32;          // queries per workgroup
-constexpr int kWaves = 4;
-constexpr int kCap = 704;          // candidate buffer entries per row
+constexpr int kWaves = 16;         // 4 per SIMD: the key stream is latency-bound
+constexpr int kCap = 768;          // candidate buffer entries per row
 constexpr int kFirstLook = 2048;   // keys of the threshold estimate
-constexpr int kMaxPasses = 80;     // 4 deviation steps + at most 64 bisections suffice
+constexpr int kPrefetch = 4;       // key blocks whose K' loads each wave keeps in flight
+constexpr int kModelSteps = 6;     // threshold corrections from the normal model before bisection
+constexpr int kMaxPasses = 80;     // kModelSteps + at most 64 bisections suffice
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ uint32_t ord_of(float x) {
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(256) void proj_kernel(const bf16* __restrict__ X, c
 // ---------------------------------------------------------------------------
 struct RowCtl {
   uint64_t K, lo, hi;  // threshold; largest known with too many keys above; smallest known with too few
-  float mean, sd, step;
+  float mean, sd;
   int n, need, done, found;  // candidates, keys to select, finished, keys in the buffer once finished
 };
 
@@ -103,22 +106,29 @@ struct SelShared {
   int active;
 };
 
-// Importance tile of key block kb for this wave's lanes: element r holds key
-// kb*32 + 8*(r/4) + 4*(lane/32) + r%4 of query i0 + lane%32; invalid pairs
-// (beyond S, or above the diagonal when causal) are -inf.
-__device__ __forceinline__ f32x16 tile_scores(const bf16* __restrict__ kp, int kb, int S, int i, bool causal,
-                                              const bf16x8 (&qf)[2], int lane) {
-  const int h2 = lane >> 5, l32 = lane & 31;
-  const int jrow = min(kb * 32 + l32, S - 1);
-  const bf16* p = kp + (int64_t)jrow * kRank + 8 * h2;
-  const bf16x8 k0 = *(const bf16x8*)p;
-  const bf16x8 k1 = *(const bf16x8*)(p + 16);
-  f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], f32x16{}, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[1], acc, 0, 0, 0);
+// K' operand of key block kb: lane holds K'[kb*32 + lane%32][8*(lane/32) .. +7] and the
+// same 8 ranks + 16 (rows beyond S repeat the last row; they are masked below).
+struct KFrag {
+  bf16x8 k0, k1;
+};
+__device__ __forceinline__ KFrag load_kfrag(const bf16* __restrict__ kp, int kb, int S, int lane) {
+  const bf16* p = kp + (int64_t)min(kb * 32 + (lane & 31), S - 1) * kRank + 8 * (lane >> 5);
+  return KFrag{*(const bf16x8*)p, *(const bf16x8*)(p + 16)};
+}
+
+// Importance tile of key block kb: element r holds key kb*32 + 8*(r/4) + 4*(lane/32) + r%4
+// of query i (= i0 + lane%32); when `edge` (the block crosses the diagonal or the end of the
+// sequence) invalid pairs are set to -inf.
+__device__ __forceinline__ f32x16 tile_scores(const KFrag& kf, const bf16x8 (&qf)[2], int kb, int S, int i,
+                                              bool causal, bool edge, int lane) {
+  f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.k0, qf[0], f32x16{}, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.k1, qf[1], acc, 0, 0, 0);
+  if (edge) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int j = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-    if (j >= S || i >= S || (causal && j > i)) acc[r] = kNegInf;
+    for (int r = 0; r < 16; ++r) {
+      const int j = kb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (j >= S || i >= S || (causal && j > i)) acc[r] = kNegInf;
+    }
   }
   return acc;
 }
@@ -146,6 +156,9 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
     qf[1] = *(const bf16x8*)(p + 16);
   }
   const int i_last = min(i0 + kRows - 1, a.S - 1);
+  // key blocks that need masking: those reaching past the first query of the block (causal)
+  // or past the end of the sequence, and all of them when the block has rows beyond S
+  const int first_edge_kb = i0 + kRows > a.S ? 0 : (causal ? i0 / 32 : (a.S - 1) / 32);
   const int n_max = causal ? i_last + 1 : a.S;  // most candidates of any row of the block
   const int nkb = (n_max + 31) / 32;
 
@@ -161,7 +174,6 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
     c.found = 0;
     c.mean = 0.f;
     c.sd = 0.f;
-    c.step = 0.5f;
   }
 
   // Threshold estimate for rows with more candidates than the buffer holds.
@@ -171,7 +183,7 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
     const int nfl_kb = (n_fl + 31) / 32;
     const int my_n = i < a.S ? min(causal ? i + 1 : a.S, kFirstLook) : 0;
     for (int kb = wave; kb < nfl_kb; kb += kWaves) {
-      const f32x16 sc = tile_scores(kp, kb, a.S, i, causal, qf, lane);
+      const f32x16 sc = tile_scores(load_kfrag(kp, kb, a.S, lane), qf, kb, a.S, i, causal, kb >= first_edge_kb, lane);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
@@ -222,26 +234,59 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
     const uint64_t K = live ? c.K : ~0ull;
     const uint32_t k_hi = (uint32_t)(K >> 32);
     const float t_filter = !live ? __builtin_huge_valf() : (k_hi == 0 ? kNegInf : float_of_ord(k_hi));
-    for (int kb = wave; kb < nkb; kb += kWaves) {
-      const f32x16 sc = tile_scores(kp, kb, a.S, i, causal, qf, lane);
+    auto process = [&](const KFrag& cur, int kb) {
+      const f32x16 sc = tile_scores(cur, qf, kb, a.S, i, causal, kb >= first_edge_kb, lane);
       float m = sc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) m = fmaxf(m, sc[r]);
       const bool maybe = m != kNegInf && m >= t_filter;
       if (__ballot(maybe)) {
         if (maybe) {
+          // which of the 16 keys lie above the threshold (importance above t_filter, or equal
+          // to it with the index part of the key deciding)
+          uint32_t bits = 0;
+          bool tie = false;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int j = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            const uint64_t key = ((uint64_t)ord_of(sc[r]) << 32) | (uint32_t)(0xFFFF - j);
-            if (sc[r] != kNegInf && key > K) {
-              const int pos = atomicAdd(&sh.cnt[l32], 1);
-              if (pos < kCap) {
-                sh.score[l32][pos] = sc[r];
-                sh.key[l32][pos] = (uint16_t)j;
-              }
+            bits |= (sc[r] > t_filter ? 1u : 0u) << r;
+            tie |= sc[r] == t_filter;
+          }
+          if (tie) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+              const uint64_t key = ((uint64_t)ord_of(sc[r]) << 32) | (uint32_t)(0xFFFF - j);
+              if (sc[r] == t_filter && sc[r] != kNegInf && key > K) bits |= 1u << r;
             }
           }
+          if (bits) {
+            int pos = atomicAdd(&sh.cnt[l32], __builtin_popcount(bits));  // one claim per lane
+            while (bits) {
+              const int r = __builtin_ctz(bits);
+              bits &= bits - 1;
+              if (pos < kCap) {
+                sh.score[l32][pos] = sc[r];
+                sh.key[l32][pos] = (uint16_t)(kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3));
+              }
+              ++pos;
+            }
+          }
+        }
+      }
+    };
+    // key blocks wave, wave + kWaves, ...: each wave keeps kPrefetch blocks' K' loads in flight
+    KFrag ring[kPrefetch];
+#pragma unroll
+    for (int p = 0; p < kPrefetch; ++p)
+      if (wave + p * kWaves < nkb) ring[p] = load_kfrag(kp, wave + p * kWaves, a.S, lane);
+    for (int kb0 = wave; kb0 < nkb; kb0 += kPrefetch * kWaves) {
+#pragma unroll
+      for (int p = 0; p < kPrefetch; ++p) {
+        const int kb = kb0 + p * kWaves;
+        if (kb < nkb) {
+          const KFrag cur = ring[p];
+          if (kb + kPrefetch * kWaves < nkb) ring[p] = load_kfrag(kp, kb + kPrefetch * kWaves, a.S, lane);
+          process(cur, kb);
         }
       }
     }
@@ -259,11 +304,14 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
           else
             cc.hi = cc.K;
           uint64_t next = cc.lo + (cc.hi - cc.lo) / 2;
-          if (pass < 4 && cc.sd > 0.f) {
-            // deviation steps first: usually one step from the estimate reaches the window
+          if (pass < kModelSteps && cc.sd > 0.f) {
+            // move by the normal-model distance between the observed and the target count
             const float t = float_of_ord((uint32_t)(cc.K >> 32));
-            const uint64_t kk = key_above(n > kCap ? t + cc.step * cc.sd : t - cc.step * cc.sd);
-            cc.step *= 2.f;
+            const float nn = (float)cc.n;
+            const float target = 0.5f * (float)(cc.need + kCap);
+            const float seen = fminf(fmaxf((float)n, 0.5f), nn - 0.5f);
+            const uint64_t kk = key_above(t + cc.sd * (normal_upper_quantile(target / nn) -
+                                                       normal_upper_quantile(seen / nn)));
             if (kk > cc.lo && kk < cc.hi) next = kk;
           }
           cc.K = next;
@@ -301,28 +349,54 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
     uint32_t t_ord = 0;   // selected: ord > t_ord, plus ord == t_ord with index <= t_j
     int t_j = -1;
     if (n > need) {
-      // smallest h with fewer than need importances above it: the need-th largest has ord h
-      uint32_t lo = 0, hi = 0xFFFFFFFFu;
-      while (hi - lo > 1) {
-        const uint32_t mid = lo + (hi - lo) / 2;
-        if (count_if([&](uint32_t ov, int) { return ov > mid; }) >= need)
+      // Bracket lo < h <= hi of the need-th largest ord h: count(> lo) >= need > count(> hi).
+      // Interpolation steps (the counts are close to linear in ord within the bracket)
+      // alternate with bisection, which bounds the worst case at about 64 steps.
+      uint32_t omin = 0xFFFFFFFFu, omax = 0;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (e * 64 + lane < n) {
+          omin = min(omin, o[e]);
+          omax = max(omax, o[e]);
+        }
+      for (int w = 32; w >= 1; w >>= 1) {
+        omin = min(omin, (uint32_t)__shfl_xor((int)omin, w));
+        omax = max(omax, (uint32_t)__shfl_xor((int)omax, w));
+      }
+      uint32_t lo = omin - 1, hi = omax;  // entries' ords are >= 0x00800000, so omin - 1 does not wrap
+      int c_lo = n, c_hi = 0;
+      for (int step = 0; hi - lo > 1; ++step) {
+        uint32_t mid = lo + (hi - lo) / 2;
+        if ((step & 1) == 0) {
+          const float f = (float)(c_lo - need) + 0.5f;
+          const uint32_t guess = lo + (uint32_t)((float)(hi - lo) * (f / (float)(c_lo - c_hi)));
+          mid = min(max(guess, lo + 1), hi - 1);
+        }
+        const int c = count_if([&](uint32_t ov, int) { return ov > mid; });
+        if (c >= need) {
           lo = mid;
-        else
+          c_lo = c;
+        } else {
           hi = mid;
+          c_hi = c;
+        }
       }
       t_ord = hi;
-      const int above = count_if([&](uint32_t ov, int) { return ov > hi; });
-      const int ties_needed = need - above;
-      // smallest index bound taking ties_needed of the tied keys (lowest indices first)
-      int jlo = -1, jhi = 0xFFFF;
-      while (jhi - jlo > 1) {
-        const int mid = (jlo + jhi) / 2;
-        if (count_if([&](uint32_t ov, int jv) { return ov == hi && jv <= mid; }) >= ties_needed)
-          jhi = mid;
-        else
-          jlo = mid;
+      const int ties_needed = need - c_hi;
+      if (count_if([&](uint32_t ov, int) { return ov == hi; }) == ties_needed) {
+        t_j = 0xFFFF;  // every tied key is taken (the usual case: the tie is the need-th key alone)
+      } else {
+        // smallest index bound taking ties_needed of the tied keys (lowest indices first)
+        int jlo = -1, jhi = 0xFFFF;
+        while (jhi - jlo > 1) {
+          const int mid = (jlo + jhi) / 2;
+          if (count_if([&](uint32_t ov, int jv) { return ov == hi && jv <= mid; }) >= ties_needed)
+            jhi = mid;
+          else
+            jlo = mid;
+        }
+        t_j = jhi;
       }
-      t_j = jhi;
     }
     int32_t* out = a.idx + ((int64_t)bh * a.S + ir) * a.top_k;
     int base = 0;
