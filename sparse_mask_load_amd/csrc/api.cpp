@@ -25,7 +25,6 @@ struct sa_plan {
   int32_t* d_row = nullptr;          // [B*H*nQ]
   int32_t* d_col = nullptr;          // [B*H*nK]
   int32_t* d_crow = nullptr;         // [B*H*C*nQ]
-  unsigned long long* d_total = nullptr;
   int32_t* d_items = nullptr;        // [(C+1)][n_items]: list 0 = full range, list 1+c = chunk c
   int32_t* d_bin_ptr = nullptr;      // [(C+1)][num_bins+1]
   std::vector<int32_t> h_items, h_bin_ptr;
@@ -115,7 +114,7 @@ sa_status dalloc(T** ptr, size_t n) {
 void free_plan(sa_plan* p) {
   if (!p) return;
   (void)hipDeviceSynchronize();
-  void* ptrs[] = {p->d_mask, p->d_row, p->d_col, p->d_crow, p->d_total, p->d_items,
+  void* ptrs[] = {p->d_mask, p->d_row, p->d_col, p->d_crow, p->d_items,
                   p->d_bin_ptr, p->d_idx, p->d_count, p->d_qp, p->d_kp};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
@@ -141,19 +140,15 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   sa_status st;
   if ((st = dalloc(&P->d_mask, mask_bytes)) || (st = dalloc(&P->d_row, (size_t)BH * nQ)) ||
       (st = dalloc(&P->d_col, (size_t)BH * nK)) || (st = dalloc(&P->d_crow, (size_t)BH * C * nQ)) ||
-      (st = dalloc(&P->d_total, 1)) || (st = dalloc(&P->d_items, (size_t)(C + 1) * P->n_items)) ||
+      (st = dalloc(&P->d_items, (size_t)(C + 1) * P->n_items)) ||
       (st = dalloc(&P->d_bin_ptr, (size_t)(C + 1) * (P->num_bins + 1))))
     return st;
   SA_HIP(hipMemcpyAsync(P->d_mask, sp->mask, mask_bytes, hipMemcpyDeviceToDevice, stream));
-  SA_HIP(sa::launch_popcount(P->d_mask, BH, nQ, nK, C, pr.layout, P->d_row, P->d_col, P->d_crow, P->d_total,
-                             stream));
+  SA_HIP(sa::launch_popcount(P->d_mask, BH, nQ, nK, C, pr.layout, P->d_row, P->d_col, P->d_crow, stream));
   std::vector<int32_t> row((size_t)BH * nQ), crow((size_t)BH * C * nQ);
-  unsigned long long total = 0;
   SA_HIP(hipMemcpyAsync(row.data(), P->d_row, row.size() * 4, hipMemcpyDeviceToHost, stream));
   SA_HIP(hipMemcpyAsync(crow.data(), P->d_crow, crow.size() * 4, hipMemcpyDeviceToHost, stream));
-  SA_HIP(hipMemcpyAsync(&total, P->d_total, sizeof(total), hipMemcpyDeviceToHost, stream));
   SA_HIP(hipStreamSynchronize(stream));
-  P->total_live = (int64_t)total;
 
   const int m = P->num_bins, n = P->n_items;
   P->h_items.assign((size_t)(C + 1) * n, 0);
@@ -179,12 +174,12 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
     pmax = std::max<int64_t>(pmax, row[i]);
   }
   P->load_sum = sum;
+  P->total_live = sum;  // every live tile belongs to exactly one Q-block row
   P->makespan = *std::max_element(P->h_bin_load.begin(), P->h_bin_load.begin() + m);
   P->lower_bound = std::max<int64_t>(pmax, (sum + m - 1) / m);
   SA_HIP(hipMemcpyAsync(P->d_items, P->h_items.data(), P->h_items.size() * 4, hipMemcpyHostToDevice, stream));
   SA_HIP(hipMemcpyAsync(P->d_bin_ptr, P->h_bin_ptr.data(), P->h_bin_ptr.size() * 4, hipMemcpyHostToDevice,
                         stream));
-  SA_HIP(hipStreamSynchronize(stream));
   return SA_OK;
 }
 

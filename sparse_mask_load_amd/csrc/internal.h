@@ -82,8 +82,7 @@ struct MergeArgs {
 
 // Kernel launchers (defined in the .hip files).  Return hipSuccess or the launch error.
 hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_chunks, int layout,
-                           int32_t* row, int32_t* col, int32_t* crow, unsigned long long* total,
-                           hipStream_t stream);
+                           int32_t* row, int32_t* col, int32_t* crow, hipStream_t stream);
 hipError_t launch_attn_bf16(const FwdArgs& a, int D, int block, hipStream_t stream);
 int attn_bf16_wg_per_cu(int block);  // workgroups the bf16 kernel keeps resident per CU
 hipError_t launch_attn_f32(const FwdArgs& a, int D, int block, hipStream_t stream);

@@ -10,6 +10,7 @@
 // loaded bins the lowest index (the rule the post's [8,7,6,5,4] example needs
 // to print 8+5+4 | 7+6).
 #include <algorithm>
+#include <functional>
 #include <cstdint>
 #include <numeric>
 #include <queue>
@@ -20,39 +21,90 @@
 
 namespace sa {
 
+// Work lists of one plan are rebuilt for every mask, so this runs in the
+// timed path: a counting sort replaces the comparison sort (loads are small
+// non-negative integers; equal loads keep ascending id order), a ring of
+// per-load bin bitsets replaces the bin heap, and the per-bin lists come from
+// a stable counting sort of the items by bin.
 void assign(const int64_t* loads, int n, int m, int order, int32_t* items_out, int32_t* bin_ptr_out,
             int64_t* bin_load_out) {
-  std::vector<std::vector<int32_t>> bins(m);
+  std::vector<int32_t> bin_of(n);
   std::vector<int64_t> bin_load(m, 0);
   if (order == SA_ORDER_NAIVE) {
     for (int i = 0; i < n; ++i) {
-      bins[i % m].push_back(i);
+      bin_of[i] = i % m;
       bin_load[i % m] += loads[i];
     }
   } else {
+    int64_t lmax = 0;
+    for (int i = 0; i < n; ++i) lmax = std::max(lmax, loads[i]);
     std::vector<int32_t> ids(n);
-    std::iota(ids.begin(), ids.end(), 0);
-    std::stable_sort(ids.begin(), ids.end(), [&](int32_t a, int32_t b) { return loads[a] > loads[b]; });
-    // min-heap of (load, bin): the top is the least-loaded bin, lowest index on ties
-    using Entry = std::pair<int64_t, int32_t>;
-    std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> heap;
-    for (int b = 0; b < m; ++b) heap.push({0, b});
-    for (int32_t id : ids) {
-      Entry e = heap.top();
-      heap.pop();
-      bins[e.second].push_back(id);
-      e.first += loads[id];
-      bin_load[e.second] = e.first;
-      heap.push(e);
+    if (lmax <= 4 * (int64_t)n + 65536) {
+      // counting sort, load descending, id ascending within a load
+      std::vector<int32_t> start(lmax + 2, 0);
+      for (int i = 0; i < n; ++i) ++start[lmax - loads[i] + 1];
+      for (int64_t v = 1; v <= lmax + 1; ++v) start[v] += start[v - 1];
+      for (int i = 0; i < n; ++i) ids[start[lmax - loads[i]]++] = i;
+    } else {
+      std::iota(ids.begin(), ids.end(), 0);
+      std::stable_sort(ids.begin(), ids.end(), [&](int32_t a, int32_t b) { return loads[a] > loads[b]; });
     }
+    // Least-loaded bin, lowest index first: bins are grouped by load in a ring of lmax + 1
+    // buckets (each a bitset of bins).  Every bin load lies in [lo, lo + lmax], lo being the
+    // current minimum, because a bin only receives an item while it is least loaded; lo
+    // never decreases, so the search for the lowest non-empty bucket only moves forward.
+    if (lmax <= (1 << 16)) {
+      const int words = (m + 63) / 64;
+      const int64_t nb = lmax + 1;
+      std::vector<uint64_t> bucket((size_t)nb * words, 0);
+      for (int b = 0; b < m; ++b) bucket[b / 64] |= 1ull << (b % 64);
+      int64_t lo = 0;
+      for (int32_t id : ids) {
+        uint64_t* w = &bucket[(size_t)(lo % nb) * words];
+        int k = 0;
+        for (;;) {
+          while (k < words && w[k] == 0) ++k;
+          if (k < words) break;
+          ++lo;
+          w = &bucket[(size_t)(lo % nb) * words];
+          k = 0;
+        }
+        const int b = k * 64 + __builtin_ctzll(w[k]);
+        w[k] &= w[k] - 1;
+        bin_of[id] = b;
+        bin_load[b] += loads[id];
+        bucket[(size_t)(bin_load[b] % nb) * words + b / 64] |= 1ull << (b % 64);
+      }
+    } else {
+      // very large loads (host callers): a binary heap of packed (load << 32 | bin) keys
+      std::vector<std::pair<int64_t, int32_t>> heap(m);
+      for (int b = 0; b < m; ++b) heap[b] = {0, b};
+      for (int32_t id : ids) {
+        std::pop_heap(heap.begin(), heap.end(), std::greater<std::pair<int64_t, int32_t>>());
+        auto& e = heap.back();
+        bin_of[id] = e.second;
+        e.first += loads[id];
+        bin_load[e.second] = e.first;
+        std::push_heap(heap.begin(), heap.end(), std::greater<std::pair<int64_t, int32_t>>());
+      }
+    }
+    // per-bin order is assignment order, which is the order of ids
+    std::vector<int32_t> pos(m + 1, 0);
+    for (int i = 0; i < n; ++i) ++pos[bin_of[i] + 1];
+    for (int b = 0; b < m; ++b) pos[b + 1] += pos[b];
+    for (int b = 0; b <= m; ++b) bin_ptr_out[b] = pos[b];
+    for (int32_t id : ids) items_out[pos[bin_of[id]]++] = id;
+    if (bin_load_out)
+      for (int b = 0; b < m; ++b) bin_load_out[b] = bin_load[b];
+    return;
   }
-  int32_t pos = 0;
-  for (int b = 0; b < m; ++b) {
-    bin_ptr_out[b] = pos;
-    for (int32_t id : bins[b]) items_out[pos++] = id;
-    if (bin_load_out) bin_load_out[b] = bin_load[b];
-  }
-  bin_ptr_out[m] = pos;
+  std::vector<int32_t> pos(m + 1, 0);
+  for (int i = 0; i < n; ++i) ++pos[bin_of[i] + 1];
+  for (int b = 0; b < m; ++b) pos[b + 1] += pos[b];
+  for (int b = 0; b <= m; ++b) bin_ptr_out[b] = pos[b];
+  for (int i = 0; i < n; ++i) items_out[pos[bin_of[i]]++] = i;
+  if (bin_load_out)
+    for (int b = 0; b < m; ++b) bin_load_out[b] = bin_load[b];
 }
 
 }  // namespace sa

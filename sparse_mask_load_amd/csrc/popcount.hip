@@ -2,12 +2,13 @@
 // post (scenario 2: a Q-block's work is its mask row sum, a KV-block's its
 // column sum), plus each row's count per KV chunk (one ring step's shard).
 //
-// rows:  one wavefront per mask row; 64 mask bytes per ballot, so a row of nK
-//        entries costs nK/64 coalesced 64-byte reads.
-// cols:  one thread per column, walking the rows (each step reads 64
-//        consecutive bytes across the wavefront).
-// Counts are integers accumulated exactly; the total uses a 64-bit atomic add,
-// whose result does not depend on the order of the additions.
+// One workgroup per (batch, head) mask of nQ x nK bytes (16 KiB for a
+// 128 x 128 mask).  Row and chunk counts: a thread per row reads the row in
+// 16-byte vectors and counts its non-zero bytes with a bit trick (4 bytes per
+// 32-bit word; a byte is non-zero iff its low 7 bits are or its top bit is).
+// Column counts: a thread per column walks the rows with coalesced byte loads.
+// Counts are integers accumulated exactly.  The grand total is the sum of the
+// row counts, taken on the host.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -15,62 +16,57 @@
 namespace sa {
 namespace {
 
-__global__ __launch_bounds__(256) void popcount_rows_kernel(const uint8_t* __restrict__ mask, int n_rows,
-                                                            int nQ, int nK, int n_chunks, int layout,
-                                                            int32_t* __restrict__ row,
-                                                            int32_t* __restrict__ crow,
-                                                            unsigned long long* __restrict__ total) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (r >= n_rows) return;
-  const uint8_t* m = mask + (int64_t)r * nK;
-  const int bh = r / nQ, i = r % nQ;
-  const int per_chunk = nK / n_chunks;
-  int tot = 0;
-  for (int c = 0; c < n_chunks; ++c) {
-    int cnt = 0;
-    const int j1 = (c + 1) * per_chunk;
-    for (int base = c * per_chunk; base < j1; base += 64) {
-      const int j = base + lane;
-      cnt += __popcll(__ballot(j < j1 && m[j] != 0));
-    }
-    tot += cnt;
-    if (layout == SA_LAYOUT_CONTIGUOUS && lane == 0) crow[((int64_t)bh * n_chunks + c) * nQ + i] = cnt;
-  }
-  if (lane == 0) {
-    row[r] = tot;
-    if (layout == SA_LAYOUT_STRIPED)
-      for (int c = 0; c < n_chunks; ++c) crow[((int64_t)bh * n_chunks + c) * nQ + i] = tot;
-    atomicAdd(total, (unsigned long long)tot);
-  }
+__device__ __forceinline__ int nonzero_bytes(uint32_t v) {
+  const uint32_t low7 = (v & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;  // top bit of a byte: its low 7 bits are non-zero
+  return __builtin_popcount((low7 | v) & 0x80808080u);
 }
 
-__global__ __launch_bounds__(256) void popcount_cols_kernel(const uint8_t* __restrict__ mask, int BH,
-                                                            int nQ, int nK, int32_t* __restrict__ col) {
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= (int64_t)BH * nK) return;
-  const int bh = (int)(g / nK), j = (int)(g % nK);
-  const uint8_t* m = mask + (int64_t)bh * nQ * nK + j;
-  int cnt = 0;
-  for (int i = 0; i < nQ; ++i) cnt += m[(int64_t)i * nK] != 0;
-  col[g] = cnt;
+__global__ __launch_bounds__(256) void popcount_kernel(const uint8_t* __restrict__ mask, int nQ, int nK,
+                                                       int n_chunks, int layout, int32_t* __restrict__ row,
+                                                       int32_t* __restrict__ col, int32_t* __restrict__ crow) {
+  const int bh = blockIdx.x;
+  const uint8_t* m = mask + (int64_t)bh * nQ * nK;
+  const int per_chunk = nK / n_chunks;
+  const bool vec = per_chunk % 16 == 0 && nK % 16 == 0;  // rows and chunks split into whole 16-byte vectors
+  for (int i = threadIdx.x; i < nQ; i += blockDim.x) {
+    const uint8_t* mr = m + (int64_t)i * nK;
+    int tot = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      int cnt = 0;
+      if (vec) {
+        for (int j = c * per_chunk; j < (c + 1) * per_chunk; j += 16) {
+          const uint4 v = *(const uint4*)(mr + j);
+          cnt += nonzero_bytes(v.x) + nonzero_bytes(v.y) + nonzero_bytes(v.z) + nonzero_bytes(v.w);
+        }
+      } else {
+        for (int j = c * per_chunk; j < (c + 1) * per_chunk; ++j) cnt += mr[j] != 0;
+      }
+      tot += cnt;
+      if (layout == SA_LAYOUT_CONTIGUOUS) crow[((int64_t)bh * n_chunks + c) * nQ + i] = cnt;
+    }
+    row[(int64_t)bh * nQ + i] = tot;
+    // striped: every chunk holds a 1/n_chunks slice of each live block, so each chunk's load is the row's
+    if (layout == SA_LAYOUT_STRIPED)
+      for (int c = 0; c < n_chunks; ++c) crow[((int64_t)bh * n_chunks + c) * nQ + i] = tot;
+  }
+  for (int j = threadIdx.x; j < nK; j += blockDim.x) {
+    int cnt = 0;
+    int i = 0;
+    for (; i + 4 <= nQ; i += 4)
+      cnt += (m[(int64_t)i * nK + j] != 0) + (m[(int64_t)(i + 1) * nK + j] != 0) +
+             (m[(int64_t)(i + 2) * nK + j] != 0) + (m[(int64_t)(i + 3) * nK + j] != 0);
+    for (; i < nQ; ++i) cnt += m[(int64_t)i * nK + j] != 0;
+    col[(int64_t)bh * nK + j] = cnt;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_chunks, int layout,
-                           int32_t* row, int32_t* col, int32_t* crow, unsigned long long* total,
-                           hipStream_t stream) {
-  const int n_rows = BH * nQ;
-  hipError_t e = hipMemsetAsync(total, 0, sizeof(unsigned long long), stream);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(popcount_rows_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, stream, mask, n_rows, nQ,
-                     nK, n_chunks, layout, row, crow, total);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t n_cols = (int64_t)BH * nK;
-  hipLaunchKernelGGL(popcount_cols_kernel, dim3((unsigned)((n_cols + 255) / 256)), dim3(256), 0, stream,
-                     mask, BH, nQ, nK, col);
+hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_chunks, int layout, int32_t* row,
+                           int32_t* col, int32_t* crow, hipStream_t stream) {
+  if (BH == 0) return hipSuccess;
+  hipLaunchKernelGGL(popcount_kernel, dim3(BH), dim3(256), 0, stream, mask, nQ, nK, n_chunks, layout, row, col,
+                     crow);
   return hipGetLastError();
 }
 

@@ -54,6 +54,19 @@ def test_host_assign_bit_exact_random(order):
         assert np.array_equal(items, oi) and np.array_equal(ptr, op) and np.array_equal(bl, ob)
 
 
+def test_host_assign_bit_exact_large_loads():
+    """Loads beyond the counting-sort and load-bucket ranges take the comparison-sort and heap paths."""
+    rng = np.random.default_rng(1)
+    for trial in range(10):
+        n = int(rng.integers(1, 300))
+        m = int(rng.integers(1, 33))
+        loads = rng.integers(0, 10 ** 9, size=n)
+        loads[: n // 3] = rng.integers(0, 3, size=n // 3)  # with many small and equal loads
+        items, ptr, bl = bd.sparse_attn_assign_host(loads, m, "lpt")
+        oi, op, ob = _oracle_lists(loads, m, "lpt")
+        assert np.array_equal(items, oi) and np.array_equal(ptr, op) and np.array_equal(bl, ob)
+
+
 def test_host_assign_page_example():
     items, ptr, bl = bd.sparse_attn_assign_host([8, 7, 6, 5, 4], 2)
     assert items.tolist() == [0, 3, 4, 1, 2] and ptr.tolist() == [0, 3, 5] and bl.tolist() == [17, 13]
