@@ -164,6 +164,7 @@ def main() -> int:
     ap.add_argument("--mode", choices=["merged", "fused"], default="merged",
                     help="merged: partial chunks + chunk_merge (default); fused: chunks folded in-kernel")
     ap.add_argument("--order", choices=["lpt", "naive"], default="lpt")
+    ap.add_argument("--bins", type=int, default=0, help="persistent workgroups (0: one per resident slot)")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the untimed breakdown runs")
@@ -202,10 +203,14 @@ def main() -> int:
     out = torch.empty_like(q)
     rows = B * H * S
     stream = torch.cuda.current_stream()
+    # the plan of a step is built on a side stream: its host part (counts, LPT, uploads) then
+    # overlaps the previous step's attention on the main stream, and the forward call waits
+    # for the plan's uploads by itself
+    plan_stream = torch.cuda.Stream()
     fwd_events = []
 
     def step(record: bool):
-        plan = bd.sparse_attn_plan(prob, "block", mask=mask, order=args.order)
+        plan = bd.sparse_attn_plan(prob, "block", mask=mask, order=args.order, num_bins=args.bins, stream=plan_stream)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -225,12 +230,9 @@ def main() -> int:
         step(False).close()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    plans = []
+    plans = []  # destroyed after the timed region (destroying a plan synchronises the device)
     for _ in range(args.steps):
-        p = step(True)
-        plans.append(p)
-        if len(plans) > 2:
-            plans.pop(0).close()
+        plans.append(step(True))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for p in plans:
@@ -238,7 +240,7 @@ def main() -> int:
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in fwd_events]))
 
-    plan = bd.sparse_attn_plan(prob, "block", mask=mask, order=args.order)
+    plan = bd.sparse_attn_plan(prob, "block", mask=mask, order=args.order, num_bins=args.bins)
     info = bd.sparse_attn_plan_info(plan)
     flop = 4.0 * w.block * w.block * D * info["total_live"]
     value = flop / (ms_per_step * 1e-3) / 1e12

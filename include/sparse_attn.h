@@ -132,10 +132,15 @@ typedef enum {
  *  (row/column sums of the db-SP post, scenario 2), copies the row counts to
  *  the host and runs the LPT greedy of the same post (longest item to the
  *  least-loaded bin; ties: lower item id first, lower bin index) — or
- *  round-robin for SA_ORDER_NAIVE — once over the full chunk range and once
- *  per chunk; the lists are uploaded for the persistent kernel.  This kind
- *  synchronises the stream.
+ *  round-robin for SA_ORDER_NAIVE — over the full chunk range, and uploads
+ *  the list for the persistent kernel.  The list of a single chunk c (used by
+ *  sparse_attn_fwd over [c, c+1), one ring step) is built from the same counts
+ *  on its first use (that forward call, which then waits for its upload once,
+ *  or sparse_attn_plan_copy).  This kind synchronises the stream once.
  *  TOPK: runs the indexer and top-k selection on the GPU; asynchronous.
+ *  All kinds: the plan's device arrays are written on `stream`; sparse_attn_fwd
+ *  makes its own stream wait for them, so a plan may be built on a side stream
+ *  (for instance the next step's plan while the current step computes).
  *  num_bins: persistent workgroups; 0 picks one per resident workgroup slot
  *  (bf16: 1 per compute unit for block 128, 2 for block 64; f32: 1).
  *  out (host): receives the plan.  Returns SA_ERR_NOMEM if the plan's device

@@ -109,7 +109,7 @@ def _ptr(t) -> Optional[int]:
 
 def _stream(stream) -> Optional[int]:
     if stream is not None:
-        return int(stream)
+        return int(getattr(stream, "cuda_stream", stream))  # a torch stream or a raw handle
     import torch
     return int(torch.cuda.current_stream().cuda_stream)
 

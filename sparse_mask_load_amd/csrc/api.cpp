@@ -6,6 +6,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <memory>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -29,12 +31,21 @@ struct sa_plan {
   int32_t* d_bin_ptr = nullptr;      // [(C+1)][num_bins+1]
   std::vector<int32_t> h_items, h_bin_ptr;
   std::vector<int64_t> h_bin_load;   // [(C+1)][num_bins]
+  // The full-range list is built by the plan call; the list of chunk c (used by forward calls
+  // over that chunk alone, as in one ring step) is built on first use from the host counts.
+  std::vector<int32_t> h_crow;       // [B*H*C*nQ] per-chunk row counts
+  std::unique_ptr<std::once_flag[]> list_once;
+  std::unique_ptr<bool[]> list_uploaded;
+  std::mutex upload_mutex;
   int64_t total_live = 0, load_sum = 0, makespan = 0, lower_bound = 0;
   // TOPK / INDEX
   int32_t* d_idx = nullptr;          // [B][H][S][top_k]
   int32_t* d_count = nullptr;        // [B][H][S]
   __bf16* d_qp = nullptr;            // [B][H][S][rank]
   __bf16* d_kp = nullptr;
+  // recorded on the plan's stream once its device arrays are complete; every forward call
+  // makes its own stream wait for it, so a plan may be built on a side stream
+  hipEvent_t ready = nullptr;
 };
 
 namespace {
@@ -118,6 +129,7 @@ void free_plan(sa_plan* p) {
                   p->d_bin_ptr, p->d_idx, p->d_count, p->d_qp, p->d_kp};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
+  if (p->ready) (void)hipEventDestroy(p->ready);
   delete p;
 }
 
@@ -125,7 +137,7 @@ int default_bins(const sa_problem& p, int device) {
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
     cus = 256;
-  // one bin per resident workgroup: the bf16 kernel keeps 2 (block 128) or 4 (block 64) per CU
+  // one bin per resident workgroup: the bf16 kernel keeps 1 (block 128) or 2 (block 64) per CU
   return p.dtype == SA_BF16 ? cus * sa::attn_bf16_wg_per_cu(p.block) : cus;
 }
 
@@ -154,20 +166,14 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   P->h_items.assign((size_t)(C + 1) * n, 0);
   P->h_bin_ptr.assign((size_t)(C + 1) * (m + 1), 0);
   P->h_bin_load.assign((size_t)(C + 1) * m, 0);
-  std::vector<int64_t> loads(n);
-  for (int list = 0; list <= C; ++list) {
-    if (list == 0) {
-      for (int i = 0; i < n; ++i) loads[i] = row[i];
-    } else {
-      const int c = list - 1;
-      for (int i = 0; i < n; ++i) {
-        const int bh = i / nQ, q = i % nQ;
-        loads[i] = crow[((size_t)bh * C + c) * nQ + q];
-      }
-    }
-    sa::assign(loads.data(), n, m, P->order, P->h_items.data() + (size_t)list * n,
-               P->h_bin_ptr.data() + (size_t)list * (m + 1), P->h_bin_load.data() + (size_t)list * m);
+  P->h_crow = std::move(crow);
+  P->list_once.reset(new std::once_flag[C + 1]);
+  P->list_uploaded.reset(new bool[C + 1]());
+  {
+    std::vector<int64_t> loads(row.begin(), row.end());
+    sa::assign(loads.data(), n, m, P->order, P->h_items.data(), P->h_bin_ptr.data(), P->h_bin_load.data());
   }
+  std::call_once(P->list_once[0], [] {});  // list 0 is built
   int64_t sum = 0, pmax = 0;
   for (int i = 0; i < n; ++i) {
     sum += row[i];
@@ -177,9 +183,36 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   P->total_live = sum;  // every live tile belongs to exactly one Q-block row
   P->makespan = *std::max_element(P->h_bin_load.begin(), P->h_bin_load.begin() + m);
   P->lower_bound = std::max<int64_t>(pmax, (sum + m - 1) / m);
-  SA_HIP(hipMemcpyAsync(P->d_items, P->h_items.data(), P->h_items.size() * 4, hipMemcpyHostToDevice, stream));
-  SA_HIP(hipMemcpyAsync(P->d_bin_ptr, P->h_bin_ptr.data(), P->h_bin_ptr.size() * 4, hipMemcpyHostToDevice,
-                        stream));
+  SA_HIP(hipMemcpyAsync(P->d_items, P->h_items.data(), (size_t)n * 4, hipMemcpyHostToDevice, stream));
+  SA_HIP(hipMemcpyAsync(P->d_bin_ptr, P->h_bin_ptr.data(), (size_t)(m + 1) * 4, hipMemcpyHostToDevice, stream));
+  P->list_uploaded[0] = true;
+  return SA_OK;
+}
+
+// Host lists of chunk `list - 1` (LPT or round-robin over the chunk's row counts), once.
+void build_chunk_list(sa_plan* P, int list) {
+  std::call_once(P->list_once[list], [P, list] {
+    const int C = P->prob.n_chunks, nQ = P->nQ, n = P->n_items, m = P->num_bins, c = list - 1;
+    std::vector<int64_t> loads(n);
+    for (int i = 0; i < n; ++i) loads[i] = P->h_crow[((size_t)(i / nQ) * C + c) * nQ + i % nQ];
+    sa::assign(loads.data(), n, m, P->order, P->h_items.data() + (size_t)list * n,
+               P->h_bin_ptr.data() + (size_t)list * (m + 1), P->h_bin_load.data() + (size_t)list * m);
+  });
+}
+
+// Device copy of list `list` (built on the host first if needed), ordered on `stream`.
+sa_status ensure_list_on_device(sa_plan* P, int list, hipStream_t stream) {
+  build_chunk_list(P, list);
+  std::lock_guard<std::mutex> lock(P->upload_mutex);
+  if (P->list_uploaded[list]) return SA_OK;
+  const int n = P->n_items, m = P->num_bins;
+  SA_HIP(hipMemcpyAsync(P->d_items + (size_t)list * n, P->h_items.data() + (size_t)list * n, (size_t)n * 4,
+                        hipMemcpyHostToDevice, stream));
+  SA_HIP(hipMemcpyAsync(P->d_bin_ptr + (size_t)list * (m + 1), P->h_bin_ptr.data() + (size_t)list * (m + 1),
+                        (size_t)(m + 1) * 4, hipMemcpyHostToDevice, stream));
+  // later calls on other streams must not race the copy: wait for it here (first use only)
+  SA_HIP(hipStreamSynchronize(stream));
+  P->list_uploaded[list] = true;
   return SA_OK;
 }
 
@@ -260,6 +293,11 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
   }
   P->num_bins = num_bins ? num_bins : default_bins(*prob, P->device);
   st = sp->kind == SA_KIND_BLOCK ? plan_block(P, sp, stream) : plan_topk(P, sp, stream);
+  if (!st) {
+    hipError_t e = hipEventCreateWithFlags(&P->ready, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(P->ready, stream);
+    if (e != hipSuccess) st = hip_fail(e, "plan completion event");
+  }
   if (st) {
     std::string keep = g_last_error;
     free_plan(P);
@@ -276,6 +314,7 @@ sa_status sparse_attn_fwd(const sa_plan* P, const void* q, const void* k, const 
   if (!P) return fail(SA_ERR_INVALID, "plan is NULL");
   if (!q || !k || !v) return fail(SA_ERR_INVALID, "q, k or v is NULL");
   const sa_problem& pr = P->prob;
+  if (P->ready) SA_HIP(hipStreamWaitEvent(stream, P->ready, 0));  // the plan may come from another stream
   if (P->kind != SA_KIND_BLOCK) {
     if (!o) return fail(SA_ERR_INVALID, "top-k plans support full mode only (o must be non-NULL)");
     if (chunk_begin != 0 || chunk_end != 1) return fail(SA_ERR_INVALID, "top-k plans take the chunk range [0, 1)");
@@ -292,6 +331,10 @@ sa_status sparse_attn_fwd(const sa_plan* P, const void* q, const void* k, const 
   if (!o && (!o_part || !m_part || !l_part))
     return fail(SA_ERR_INVALID, "partial mode needs o_part, m_part and l_part");
   const int list = (chunk_end - chunk_begin == 1) ? 1 + chunk_begin : 0;
+  if (list > 0) {
+    const sa_status st = ensure_list_on_device(const_cast<sa_plan*>(P), list, stream);
+    if (st) return st;
+  }
   sa::FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.o_part = o ? nullptr : o_part;
@@ -366,6 +409,8 @@ sa_status sparse_attn_plan_copy(const sa_plan* P, int32_t what, int32_t chunk, v
     if (chunk < -1 || chunk >= C) return fail(SA_ERR_INVALID, "chunk %d outside [-1, %d)", chunk, C);
   }
   const int list = chunk + 1;
+  if (block && list > 0 && (what == SA_PLAN_ITEMS || what == SA_PLAN_BIN_PTR || what == SA_PLAN_BIN_LOAD))
+    build_chunk_list(const_cast<sa_plan*>(P), list);
   const void* src = nullptr;
   bool device = true;
   int64_t count = 0;

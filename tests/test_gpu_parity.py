@@ -287,3 +287,17 @@ def test_fwd_argument_errors_on_gpu():
     with pytest.raises(bd.SparseAttnError) as e:
         bd.sparse_attn_fwd(plan, q, k, v, 0, 2, o=None, o_part=torch.empty(1, device="cuda"))
     assert e.value.status == bd.SA_ERR_INVALID
+
+
+def test_plan_on_side_stream():
+    """A plan built on another stream: the forward call on the main stream waits for its lists."""
+    w = W.make_custom(1, 2, 512, 128, block=128, n_chunks=2, pattern="bernoulli", density=0.6, seed=21)
+    q, k, v = G.upload(w)
+    side = torch.cuda.Stream()
+    mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
+    torch.cuda.synchronize()
+    plan = bd.sparse_attn_plan(bd.make_problem(q, w.block, w.n_chunks, w.layout), "block", mask=mask, stream=side)
+    o = G.empty_like_qkv(q)
+    bd.sparse_attn_fwd(plan, q, k, v, 0, w.n_chunks, o=o)  # current stream
+    torch.cuda.synchronize()
+    G.assert_close(G.to64(o), _full_oracle(w), G.tol_for(w), "side-stream plan")
