@@ -2,10 +2,12 @@
 
 One step = one pass of the whole path over one batch of the causal long-sequence
 workload (B1 H16 S16384 d128, block 128, lower-triangular block mask, KV in 4 contiguous
-chunks, LPT over one bin per compute unit):
+chunks, two-level LPT over one bin per compute unit: heads to the XCDs, then Q-blocks to
+each XCD's bins):
 
   1. sparse_attn_plan: GPU popcount of the mask + host LPT + upload of the work lists
-     (the mask is a runtime input, so every step re-plans);
+     (the mask is a runtime input, so every step re-plans; the plan is built on a side
+     stream, so its host part overlaps the previous step's attention);
   2. sparse_attn_fwd in partial mode over chunks [0, 4): one (O, m, l) partial per chunk;
   3. chunk_merge: online-softmax merge of the 4 partials into O (bf16).
 
@@ -163,7 +165,8 @@ def main() -> int:
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="causal")
     ap.add_argument("--mode", choices=["merged", "fused"], default="merged",
                     help="merged: partial chunks + chunk_merge (default); fused: chunks folded in-kernel")
-    ap.add_argument("--order", choices=["lpt", "naive"], default="lpt")
+    ap.add_argument("--order", choices=["lpt_xcd", "lpt", "naive"], default="lpt_xcd",
+                    help="work order: two-level LPT (heads to XCDs, then Q-blocks), one-level LPT, round-robin")
     ap.add_argument("--bins", type=int, default=0, help="persistent workgroups (0: one per resident slot)")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -253,7 +256,7 @@ def main() -> int:
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name} block-sparse MHA B{B} H{H} S{S} d{D} block {w.block}, "
                                f"{C} {w.layout} KV chunks {'merged by chunk_merge' if args.mode == 'merged' else 'folded in-kernel'}, "
-                               f"{args.order.upper()} over {info['num_bins']} bins",
+                               f"{ {'lpt_xcd': 'two-level LPT (heads to XCDs, then Q-blocks)', 'lpt': 'LPT', 'naive': 'round-robin'}[args.order]} over {info['num_bins']} bins",
                    "B": B, "H": H, "S": S, "D": D, "block": w.block, "n_chunks": C, "layout": w.layout,
                    "mask": {"tiny": "Bernoulli(0.5)+diag", "video": "frame band / Bernoulli",
                             "causal": "block lower-triangular", "skewed": "Zipf(1.2) rows"}[args.workload],
@@ -294,20 +297,25 @@ def main() -> int:
         for _ in range(reps):
             bd.sparse_attn_plan(prob, "block", mask=mask, order=args.order).close()
         plan_ms = (time.perf_counter() - t_plan) * 1e3 / reps
-        naive = bd.sparse_attn_plan(prob, "block", mask=mask, order="naive")
-        e0.record(stream)
-        for _ in range(reps):
-            bd.sparse_attn_fwd(naive, q, k, v, 0, C, o=out)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        naive_ms = e0.elapsed_time(e1) / reps
-        naive.close()
+        alt_ms = {}
+        for alt in ("naive", "lpt", "lpt_xcd"):
+            p_alt = bd.sparse_attn_plan(prob, "block", mask=mask, order=alt)
+            e0.record(stream)
+            for _ in range(reps):
+                bd.sparse_attn_fwd(p_alt, q, k, v, 0, C, o=out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            alt_ms[alt] = (e0.elapsed_time(e1) / reps, bd.sparse_attn_plan_info(p_alt))
+            p_alt.close()
+
         result["breakdown"] = {
             "plan_ms": round(plan_ms, 4), "fwd_partial_ms": round(kernel_ms, 4),
             "fwd_fused_ms": round(fused_ms, 4), "fused_tflops": round(flop / fused_ms / 1e9, 2),
             "fused_pct_bf16_peak": round(100 * flop / fused_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
             "merge_ms": round(merge_ms, 4), "merge_gbs": round(merge_bytes / merge_ms / 1e6, 1),
-            "fwd_fused_naive_order_ms": round(naive_ms, 4),
+            "fwd_fused_ms_by_order": {o: round(t, 4) for o, (t, _) in alt_ms.items()},
+            "makespan_tiles_by_order": {o: i["makespan"] for o, (_, i) in alt_ms.items()},
+            "xcd_groups": alt_ms["lpt_xcd"][1]["groups"],
         }
     plan.close()
 

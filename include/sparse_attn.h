@@ -50,7 +50,15 @@ typedef enum {
 } sa_status;
 
 typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
-typedef enum { SA_ORDER_LPT = 0, SA_ORDER_NAIVE = 1 } sa_order;
+/* Work order of a block plan (db-SP post, LPT paragraph).
+ *  SA_ORDER_LPT:     one LPT pass over all (b, h, Q-block) items onto the bins.
+ *  SA_ORDER_NAIVE:   item i to bin i mod num_bins (round-robin in id order).
+ *  SA_ORDER_LPT_XCD: two-level LPT for L2 locality (the post's "stay-home" bonus
+ *                    re-read for one chip): heads to the chip's XCDs by LPT on
+ *                    head loads, then each XCD's items by LPT onto its bins (bin b
+ *                    runs on XCD b mod #XCDs).  Plain LPT when num_bins is not a
+ *                    multiple of the XCD count. */
+typedef enum { SA_ORDER_LPT = 0, SA_ORDER_NAIVE = 1, SA_ORDER_LPT_XCD = 2 } sa_order;
 typedef enum { SA_LAYOUT_CONTIGUOUS = 0, SA_LAYOUT_STRIPED = 1 } sa_layout;
 typedef enum { SA_KIND_BLOCK = 0, SA_KIND_TOPK = 1, SA_KIND_INDEX = 2 } sa_kind;
 
@@ -113,6 +121,8 @@ typedef struct {
   int64_t load_sum;     /* sum of the full-range item loads (= total_live for BLOCK) */
   int64_t makespan;     /* max bin load of the full-range list */
   int64_t lower_bound;  /* max(max item load, ceil(load_sum / num_bins)) */
+  int32_t groups;       /* bin groups of SA_ORDER_LPT_XCD (XCDs), 1 otherwise */
+  int32_t reserved;
 } sa_plan_info;
 
 /* Arrays that sparse_attn_plan_copy can export to host memory. */
@@ -189,6 +199,16 @@ sa_status sparse_attn_plan_copy(const sa_plan* plan, int32_t what, int32_t chunk
  *  [m+1]; bin_load_out (host, nullable) [m].  Touches no GPU. */
 sa_status sparse_attn_assign_host(const int64_t* loads, int32_t n, int32_t m, int32_t order,
                                   int32_t* items_out, int32_t* bin_ptr_out, int64_t* bin_load_out);
+
+/* Host-only two-level LPT (SA_ORDER_LPT_XCD), the same code the plan uses:
+ *  loads (host) [n_heads * items_per_head], item i = head * items_per_head + q;
+ *  heads go to `groups` bin groups (bins b with b mod groups == g), then each
+ *  group's items (its heads in assignment order, then q) to its bins by LPT.
+ *  Plain LPT when groups <= 1 or m is not a multiple of groups.  Outputs as in
+ *  sparse_attn_assign_host.  Touches no GPU. */
+sa_status sparse_attn_assign_host_grouped(const int64_t* loads, int32_t n_heads, int32_t items_per_head, int32_t m,
+                                          int32_t groups, int32_t* items_out, int32_t* bin_ptr_out,
+                                          int64_t* bin_load_out);
 
 /* Free a plan.  Synchronises the device first.  NULL is a no-op. */
 void sparse_attn_plan_destroy(sa_plan* plan);

@@ -71,6 +71,37 @@ def lpt(loads: Sequence[int], m: int) -> Tuple[List[List[int]], List[int]]:
     return bins, bin_load
 
 
+def lpt_grouped(loads: Sequence[int], items_per_head: int, m: int, groups: int
+                ) -> Tuple[List[List[int]], List[int]]:
+    """Two-level LPT: heads onto bin groups, then each group's items onto its bins.
+
+    The db-SP post rewards keeping a head's blocks where the head already is
+    (its "stay-home" bonus); on one chip the place is the L2 of one XCD, whose
+    compute units run the persistent workgroups b with b mod groups == g.  Job
+    i = head * items_per_head + q.  Level 1 is LPT of the heads (load = sum of
+    their items) onto ``groups`` machines; level 2 is, per group g, LPT of the
+    items of g's heads (taken in the order the heads were given to g, then by
+    q) onto the m / groups bins of g, whose k-th bin is bin k * groups + g.
+    With groups = 1 (or m not a multiple of groups) this is plain LPT.
+    """
+    n = len(loads)
+    if groups <= 1 or m % groups != 0:
+        return lpt(loads, m)
+    n_heads = n // items_per_head
+    head_loads = [sum(int(x) for x in loads[h * items_per_head:(h + 1) * items_per_head]) for h in range(n_heads)]
+    head_bins, _ = lpt(head_loads, groups)
+    per = m // groups
+    bins: List[List[int]] = [[] for _ in range(m)]
+    bin_load = [0] * m
+    for g in range(groups):
+        ids = [h * items_per_head + q for h in head_bins[g] for q in range(items_per_head)]
+        local_bins, local_loads = lpt([loads[i] for i in ids], per)
+        for k in range(per):
+            bins[k * groups + g] = [ids[j] for j in local_bins[k]]
+            bin_load[k * groups + g] = local_loads[k]
+    return bins, bin_load
+
+
 def naive(loads: Sequence[int], m: int) -> Tuple[List[List[int]], List[int]]:
     """Round-robin in job-id order: job i runs on machine i mod m."""
     bins: List[List[int]] = [[] for _ in range(m)]
@@ -94,14 +125,20 @@ def brute_force_makespan(loads: Sequence[int], m: int) -> Tuple[int, Tuple[int, 
     return best, best_assign
 
 
-def plan_items(row_loads: np.ndarray, m: int, order: str = "lpt") -> Dict[str, np.ndarray]:
+def plan_items(row_loads: np.ndarray, m: int, order: str = "lpt", groups: int = 1) -> Dict[str, np.ndarray]:
     """Assign every (b, h, q) item (id = (b*H + h)*nQ + q, load = row count) to m bins.
 
-    Returns ``items`` (all bins' lists concatenated), ``bin_ptr`` (m + 1 offsets),
-    ``bin_load`` and ``makespan``.
+    ``order``: "lpt", "naive" or "lpt_xcd" (``lpt_grouped`` with the heads of
+    ``row_loads`` [B, H, nQ] and ``groups`` bin groups).  Returns ``items`` (all
+    bins' lists concatenated), ``bin_ptr`` (m + 1 offsets), ``bin_load`` and
+    ``makespan``.
     """
-    loads = np.asarray(row_loads, dtype=np.int64).reshape(-1).tolist()
-    bins, bin_load = (lpt if order == "lpt" else naive)(loads, m)
+    row_loads = np.asarray(row_loads, dtype=np.int64)
+    loads = row_loads.reshape(-1).tolist()
+    if order == "lpt_xcd":
+        bins, bin_load = lpt_grouped(loads, row_loads.shape[-1], m, groups)
+    else:
+        bins, bin_load = (lpt if order == "lpt" else naive)(loads, m)
     items, ptr = [], [0]
     for b in bins:
         items.extend(b)

@@ -18,14 +18,14 @@ LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 
 SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_NOMEM = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
-SA_ORDER_LPT, SA_ORDER_NAIVE = 0, 1
+SA_ORDER_LPT, SA_ORDER_NAIVE, SA_ORDER_LPT_XCD = 0, 1, 2
 SA_LAYOUT_CONTIGUOUS, SA_LAYOUT_STRIPED = 0, 1
 SA_KIND_BLOCK, SA_KIND_TOPK, SA_KIND_INDEX = 0, 1, 2
 (SA_PLAN_ROW, SA_PLAN_COL, SA_PLAN_CROW, SA_PLAN_ITEMS, SA_PLAN_BIN_PTR, SA_PLAN_BIN_LOAD,
  SA_PLAN_TOPK_IDX, SA_PLAN_TOPK_COUNT) = range(8)
 
 _DTYPES = {"f32": SA_F32, "bf16": SA_BF16}
-_ORDERS = {"lpt": SA_ORDER_LPT, "naive": SA_ORDER_NAIVE}
+_ORDERS = {"lpt": SA_ORDER_LPT, "naive": SA_ORDER_NAIVE, "lpt_xcd": SA_ORDER_LPT_XCD}
 _LAYOUTS = {"contiguous": SA_LAYOUT_CONTIGUOUS, "striped": SA_LAYOUT_STRIPED}
 
 
@@ -53,7 +53,8 @@ class sa_plan_info(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("num_bins", ctypes.c_int32), ("order", ctypes.c_int32),
                 ("n_chunks", ctypes.c_int32), ("nQ", ctypes.c_int32), ("nK", ctypes.c_int32),
                 ("n_items", ctypes.c_int32), ("top_k", ctypes.c_int32), ("total_live", ctypes.c_int64),
-                ("load_sum", ctypes.c_int64), ("makespan", ctypes.c_int64), ("lower_bound", ctypes.c_int64)]
+                ("load_sum", ctypes.c_int64), ("makespan", ctypes.c_int64), ("lower_bound", ctypes.c_int64),
+                ("groups", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -66,6 +67,8 @@ _SIGNATURES = {
     "sparse_attn_plan_info": (ctypes.c_int32, [_P, ctypes.POINTER(sa_plan_info)]),
     "sparse_attn_plan_copy": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64]),
     "sparse_attn_assign_host": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "sparse_attn_assign_host_grouped": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                         ctypes.c_int32, _P, _P, _P]),
     "sparse_attn_plan_destroy": (None, [_P]),
     "sa_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "sa_last_error": (ctypes.c_char_p, []),
@@ -199,6 +202,18 @@ def sparse_attn_assign_host(loads, m: int, order: str = "lpt"):
     bl = np.empty(m, np.int64)
     _check(lib().sparse_attn_assign_host(loads.ctypes.data, n, m, _ORDERS[order], items.ctypes.data,
                                          ptr.ctypes.data, bl.ctypes.data), "sparse_attn_assign_host")
+    return items[:n], ptr, bl
+
+
+def sparse_attn_assign_host_grouped(loads, items_per_head: int, m: int, groups: int):
+    loads = np.ascontiguousarray(loads, dtype=np.int64).reshape(-1)
+    n = loads.shape[0]
+    items = np.empty(max(n, 1), np.int32)
+    ptr = np.empty(m + 1, np.int32)
+    bl = np.empty(m, np.int64)
+    _check(lib().sparse_attn_assign_host_grouped(loads.ctypes.data, n // items_per_head, items_per_head, m, groups,
+                                                 items.ctypes.data, ptr.ctypes.data, bl.ctypes.data),
+           "sparse_attn_assign_host_grouped")
     return items[:n], ptr, bl
 
 

@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -20,6 +21,7 @@ struct sa_plan {
   int32_t kind = SA_KIND_BLOCK;
   int32_t num_bins = 0;
   int32_t order = SA_ORDER_LPT;
+  int32_t groups = 1;  // bin groups of SA_ORDER_LPT_XCD (one per XCD), else 1
   int32_t nQ = 0, nK = 0, n_items = 0, top_k = 0, rank = 0, causal = 0;
   int device = 0;
   // BLOCK
@@ -141,6 +143,23 @@ int default_bins(const sa_problem& p, int device) {
   return p.dtype == SA_BF16 ? cus * sa::attn_bf16_wg_per_cu(p.block) : cus;
 }
 
+// One work list of a block plan from per-item loads, in the plan's order.
+void assign_list(const sa_plan* P, const int64_t* loads, int32_t* items, int32_t* bin_ptr, int64_t* bin_load) {
+  const int m = P->num_bins, n = P->n_items;
+  if (P->order == SA_ORDER_LPT_XCD)
+    sa::assign_grouped(loads, n / P->nQ, P->nQ, m, P->groups, items, bin_ptr, bin_load);
+  else
+    sa::assign(loads, n, m, P->order, items, bin_ptr, bin_load);
+}
+
+// Number of XCDs (L2 domains) of the device; the persistent workgroups are dispatched to
+// them round-robin, so workgroup b runs on XCD b mod this count.
+int xcd_count(int device) {
+  int x = 0;
+  if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, device) != hipSuccess || x <= 0) x = 1;
+  return x;
+}
+
 sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   const sa_problem& pr = P->prob;
   const int BH = pr.B * pr.H, C = pr.n_chunks;
@@ -171,7 +190,7 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   P->list_uploaded.reset(new bool[C + 1]());
   {
     std::vector<int64_t> loads(row.begin(), row.end());
-    sa::assign(loads.data(), n, m, P->order, P->h_items.data(), P->h_bin_ptr.data(), P->h_bin_load.data());
+    assign_list(P, loads.data(), P->h_items.data(), P->h_bin_ptr.data(), P->h_bin_load.data());
   }
   std::call_once(P->list_once[0], [] {});  // list 0 is built
   int64_t sum = 0, pmax = 0;
@@ -195,8 +214,8 @@ void build_chunk_list(sa_plan* P, int list) {
     const int C = P->prob.n_chunks, nQ = P->nQ, n = P->n_items, m = P->num_bins, c = list - 1;
     std::vector<int64_t> loads(n);
     for (int i = 0; i < n; ++i) loads[i] = P->h_crow[((size_t)(i / nQ) * C + c) * nQ + i % nQ];
-    sa::assign(loads.data(), n, m, P->order, P->h_items.data() + (size_t)list * n,
-               P->h_bin_ptr.data() + (size_t)list * (m + 1), P->h_bin_load.data() + (size_t)list * m);
+    assign_list(P, loads.data(), P->h_items.data() + (size_t)list * n, P->h_bin_ptr.data() + (size_t)list * (m + 1),
+                P->h_bin_load.data() + (size_t)list * m);
   });
 }
 
@@ -280,7 +299,8 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
     return fail(SA_ERR_INVALID, "unknown sparsity kind %d", sp->kind);
   sa_status st = validate_problem(prob, sp->kind == SA_KIND_BLOCK);
   if (st) return st;
-  if (order != SA_ORDER_LPT && order != SA_ORDER_NAIVE) return fail(SA_ERR_INVALID, "unknown order %d", order);
+  if (order != SA_ORDER_LPT && order != SA_ORDER_NAIVE && order != SA_ORDER_LPT_XCD)
+    return fail(SA_ERR_INVALID, "unknown order %d", order);
   if (num_bins < 0) return fail(SA_ERR_INVALID, "num_bins %d < 0", num_bins);
   sa_plan* P = new (std::nothrow) sa_plan();
   if (!P) return fail(SA_ERR_NOMEM, "host allocation of the plan failed");
@@ -292,6 +312,10 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
     return fail(SA_ERR_HIP, "hipGetDevice failed");
   }
   P->num_bins = num_bins ? num_bins : default_bins(*prob, P->device);
+  if (order == SA_ORDER_LPT_XCD) {
+    P->groups = xcd_count(P->device);
+    if (P->num_bins % P->groups != 0) P->groups = 1;  // groups must split the bins evenly
+  }
   st = sp->kind == SA_KIND_BLOCK ? plan_block(P, sp, stream) : plan_topk(P, sp, stream);
   if (!st) {
     hipError_t e = hipEventCreateWithFlags(&P->ready, hipEventDisableTiming);
@@ -395,6 +419,7 @@ sa_status sparse_attn_plan_info(const sa_plan* P, sa_plan_info* out) {
   out->load_sum = P->load_sum;
   out->makespan = P->makespan;
   out->lower_bound = P->lower_bound;
+  out->groups = P->groups;
   return SA_OK;
 }
 
@@ -448,6 +473,20 @@ sa_status sparse_attn_assign_host(const int64_t* loads, int32_t n, int32_t m, in
   for (int i = 0; i < n; ++i)
     if (loads[i] < 0) return fail(SA_ERR_INVALID, "loads[%d] = %lld < 0", i, (long long)loads[i]);
   sa::assign(loads, n, m, order, items_out, bin_ptr_out, bin_load_out);
+  return SA_OK;
+}
+
+sa_status sparse_attn_assign_host_grouped(const int64_t* loads, int32_t n_heads, int32_t items_per_head, int32_t m,
+                                          int32_t groups, int32_t* items_out, int32_t* bin_ptr_out,
+                                          int64_t* bin_load_out) {
+  if (n_heads < 0 || items_per_head <= 0 || m <= 0 || groups <= 0)
+    return fail(SA_ERR_INVALID, "need n_heads >= 0, items_per_head > 0, m > 0, groups > 0");
+  const int64_t n = (int64_t)n_heads * items_per_head;
+  if (n > INT32_MAX) return fail(SA_ERR_INVALID, "too many items");
+  if ((n > 0 && (!loads || !items_out)) || !bin_ptr_out) return fail(SA_ERR_INVALID, "NULL argument");
+  for (int64_t i = 0; i < n; ++i)
+    if (loads[i] < 0) return fail(SA_ERR_INVALID, "loads[%lld] = %lld < 0", (long long)i, (long long)loads[i]);
+  sa::assign_grouped(loads, n_heads, items_per_head, m, groups, items_out, bin_ptr_out, bin_load_out);
   return SA_OK;
 }
 

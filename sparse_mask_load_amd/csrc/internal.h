@@ -96,5 +96,9 @@ hipError_t launch_gather_attn(const GatherArgs& a, hipStream_t stream);
 //   NAIVE: item i goes to bin i mod m, in id order.
 void assign(const int64_t* loads, int n, int m, int order, int32_t* items_out, int32_t* bin_ptr_out,
             int64_t* bin_load_out);
+// Two-level LPT: heads to bin groups (bins b with b mod groups == g), then each group's
+// items to its bins (lpt.cpp).  n = n_heads * per_head items, item id = head * per_head + q.
+void assign_grouped(const int64_t* loads, int n_heads, int per_head, int m, int groups, int32_t* items_out,
+                    int32_t* bin_ptr_out, int64_t* bin_load_out);
 
 }  // namespace sa

@@ -107,4 +107,55 @@ void assign(const int64_t* loads, int n, int m, int order, int32_t* items_out, i
     for (int b = 0; b < m; ++b) bin_load_out[b] = bin_load[b];
 }
 
+// Two-level LPT for XCD affinity (the db-SP "stay-home" bonus re-read for one
+// chip): a head's items should share one XCD's L2, and the persistent
+// workgroups b with b mod groups == g run on XCD g.  Level 1 assigns heads
+// (load = sum of their items) to the groups by LPT; level 2 assigns, per group,
+// the items of its heads (in the order the heads were given to the group,
+// then by Q-block) to the group's bins by LPT; the k-th bin of group g is bin
+// k * groups + g.  With groups <= 1, or m not a multiple of groups, plain LPT.
+void assign_grouped(const int64_t* loads, int n_heads, int per_head, int m, int groups, int32_t* items_out,
+                    int32_t* bin_ptr_out, int64_t* bin_load_out) {
+  const int n = n_heads * per_head;
+  if (groups <= 1 || m % groups != 0) {
+    assign(loads, n, m, SA_ORDER_LPT, items_out, bin_ptr_out, bin_load_out);
+    return;
+  }
+  std::vector<int64_t> head_load(n_heads, 0);
+  for (int h = 0; h < n_heads; ++h)
+    for (int q = 0; q < per_head; ++q) head_load[h] += loads[(size_t)h * per_head + q];
+  std::vector<int32_t> heads(std::max(n_heads, 1)), head_ptr(groups + 1);
+  assign(head_load.data(), n_heads, groups, SA_ORDER_LPT, heads.data(), head_ptr.data(), nullptr);
+  const int per = m / groups;
+  std::vector<int32_t> bin_of(n), rank_in_bin(n), bin_count(m, 0);
+  std::vector<int64_t> bin_load(m, 0);
+  std::vector<int32_t> order(n);  // items in global assignment order within their bins
+  for (int g = 0; g < groups; ++g) {
+    std::vector<int32_t> ids;
+    for (int p = head_ptr[g]; p < head_ptr[g + 1]; ++p)
+      for (int q = 0; q < per_head; ++q) ids.push_back(heads[p] * per_head + q);
+    const int ng = (int)ids.size();
+    std::vector<int64_t> local(ng);
+    for (int i = 0; i < ng; ++i) local[i] = loads[ids[i]];
+    std::vector<int32_t> litems(std::max(ng, 1)), lptr(per + 1);
+    std::vector<int64_t> lload(per);
+    assign(local.data(), ng, per, SA_ORDER_LPT, litems.data(), lptr.data(), lload.data());
+    for (int k = 0; k < per; ++k) {
+      const int b = k * groups + g;
+      bin_load[b] = lload[k];
+      for (int p = lptr[k]; p < lptr[k + 1]; ++p) {
+        const int32_t id = ids[litems[p]];
+        bin_of[id] = b;
+        rank_in_bin[id] = bin_count[b]++;
+      }
+    }
+  }
+  std::vector<int32_t> pos(m + 1, 0);
+  for (int b = 0; b < m; ++b) pos[b + 1] = pos[b] + bin_count[b];
+  for (int b = 0; b <= m; ++b) bin_ptr_out[b] = pos[b];
+  for (int i = 0; i < n; ++i) items_out[pos[bin_of[i]] + rank_in_bin[i]] = i;
+  if (bin_load_out)
+    for (int b = 0; b < m; ++b) bin_load_out[b] = bin_load[b];
+}
+
 }  // namespace sa

@@ -136,3 +136,35 @@ def test_fwd_and_merge_argument_errors():
     assert lib.chunk_merge(1, arr, arr, arr, 10, 96, 1, 0, None, None) == bd.SA_ERR_UNSUPPORTED
     assert lib.chunk_merge(1, arr, arr, arr, 0, 64, 1, 0, None, None) == bd.SA_OK  # nothing to do
     lib.sparse_attn_plan_destroy(None)  # no-op
+
+
+def test_host_grouped_assign_bit_exact_random():
+    """Two-level (XCD-affine) LPT: the library's host code equals the oracle's definition."""
+    rng = np.random.default_rng(3)
+    for trial in range(40):
+        heads = int(rng.integers(0, 12))
+        per = int(rng.integers(1, 30))
+        groups = int(rng.choice([1, 2, 4, 8]))
+        m = groups * int(rng.integers(1, 6)) + (int(rng.integers(0, 2)) if trial % 5 == 0 else 0)
+        loads = rng.integers(0, int(rng.integers(1, 50)), size=heads * per)
+        items, ptr, bl = bd.sparse_attn_assign_host_grouped(loads, per, m, groups)
+        bins, ref_bl = P.lpt_grouped(loads.tolist(), per, m, groups)
+        assert np.array_equal(items, [j for b in bins for j in b])
+        assert np.array_equal(ptr, np.cumsum([0] + [len(b) for b in bins]))
+        assert np.array_equal(bl, ref_bl)
+
+
+@pytest.mark.parametrize("cfg,m", [(3, 256), (4, 256)])
+def test_host_grouped_assign_on_workload_rows(cfg, m):
+    w = W.make(cfg, with_data=False)
+    cnt = P.popcount(w.mask, w.n_chunks)
+    items, ptr, bl = bd.sparse_attn_assign_host_grouped(cnt["row"], w.nQ, m, 8)
+    ref = P.plan_items(cnt["row"], m, "lpt_xcd", groups=8)
+    assert np.array_equal(items, ref["items"]) and np.array_equal(ptr, ref["bin_ptr"])
+    assert np.array_equal(bl, ref["bin_load"])
+    # every head's items land in one group of bins (b mod 8)
+    heads = cnt["row"].reshape(-1, w.nQ).shape[0]
+    bin_of = np.empty(heads * w.nQ, np.int64)
+    for b in range(m):
+        bin_of[items[ptr[b]:ptr[b + 1]]] = b
+    assert all(len(set((bin_of[h * w.nQ:(h + 1) * w.nQ] % 8).tolist())) == 1 for h in range(heads))

@@ -35,13 +35,13 @@ def _check_plan(w, plan, order, layout=None):
     assert info["total_live"] == ref["total"]
     lists = [(-1, ref["row"])] + [(c, ref["crow"][:, :, c, :]) for c in range(C)]
     for chunk, loads in lists:
-        want = P.plan_items(loads, m, order)
+        want = P.plan_items(loads, m, order, groups=info["groups"])
         items = bd.sparse_attn_plan_copy(plan, bd.SA_PLAN_ITEMS, B * H * nQ, chunk)
         ptr = bd.sparse_attn_plan_copy(plan, bd.SA_PLAN_BIN_PTR, m + 1, chunk)
         bl = bd.sparse_attn_plan_copy(plan, bd.SA_PLAN_BIN_LOAD, m, chunk)
         assert np.array_equal(items, want["items"]) and np.array_equal(ptr, want["bin_ptr"])
         assert np.array_equal(bl, want["bin_load"])
-    assert info["makespan"] == P.plan_items(ref["row"], m, order)["makespan"]
+    assert info["makespan"] == P.plan_items(ref["row"], m, order, groups=info["groups"])["makespan"]
     return info
 
 
@@ -301,3 +301,19 @@ def test_plan_on_side_stream():
     bd.sparse_attn_fwd(plan, q, k, v, 0, w.n_chunks, o=o)  # current stream
     torch.cuda.synchronize()
     G.assert_close(G.to64(o), _full_oracle(w), G.tol_for(w), "side-stream plan")
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_xcd_order_plan_and_output(cfg):
+    """Two-level (XCD-affine) LPT plan: bit-exact lists against the oracle with the device's XCD
+    count, and the same attention output as the plain LPT order on sampled rows."""
+    w = W.make(cfg)
+    q, k, v = G.upload(w)
+    plan = G.plan_block(w, q, order="lpt_xcd")
+    info = _check_plan(w, plan, "lpt_xcd")
+    assert info["groups"] >= 1
+    o = G.run_full(plan, q, k, v)
+    plan2 = G.plan_block(w, q, order="lpt")
+    o2 = G.run_full(plan2, q, k, v)
+    # the order changes which workgroup runs an item, not the arithmetic of the item
+    assert torch.equal(o, o2)

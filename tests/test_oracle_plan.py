@@ -174,3 +174,20 @@ def test_plan_items_ids_and_ptrs():
     assert out["makespan"] == max(out["bin_load"]) == 6
     # item id = (b*H + h)*nQ + q; LPT order: 4(5), 0(3), 2(2), 1(1), 5(1), 3(0)
     assert out["items"].tolist() == [4, 1, 3, 0, 2, 5]
+
+
+def test_grouped_lpt_hand_example():
+    """Heads of loads 12, 3, 9, 6 (3 items each) on 4 bins in 2 groups, worked by hand:
+    level 1 puts heads 0 and 1 on group 0 (12, then 3 on the 12/15 tie-free lighter group) and
+    heads 2 and 3 on group 1; level 2 runs LPT inside each group; group g's k-th bin is k*2+g."""
+    loads = [5, 4, 3, 1, 1, 1, 9, 0, 0, 2, 2, 2]
+    bins, bl = P.lpt_grouped(loads, 3, 4, 2)
+    assert bins == [[0, 3, 4, 5], [6], [1, 2], [9, 10, 11, 7, 8]]
+    assert bl == [8, 9, 7, 6]
+
+
+def test_grouped_lpt_reduces_to_lpt():
+    rng = np.random.default_rng(7)
+    loads = rng.integers(0, 20, size=24).tolist()
+    assert P.lpt_grouped(loads, 6, 5, 1) == P.lpt(loads, 5)
+    assert P.lpt_grouped(loads, 6, 5, 2) == P.lpt(loads, 5)  # 5 bins do not split into 2 groups
