@@ -81,7 +81,9 @@ typedef struct {
   int32_t layout; /* sa_layout */
   int32_t dtype;  /* sa_dtype */
   float scale;
-  int32_t pad0;
+  int32_t token_causal; /* non-zero: inside live tiles, key j is also dropped for query i when
+                           j > i (token positions; striped chunks use each key's original
+                           position), i.e. causal attention at token granularity */
   int64_t sb, sh, ss;
 } sa_problem;
 

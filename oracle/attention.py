@@ -24,6 +24,11 @@ Definitions followed:
   ``O = alpha*O + beta*O_step``; the result is ``O_acc / l_acc``.  The page is
   silent on rows where both maxima are -inf; there ``alpha = beta = 0`` so the
   state stays ``(0, -inf, 0)``.
+* Token-level causality (option ``token_causal``): the mask above decides which
+  tiles exist; inside them key j is also dropped for query i when ``j > i``
+  (positions in the original sequence, also for striped chunks).  With an
+  all-ones block mask this is plain causal softmax attention.  Rows left with
+  no key behave as rows with no live key above.
 * Chunk composition: contiguous chunk c holds KV blocks
   ``[c*nK/C, (c+1)*nK/C)``; striped chunk c holds tokens ``j`` with
   ``j mod C == c`` (section 2.3's striped attention, "token i -> chunk i mod C").
@@ -64,13 +69,30 @@ def _key_live(mask_row: np.ndarray, block: int, S: int) -> np.ndarray:
     return np.repeat(mask_row != 0, block)[:S]
 
 
+def _softmax_rows(s):
+    """Row max, exp(s - max) and row sum of a score matrix whose rows may be all -inf.
+
+    Such rows get m = -inf, p = 0 and l = 0.
+    """
+    m = s.max(axis=1)
+    m_safe = np.where(np.isneginf(m), 0.0, m)
+    p = np.exp(s - m_safe[:, None])  # exp(-inf) = 0
+    return m, p, p.sum(axis=1)
+
+
+def _drop_future(s, q_pos, k_pos):
+    """Token-level causality: score (i, j) becomes -inf when key position j > query position i."""
+    return np.where(k_pos[None, :] > q_pos[:, None], NEG_INF, s)
+
+
 def masked_attention(q, k, v, mask, block: int, scale: Optional[float] = None,
-                     rows: Optional[Sequence[Tuple[int, int, int]]] = None):
+                     rows: Optional[Sequence[Tuple[int, int, int]]] = None, token_causal: bool = False):
     """Dense softmax attention with dead (Q-block, KV-block) tiles set to -inf.
 
     q, k, v: [B, H, S, D]; mask: [B, H, nQ, nK].  Returns ``(O, lse)`` in fp64,
     shaped [B, H, S, D] / [B, H, S], or [len(rows), D] / [len(rows)] when ``rows``
-    (a list of (b, h, token)) selects individual output rows.
+    (a list of (b, h, token)) selects individual output rows.  ``token_causal``
+    also drops keys after each query inside live tiles.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, S, D = q.shape
@@ -80,6 +102,8 @@ def masked_attention(q, k, v, mask, block: int, scale: Optional[float] = None,
         lse = np.full(len(rows), NEG_INF)
         for n, (b, h, i) in enumerate(rows):
             live = _key_live(mask[b, h, i // block], block, S)
+            if token_causal:
+                live = live & (np.arange(S) <= i)
             if not live.any():
                 continue
             s = sc * (k[b, h][live] @ q[b, h, i])
@@ -99,16 +123,17 @@ def masked_attention(q, k, v, mask, block: int, scale: Optional[float] = None,
                 if not live.any():
                     continue
                 s = sc * (q[b, h, r0:r1] @ k[b, h][live].T)
-                m = s.max(axis=1, keepdims=True)
-                p = np.exp(s - m)
-                l = p.sum(axis=1, keepdims=True)
-                out[b, h, r0:r1] = (p @ v[b, h][live]) / l
-                lse[b, h, r0:r1] = (m + np.log(l))[:, 0]
+                if token_causal:
+                    s = _drop_future(s, np.arange(r0, r1), np.nonzero(live)[0])
+                m, p, l = _softmax_rows(s)
+                has = l > 0
+                out[b, h, r0:r1][has] = (p[has] @ v[b, h][live]) / l[has, None]
+                lse[b, h, r0:r1][has] = m[has] + np.log(l[has])
     return out, lse
 
 
 def chunk_partial(q, k, v, mask, block: int, n_chunks: int, layout: str, c: int,
-                  scale: Optional[float] = None):
+                  scale: Optional[float] = None, token_causal: bool = False):
     """One ring step's partial ``(O_unnormalised, m, l)`` over the KV tokens of chunk ``c``.
 
     Shapes: O [B, H, S, D], m and l [B, H, S], fp64.
@@ -130,11 +155,12 @@ def chunk_partial(q, k, v, mask, block: int, n_chunks: int, layout: str, c: int,
                     continue
                 kt = toks[live]
                 s = sc * (q[b, h, r0:r1] @ k[b, h, kt].T)
-                m = s.max(axis=1, keepdims=True)
-                p = np.exp(s - m)
+                if token_causal:
+                    s = _drop_future(s, np.arange(r0, r1), kt)
+                m, p, l = _softmax_rows(s)
                 O[b, h, r0:r1] = p @ v[b, h, kt]
-                M[b, h, r0:r1] = m[:, 0]
-                L[b, h, r0:r1] = p.sum(axis=1)
+                M[b, h, r0:r1] = m
+                L[b, h, r0:r1] = l
     return O, M, L
 
 
@@ -166,8 +192,8 @@ def merge(parts: List[Tuple[np.ndarray, np.ndarray, np.ndarray]]):
 
 
 def chunked_attention(q, k, v, mask, block: int, n_chunks: int, layout: str,
-                      scale: Optional[float] = None):
+                      scale: Optional[float] = None, token_causal: bool = False):
     """The ring emulation on one device: every chunk's partial, then the merge."""
-    parts = [chunk_partial(q, k, v, mask, block, n_chunks, layout, c, scale)
+    parts = [chunk_partial(q, k, v, mask, block, n_chunks, layout, c, scale, token_causal)
              for c in range(n_chunks)]
     return merge(parts)

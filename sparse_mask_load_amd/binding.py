@@ -38,7 +38,7 @@ class SparseAttnError(RuntimeError):
 class sa_problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("S", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("n_chunks", ctypes.c_int32), ("layout", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("pad0", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("token_causal", ctypes.c_int32),
                 ("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("ss", ctypes.c_int64)]
 
 
@@ -118,14 +118,14 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_problem(q, block: int = 0, n_chunks: int = 1, layout: str = "contiguous",
-                 scale: float = 0.0) -> sa_problem:
+                 scale: float = 0.0, token_causal: bool = False) -> sa_problem:
     """Describe a [B, H, S, D] tensor (last dim contiguous) as an sa_problem."""
     import torch
     if q.dim() != 4 or q.stride(-1) != 1:
         raise ValueError("q must be [B, H, S, D] with a contiguous last dimension")
     dtype = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}[q.dtype]
     B, H, S, D = q.shape
-    return sa_problem(B, H, S, D, block, n_chunks, _LAYOUTS[layout], dtype, float(scale), 0,
+    return sa_problem(B, H, S, D, block, n_chunks, _LAYOUTS[layout], dtype, float(scale), 1 if token_causal else 0,
                       q.stride(0), q.stride(1), q.stride(2))
 
 

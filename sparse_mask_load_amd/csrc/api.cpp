@@ -87,7 +87,12 @@ sa_status validate_problem(const sa_problem* p, bool block_kind) {
                 (long long)p->sb, (long long)p->sh, (long long)p->ss);
   if ((p->ss % 8) || (p->sh % 8) || (p->sb % 8))
     return fail(SA_ERR_UNSUPPORTED, "strides must be multiples of 8 elements (16-byte rows)");
-  if (!block_kind) return SA_OK;
+  if (!block_kind) {
+    if (p->token_causal)
+      return fail(SA_ERR_INVALID, "token_causal applies to block plans (top-k and index plans take causality "
+                                  "from their key selection)");
+    return SA_OK;
+  }
   if (p->dtype == SA_BF16 && p->block != 64 && p->block != 128)
     return fail(SA_ERR_UNSUPPORTED, "bf16 block %d (supported: 64, 128)", p->block);
   if (p->dtype == SA_F32 && p->block != 64)
@@ -370,6 +375,7 @@ sa_status sparse_attn_fwd(const sa_plan* P, const void* q, const void* k, const 
   a.trace = trace;
   a.B = pr.B; a.H = pr.H; a.S = pr.S; a.nQ = P->nQ; a.nK = P->nK; a.n_chunks = pr.n_chunks;
   a.layout = pr.layout; a.c0 = chunk_begin; a.c1 = chunk_end; a.num_bins = P->num_bins;
+  a.token_causal = pr.token_causal ? 1 : 0;
   a.sb = pr.sb; a.sh = pr.sh; a.ss = pr.ss;
   a.scale = effective_scale(pr);
   a.scale_log2 = a.scale * 1.4426950408889634f;

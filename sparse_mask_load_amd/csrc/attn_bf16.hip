@@ -269,20 +269,23 @@ __device__ __forceinline__ void tile_scores(const bf16* __restrict__ Kt, const b
   }
 }
 
-// Row max of the wave's tile scores (after masking keys beyond S on a ragged
-// tile) and the lazy move of the exponent's reference max.  key0 is the first
-// key of the wave's first block.  Returns the reference to use.
+// Row max of the wave's tile scores and the lazy move of the exponent's
+// reference max.  When `masked`, score (j, r) is first dropped if its key
+// offset j*32 + 16*(r>>3) + (r&7) within the lane's keys exceeds off_max (keys
+// beyond S on a ragged tile, keys after the query on a diagonal tile).
+// Returns the reference to use: 0 for a row that has no finite score yet, so
+// that its dropped scores give probabilities 0 rather than exp(-inf + inf).
 template <int D, int BLK, bool GENERAL>
-__device__ __forceinline__ float tile_max(f32x16 (&s)[BLK / 64], RowState<D / 32>& st, int live_w, bool ragged,
-                                          int key0, int S, int h2, float sl2) {
+__device__ __forceinline__ float tile_max(f32x16 (&s)[BLK / 64], RowState<D / 32>& st, int live_w, bool masked,
+                                          int off_max, float sl2) {
   using SH = Shape<D, BLK>;
   auto live = [&](int j) { return !GENERAL || ((live_w >> j) & 1); };
-  if (GENERAL && ragged) {
+  if (GENERAL && masked) {
 #pragma unroll
     for (int j = 0; j < SH::NKBW; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (key0 + j * 32 + 16 * (r >> 3) + 8 * h2 + (r & 7) >= S) s[j][r] = kNegInf;
+        if (j * 32 + 16 * (r >> 3) + (r & 7) > off_max) s[j][r] = kNegInf;
   }
   float mx = kNegInf;
 #pragma unroll
@@ -295,13 +298,15 @@ __device__ __forceinline__ float tile_max(f32x16 (&s)[BLK / 64], RowState<D / 32
   st.m_true = fmaxf(st.m_true, mx);
   if (__builtin_amdgcn_ballot_w64(mx > st.m_ref + kRescaleSlack)) {
     const float m_new = (mx > st.m_ref + kRescaleSlack) ? st.m_true : st.m_ref;
-    const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);
+    // a lane with no finite score yet (possible only under token-level causality) keeps
+    // its zero state: alpha = 1 instead of exp2(-inf - -inf)
+    const float alpha = (GENERAL && m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
     st.m_ref = m_new;
     st.l *= alpha;
 #pragma unroll
     for (int d = 0; d < SH::ND; ++d) st.acc[d] *= alpha;
   }
-  return st.m_ref;
+  return (GENERAL && st.m_ref == kNegInf) ? 0.f : st.m_ref;
 }
 
 // P of one key block as two bf16x8 B operands (keys 16*half + 8*h2 + 0..7),
@@ -375,8 +380,9 @@ __device__ __forceinline__ void merge_halves(RowState<D / 32>& st, float& m, flo
   }
 }
 
-// GENERAL: the problem has striped chunks or a partial last block, so a tile
-// may have dead 32-key groups or keys beyond S; otherwise every tile is full.
+// GENERAL: the problem has striped chunks, a partial last block or token-level
+// causality, so a tile may have dead 32-key groups, keys beyond S or keys after
+// some of its queries; otherwise every tile is full.
 template <int D, int BLK, bool GENERAL>
 __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(FwdArgs a) {
@@ -505,8 +511,19 @@ void attn_bf16_kernel(FwdArgs a) {
       // the S MFMAs and the exponentials share one basic block
       const int desc1 = has_next ? __builtin_amdgcn_readfirstlane(sList[t + 1]) : desc;
       const int live_w = live_of(desc);
+      // Token positions of the wave's keys: kpos0 + kstep * offset (a striped
+      // chunk's compacted position p is token chunk + n_chunks * p).
       const int key0 = (desc & 0xFFFFF) * BLK + kb0 * 32;
-      const bool ragged = !striped && (desc & 0xFFFFF) * BLK + BLK > a.S;
+      const int kstep = striped ? a.n_chunks : 1;
+      const int kpos0 = striped ? ((desc >> kDescChunkShift) & 63) + a.n_chunks * key0 : key0;
+      const bool ragged = !striped && key0 - kb0 * 32 + BLK > a.S;
+      // diagonal: the wave's last key lies after its first query
+      const bool diag = GENERAL && a.token_causal && kpos0 + kstep * (NB * 32 - 1) > qb * BLK + rg * 32;
+      int off_max = 0;
+      if (GENERAL && (ragged || diag)) {
+        const int rel = (diag ? min(qrow, a.S - 1) : a.S - 1) - kpos0 - kstep * 8 * h2;
+        off_max = rel < 0 ? -1 : rel / kstep;
+      }
 
       // K of tile t+1 and V of tile t have landed; K of tile t and V of tile t-1 are free.
       wait_vm();
@@ -527,7 +544,7 @@ void attn_bf16_kernel(FwdArgs a) {
       // tile t+1 and the P V MFMAs of block j of tile t all issue in one basic
       // block; block j of the scores is overwritten by tile t+1 once its
       // probabilities are formed.
-      const float m_ref = tile_max<D, BLK, GENERAL>(s, st, live_w, ragged, key0, a.S, h2, sl2);
+      const float m_ref = tile_max<D, BLK, GENERAL>(s, st, live_w, ragged || diag, off_max, sl2);
       const int live_next = live_of(desc1);
       float lsum0 = 0.f, lsum1 = 0.f;
       constexpr int LPB = SH::IPW / NB;  // load instructions per tensor per key block
@@ -598,7 +615,7 @@ void attn_bf16_kernel(FwdArgs a) {
 
 template <int D, int BLK>
 hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
-  const bool general = a.layout == SA_LAYOUT_STRIPED || a.S % BLK != 0;
+  const bool general = a.layout == SA_LAYOUT_STRIPED || a.S % BLK != 0 || a.token_causal;
   if (general)
     hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, true>), dim3(a.num_bins), dim3(Shape<D, BLK>::NW * 64), 0, stream, a);
   else

@@ -105,10 +105,15 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(FwdArgs a) {
       for (int jj = 0; jj < 16; ++jj) {
         const int j = quarter * 16 + jj;
         bool live;
-        if (!striped)
-          live = tidx * BLK + j < a.S;
-        else
+        int kpos;  // token position of key j
+        if (!striped) {
+          kpos = tidx * BLK + j;
+          live = kpos < a.S;
+        } else {
+          kpos = tchunk + a.n_chunks * (tidx * BLK + j);
           live = (code >> (j / (BLK / a.n_chunks))) & 1;
+        }
+        if (a.token_causal && kpos > qrow) live = false;
         float acc = 0.f;
         for (int d = 0; d < D; ++d) acc = fmaf(sQ[row][d], sK[j][d], acc);
         s[jj] = live ? acc * a.scale : kNegInf;
@@ -117,10 +122,12 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(FwdArgs a) {
       mx = fmaxf(mx, __shfl_xor(mx, 1));
       mx = fmaxf(mx, __shfl_xor(mx, 2));
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = expf(m_run - m_new);
+      // a row with no finite score yet (token-causal) keeps p = 0 and alpha = 0
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = expf(m_run - m_use);
       float lsum = 0.f;
       for (int jj = 0; jj < 16; ++jj) {
-        const float p = expf(s[jj] - m_new);
+        const float p = expf(s[jj] - m_use);
         lsum += p;
         sP[row][quarter * 16 + jj] = p;
       }

@@ -37,6 +37,7 @@ struct FwdArgs {
   int64_t* trace;         // nullable
   int32_t B, H, S, nQ, nK, n_chunks, layout, c0, c1;
   int32_t num_bins;
+  int32_t token_causal;  // also drop keys after the query inside live tiles
   int64_t sb, sh, ss;
   float scale;        // natural-log softmax scale
   float scale_log2;   // scale * log2(e)

@@ -157,3 +157,82 @@ def test_chunk_token_sets_partition_the_sequence():
         assert sorted(toks.tolist()) == list(range(1024))
     assert A.chunk_token_ids(1024, 128, 4, "striped", 1)[:3].tolist() == [1, 5, 9]
     assert A.chunk_token_ids(1024, 128, 4, "contiguous", 1)[[0, -1]].tolist() == [256, 511]
+
+
+# ---- token-level causality inside live tiles ----
+
+@pytest.mark.parametrize("pattern,S,block", [("ones", 192, 64), ("causal", 200, 64), ("causal", 256, 32)])
+def test_token_causal_is_sdpa_causal(pattern, S, block):
+    # an all-ones or block-lower-triangular mask contains every (i, j <= i) pair, so the
+    # token-causal result is plain causal attention
+    w = W.make_custom(1, 2, S, 32, block=block, pattern=pattern, dtype="f32", seed=21)
+    O, lse = A.masked_attention(w.q, w.k, w.v, w.mask, block, token_causal=True)
+    ref = _sdpa(w.q, w.k, w.v, is_causal=True)
+    assert np.abs(O - ref).max() < 1e-12
+    # the first query sees key 0 only: O = v_0 and lse = its single score
+    assert np.abs(O[0, :, 0] - w.v[0, :, 0]).max() < 1e-12
+    s00 = np.einsum("hd,hd->h", w.q[0, :, 0].astype(np.float64), w.k[0, :, 0].astype(np.float64)) / math.sqrt(32)
+    assert np.abs(lse[0, :, 0] - s00).max() < 1e-12
+
+
+def test_token_causal_bernoulli_equals_sdpa_with_combined_mask():
+    S, block = 256, 32
+    w = W.make_custom(2, 2, S, 16, block=block, pattern="bernoulli", density=0.4, dtype="f32", seed=22)
+    w.mask[0, 0, 0] = 0
+    w.mask[0, 0, 0, 3] = 1  # the first Q-block sees only a later KV block
+    O, lse = A.masked_attention(w.q, w.k, w.v, w.mask, block, token_causal=True)
+    tril = np.tril(np.ones((S, S), dtype=bool))
+    n_empty = 0
+    for b in range(2):
+        for h in range(2):
+            tm = _token_mask(w.mask[b, h], block, S) & tril
+            has = tm.any(axis=1)
+            n_empty += int((~has).sum())
+            ref = _sdpa(w.q[b, h], w.k[b, h], w.v[b, h], token_mask=tm)
+            assert np.abs(O[b, h][has] - ref[has]).max() < 1e-12
+            # rows whose live tiles hold only later keys have no key at all
+            assert (O[b, h][~has] == 0).all() and np.isneginf(lse[b, h][~has]).all()
+    assert n_empty > 0  # the case is exercised
+
+
+def test_token_causal_pure_python_loops_tiny():
+    w = W.make_custom(1, 1, 20, 4, block=8, pattern="bernoulli", density=0.6, dtype="f32", seed=23)
+    O, lse = A.masked_attention(w.q, w.k, w.v, w.mask, w.block, token_causal=True)
+    for i in range(20):
+        live = [j for j in range(i + 1) if w.mask[0, 0, i // 8, j // 8]]
+        if not live:
+            assert (O[0, 0, i] == 0).all() and lse[0, 0, i] == -np.inf
+            continue
+        s = [0.5 * sum(float(w.q[0, 0, i, d]) * float(w.k[0, 0, j, d]) for d in range(4)) for j in live]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        for d in range(4):
+            ref = sum(e[n] * float(w.v[0, 0, j, d]) for n, j in enumerate(live)) / sum(e)
+            assert abs(O[0, 0, i, d] - ref) < 1e-12
+
+
+@pytest.mark.parametrize("C,layout", [(4, "contiguous"), (2, "striped"), (4, "striped")])
+def test_token_causal_chunked_merge_equals_unchunked(C, layout):
+    S = 512
+    w = W.make_custom(1, 2, S, 32, block=64, pattern="bernoulli", density=0.5, dtype="f32",
+                      seed=24 + C, layout=layout)
+    ref, ref_lse = A.masked_attention(w.q, w.k, w.v, w.mask, 64, token_causal=True)
+    parts = [A.chunk_partial(w.q, w.k, w.v, w.mask, 64, C, layout, c, token_causal=True) for c in range(C)]
+    O, lse = A.merge(parts)
+    assert np.abs(O - ref).max() < 1e-12
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lse)) and np.abs(lse[fin] - ref_lse[fin]).max() < 1e-12
+    if layout == "striped":
+        # query 0 has no key in chunks 1.. (their first token is c > 0)
+        for c in range(1, C):
+            assert np.isneginf(parts[c][1][0, :, 0]).all() and (parts[c][2][0, :, 0] == 0).all()
+
+
+def test_token_causal_row_sampling_matches_full():
+    w = W.make_custom(1, 2, 320, 32, block=64, pattern="bernoulli", density=0.5, dtype="f32", seed=25)
+    O, lse = A.masked_attention(w.q, w.k, w.v, w.mask, 64, token_causal=True)
+    rows = [(0, 0, 0), (0, 1, 319), (0, 1, 130), (0, 0, 64), (0, 0, 63)]
+    Os, ls = A.masked_attention(w.q, w.k, w.v, w.mask, 64, rows=rows, token_causal=True)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.abs(Os[n] - O[b, h, i]).max() < 1e-13
+        assert (np.isneginf(ls[n]) and np.isneginf(lse[b, h, i])) or abs(ls[n] - lse[b, h, i]) < 1e-12
