@@ -307,6 +307,16 @@ def main() -> int:
             torch.cuda.synchronize()
             alt_ms[alt] = (e0.elapsed_time(e1) / reps, bd.sparse_attn_plan_info(p_alt))
             p_alt.close()
+        # the same mask with token-level causality inside the live tiles
+        p_tc = bd.sparse_attn_plan(bd.make_problem(q, w.block, C, w.layout, token_causal=True), "block",
+                                   mask=mask, order=args.order)
+        e0.record(stream)
+        for _ in range(reps):
+            bd.sparse_attn_fwd(p_tc, q, k, v, 0, C, o=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tc_ms = e0.elapsed_time(e1) / reps
+        p_tc.close()
 
         result["breakdown"] = {
             "plan_ms": round(plan_ms, 4), "fwd_partial_ms": round(kernel_ms, 4),
@@ -316,6 +326,7 @@ def main() -> int:
             "fwd_fused_ms_by_order": {o: round(t, 4) for o, (t, _) in alt_ms.items()},
             "makespan_tiles_by_order": {o: i["makespan"] for o, (_, i) in alt_ms.items()},
             "xcd_groups": alt_ms["lpt_xcd"][1]["groups"],
+            "fwd_fused_token_causal_ms": round(tc_ms, 4),
         }
     plan.close()
 

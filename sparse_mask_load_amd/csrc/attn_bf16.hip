@@ -275,12 +275,12 @@ __device__ __forceinline__ void tile_scores(const bf16* __restrict__ Kt, const b
 // beyond S on a ragged tile, keys after the query on a diagonal tile).
 // Returns the reference to use: 0 for a row that has no finite score yet, so
 // that its dropped scores give probabilities 0 rather than exp(-inf + inf).
-template <int D, int BLK, bool GENERAL>
+template <int D, int BLK, bool GENERAL, bool MASKED>
 __device__ __forceinline__ float tile_max(f32x16 (&s)[BLK / 64], RowState<D / 32>& st, int live_w, bool masked,
                                           int off_max, float sl2) {
   using SH = Shape<D, BLK>;
   auto live = [&](int j) { return !GENERAL || ((live_w >> j) & 1); };
-  if (GENERAL && masked) {
+  if (MASKED && masked) {
 #pragma unroll
     for (int j = 0; j < SH::NKBW; ++j)
 #pragma unroll
@@ -300,13 +300,13 @@ __device__ __forceinline__ float tile_max(f32x16 (&s)[BLK / 64], RowState<D / 32
     const float m_new = (mx > st.m_ref + kRescaleSlack) ? st.m_true : st.m_ref;
     // a lane with no finite score yet (possible only under token-level causality) keeps
     // its zero state: alpha = 1 instead of exp2(-inf - -inf)
-    const float alpha = (GENERAL && m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
+    const float alpha = (MASKED && m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
     st.m_ref = m_new;
     st.l *= alpha;
 #pragma unroll
     for (int d = 0; d < SH::ND; ++d) st.acc[d] *= alpha;
   }
-  return (GENERAL && st.m_ref == kNegInf) ? 0.f : st.m_ref;
+  return (MASKED && st.m_ref == kNegInf) ? 0.f : st.m_ref;
 }
 
 // P of one key block as two bf16x8 B operands (keys 16*half + 8*h2 + 0..7),
@@ -380,13 +380,15 @@ __device__ __forceinline__ void merge_halves(RowState<D / 32>& st, float& m, flo
   }
 }
 
-// GENERAL: the problem has striped chunks, a partial last block or token-level
-// causality, so a tile may have dead 32-key groups, keys beyond S or keys after
-// some of its queries; otherwise every tile is full.
-template <int D, int BLK, bool GENERAL>
+// GENERAL: the problem has striped chunks or a partial last block, so a tile
+// may have dead 32-key groups or keys beyond S; otherwise every tile is full.
+// Token-level causality (keys after some of a tile's queries) is handled by the
+// GENERAL variant, or by TCAUSAL on top of the full-tile one.
+template <int D, int BLK, bool GENERAL, bool TCAUSAL>
 __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(FwdArgs a) {
   using SH = Shape<D, BLK>;
+  constexpr bool MASKED = GENERAL || TCAUSAL;  // scores may be dropped per element
   static_assert(SH::NW * 64 == BLK * 4, "launch bounds");
   constexpr int NKB = SH::NKB, NB = SH::NKBW, ND = SH::ND, NKS = SH::NKS, NRG = SH::NRG;
   static_assert(SH::TILE * 2 >= NRG * SH::RB * 4096, "merge round must fit in a K buffer");
@@ -518,9 +520,9 @@ void attn_bf16_kernel(FwdArgs a) {
       const int kpos0 = striped ? ((desc >> kDescChunkShift) & 63) + a.n_chunks * key0 : key0;
       const bool ragged = !striped && key0 - kb0 * 32 + BLK > a.S;
       // diagonal: the wave's last key lies after its first query
-      const bool diag = GENERAL && a.token_causal && kpos0 + kstep * (NB * 32 - 1) > qb * BLK + rg * 32;
+      const bool diag = MASKED && a.token_causal && kpos0 + kstep * (NB * 32 - 1) > qb * BLK + rg * 32;
       int off_max = 0;
-      if (GENERAL && (ragged || diag)) {
+      if (MASKED && (ragged || diag)) {
         const int rel = (diag ? min(qrow, a.S - 1) : a.S - 1) - kpos0 - kstep * 8 * h2;
         off_max = rel < 0 ? -1 : rel / kstep;
       }
@@ -544,7 +546,7 @@ void attn_bf16_kernel(FwdArgs a) {
       // tile t+1 and the P V MFMAs of block j of tile t all issue in one basic
       // block; block j of the scores is overwritten by tile t+1 once its
       // probabilities are formed.
-      const float m_ref = tile_max<D, BLK, GENERAL>(s, st, live_w, ragged || diag, off_max, sl2);
+      const float m_ref = tile_max<D, BLK, GENERAL, MASKED>(s, st, live_w, ragged || diag, off_max, sl2);
       const int live_next = live_of(desc1);
       float lsum0 = 0.f, lsum1 = 0.f;
       constexpr int LPB = SH::IPW / NB;  // load instructions per tensor per key block
@@ -615,12 +617,14 @@ void attn_bf16_kernel(FwdArgs a) {
 
 template <int D, int BLK>
 hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
-  const bool general = a.layout == SA_LAYOUT_STRIPED || a.S % BLK != 0 || a.token_causal;
+  const bool general = a.layout == SA_LAYOUT_STRIPED || a.S % BLK != 0;
+  const dim3 grid(a.num_bins), block(Shape<D, BLK>::NW * 64);
   if (general)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, true>), dim3(a.num_bins), dim3(Shape<D, BLK>::NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, true, false>), grid, block, 0, stream, a);
+  else if (a.token_causal)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false>), dim3(a.num_bins), dim3(Shape<D, BLK>::NW * 64), 0, stream,
-                       a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
