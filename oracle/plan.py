@@ -102,6 +102,29 @@ def lpt_grouped(loads: Sequence[int], items_per_head: int, m: int, groups: int
     return bins, bin_load
 
 
+def lpt_rounds(loads: Sequence[int], m: int) -> Tuple[List[List[int]], List[int]]:
+    """Round-based LPT: the jobs in LPT order are handed out m at a time.
+
+    A parallel form of the LPT paragraph's greedy (one sort per round instead of
+    one least-loaded search per job).  Jobs are taken in the LPT order (load
+    descending, id ascending).  In each round the next m jobs go to the machines
+    ordered by their load at the start of the round (ascending, lower index
+    first on equal loads): the round's j-th job to the j-th machine, so the
+    round's longest job meets the least-loaded machine.  Every machine gets one
+    job per round, except in a last, partial round.  With at most m jobs, or a
+    single round, this is exactly LPT.
+    """
+    order = sorted(range(len(loads)), key=lambda i: (-int(loads[i]), i))
+    bins: List[List[int]] = [[] for _ in range(m)]
+    bin_load = [0] * m
+    for r0 in range(0, len(order), m):
+        machines = sorted(range(m), key=lambda b: (bin_load[b], b))
+        for job, b in zip(order[r0:r0 + m], machines):
+            bins[b].append(job)
+            bin_load[b] += int(loads[job])
+    return bins, bin_load
+
+
 def naive(loads: Sequence[int], m: int) -> Tuple[List[List[int]], List[int]]:
     """Round-robin in job-id order: job i runs on machine i mod m."""
     bins: List[List[int]] = [[] for _ in range(m)]
@@ -128,8 +151,9 @@ def brute_force_makespan(loads: Sequence[int], m: int) -> Tuple[int, Tuple[int, 
 def plan_items(row_loads: np.ndarray, m: int, order: str = "lpt", groups: int = 1) -> Dict[str, np.ndarray]:
     """Assign every (b, h, q) item (id = (b*H + h)*nQ + q, load = row count) to m bins.
 
-    ``order``: "lpt", "naive" or "lpt_xcd" (``lpt_grouped`` with the heads of
-    ``row_loads`` [B, H, nQ] and ``groups`` bin groups).  Returns ``items`` (all
+    ``order``: "lpt", "naive", "lpt_device" (``lpt_rounds``) or "lpt_xcd"
+    (``lpt_grouped`` with the heads of ``row_loads`` [B, H, nQ] and ``groups``
+    bin groups).  Returns ``items`` (all
     bins' lists concatenated), ``bin_ptr`` (m + 1 offsets), ``bin_load`` and
     ``makespan``.
     """
@@ -138,7 +162,7 @@ def plan_items(row_loads: np.ndarray, m: int, order: str = "lpt", groups: int = 
     if order == "lpt_xcd":
         bins, bin_load = lpt_grouped(loads, row_loads.shape[-1], m, groups)
     else:
-        bins, bin_load = (lpt if order == "lpt" else naive)(loads, m)
+        bins, bin_load = {"lpt": lpt, "naive": naive, "lpt_device": lpt_rounds}[order](loads, m)
     items, ptr = [], [0]
     for b in bins:
         items.extend(b)

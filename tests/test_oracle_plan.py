@@ -191,3 +191,61 @@ def test_grouped_lpt_reduces_to_lpt():
     loads = rng.integers(0, 20, size=24).tolist()
     assert P.lpt_grouped(loads, 6, 5, 1) == P.lpt(loads, 5)
     assert P.lpt_grouped(loads, 6, 5, 2) == P.lpt(loads, 5)  # 5 bins do not split into 2 groups
+
+
+# ---- round-based LPT (the device planner's rule) ----
+
+def test_rounds_lpt_page_example_and_hand_cases():
+    # db-SP's [8,7,6,5,4] on two machines: round 0 gives 8, 7 to machines 0, 1; round 1 meets
+    # loads (8, 7), so 6 goes to machine 1 and 5 to machine 0; round 2 meets a 13/13 tie
+    bins, bl = P.lpt_rounds([8, 7, 6, 5, 4], 2)
+    assert bins == [[0, 3, 4], [1, 2]] and bl == [17, 13]
+    # one job per machine and round: the long job's machine still gets a job in round 1,
+    # where plain LPT would have given every short job to machine 1
+    bins, bl = P.lpt_rounds([10, 1, 1, 1, 1], 2)
+    assert bins == [[0, 3], [1, 2, 4]] and bl == [11, 3]
+    assert P.lpt([10, 1, 1, 1, 1], 2)[1] == [10, 4]
+    # equal loads: ids ascending within the round, ties between machines to the lower index
+    assert P.lpt_rounds([1, 1, 1], 2) == ([[0, 2], [1]], [2, 1])
+    # machines ordered ascending by load at the start of a round, not by index
+    assert P.lpt_rounds([5, 3, 2, 2], 2) == ([[0, 3], [1, 2]], [7, 5])
+
+
+def test_rounds_lpt_equals_lpt_in_a_single_round_and_on_equal_loads():
+    rng = random.Random(3)
+    for _ in range(200):
+        m = rng.randint(1, 9)
+        loads = [rng.randint(0, 50) for _ in range(rng.randint(0, m))]
+        assert P.lpt_rounds(loads, m) == P.lpt(loads, m)
+        eq = [7] * rng.randint(0, 30)
+        assert P.lpt_rounds(eq, m) == P.lpt(eq, m) == P.naive(eq, m)
+
+
+def test_rounds_lpt_invariants():
+    """Every job once; machine job counts differ by at most one; the spread of machine loads
+    never exceeds the longest job (for machines i, j with a_i <= a_j, a round gives i a job
+    at least as long as j's, so the new gap is at most max(old gap, the round's longest
+    job)); hence makespan <= mean + longest job."""
+    rng = random.Random(4)
+    for _ in range(300):
+        m = rng.randint(1, 12)
+        loads = [rng.randint(0, rng.choice([3, 40, 1000])) for _ in range(rng.randint(0, 60))]
+        bins, bl = P.lpt_rounds(loads, m)
+        assert sorted(j for b in bins for j in b) == list(range(len(loads)))
+        counts = [len(b) for b in bins]
+        assert max(counts) - min(counts) <= 1
+        assert bl == [sum(loads[j] for j in b) for b in bins]
+        pmax = max(loads, default=0)
+        assert max(bl) - min(bl) <= pmax
+        assert max(bl) * m <= sum(loads) + m * pmax
+        # within a machine, jobs come in LPT order (one per round)
+        for b in bins:
+            assert all((-loads[x], x) < (-loads[y], y) for x, y in zip(b, b[1:]))
+
+
+def test_rounds_lpt_plan_items_and_workload_makespans():
+    w = W.make(3)
+    row = P.popcount(w.mask, 4)["row"]
+    r = P.plan_items(row, 256, "lpt_device")
+    assert r["makespan"] == P.plan_items(row, 256, "lpt")["makespan"] == 516
+    assert np.array_equal(np.sort(r["items"]), np.arange(row.size))
