@@ -165,8 +165,9 @@ def main() -> int:
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="causal")
     ap.add_argument("--mode", choices=["merged", "fused"], default="merged",
                     help="merged: partial chunks + chunk_merge (default); fused: chunks folded in-kernel")
-    ap.add_argument("--order", choices=["lpt_xcd", "lpt", "naive"], default="lpt_xcd",
-                    help="work order: two-level LPT (heads to XCDs, then Q-blocks), one-level LPT, round-robin")
+    ap.add_argument("--order", choices=["lpt_xcd", "lpt", "naive", "lpt_device"], default="lpt_xcd",
+                    help="work order: two-level LPT (heads to XCDs, then Q-blocks), one-level LPT, round-robin, "
+                         "round-based LPT made on the GPU")
     ap.add_argument("--bins", type=int, default=0, help="persistent workgroups (0: one per resident slot)")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -256,7 +257,7 @@ def main() -> int:
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name} block-sparse MHA B{B} H{H} S{S} d{D} block {w.block}, "
                                f"{C} {w.layout} KV chunks {'merged by chunk_merge' if args.mode == 'merged' else 'folded in-kernel'}, "
-                               f"{ {'lpt_xcd': 'two-level LPT (heads to XCDs, then Q-blocks)', 'lpt': 'LPT', 'naive': 'round-robin'}[args.order]} over {info['num_bins']} bins",
+                               f"{ {'lpt_xcd': 'two-level LPT (heads to XCDs, then Q-blocks)', 'lpt': 'LPT', 'naive': 'round-robin', 'lpt_device': 'round-based LPT made on the GPU'}[args.order]} over {info['num_bins']} bins",
                    "B": B, "H": H, "S": S, "D": D, "block": w.block, "n_chunks": C, "layout": w.layout,
                    "mask": {"tiny": "Bernoulli(0.5)+diag", "video": "frame band / Bernoulli",
                             "causal": "block lower-triangular", "skewed": "Zipf(1.2) rows"}[args.workload],
@@ -297,8 +298,37 @@ def main() -> int:
         for _ in range(reps):
             bd.sparse_attn_plan(prob, "block", mask=mask, order=args.order).close()
         plan_ms = (time.perf_counter() - t_plan) * 1e3 / reps
+        # device planner: host cost of the call (it returns without waiting) and its GPU time
+        t_plan = time.perf_counter()
+        dplans = [bd.sparse_attn_plan(prob, "block", mask=mask, order="lpt_device") for _ in range(reps)]
+        plan_device_call_ms = (time.perf_counter() - t_plan) * 1e3 / reps
+        torch.cuda.synchronize()
+        for p_d in dplans:
+            p_d.close()
+        gpu_ms = []
+        for _ in range(reps):  # device-side latency: mask copy, popcount and the planning kernel
+            e0.record(stream)
+            p_d = bd.sparse_attn_plan(prob, "block", mask=mask, order="lpt_device", stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gpu_ms.append(e0.elapsed_time(e1))
+            p_d.close()
+        plan_device_gpu_ms = float(np.median(gpu_ms))
+        # whole steps with device plans (same loop as the timed one)
+        order_main = args.order
+        args.order = "lpt_device"
+        for _ in range(2):
+            step(False).close()
+        torch.cuda.synchronize()
+        t_dev = time.perf_counter()
+        dplans = [step(False) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        step_device_plan_ms = (time.perf_counter() - t_dev) * 1e3 / args.steps
+        for p_d in dplans:
+            p_d.close()
+        args.order = order_main
         alt_ms = {}
-        for alt in ("naive", "lpt", "lpt_xcd"):
+        for alt in ("naive", "lpt", "lpt_xcd", "lpt_device"):
             p_alt = bd.sparse_attn_plan(prob, "block", mask=mask, order=alt)
             e0.record(stream)
             for _ in range(reps):
@@ -327,6 +357,8 @@ def main() -> int:
             "makespan_tiles_by_order": {o: i["makespan"] for o, (_, i) in alt_ms.items()},
             "xcd_groups": alt_ms["lpt_xcd"][1]["groups"],
             "fwd_fused_token_causal_ms": round(tc_ms, 4),
+            "plan_device_call_ms": round(plan_device_call_ms, 4), "plan_device_gpu_ms": round(plan_device_gpu_ms, 4),
+            "ms_per_step_device_plan": round(step_device_plan_ms, 4),
         }
     plan.close()
 

@@ -57,8 +57,17 @@ typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  *                    re-read for one chip): heads to the chip's XCDs by LPT on
  *                    head loads, then each XCD's items by LPT onto its bins (bin b
  *                    runs on XCD b mod #XCDs).  Plain LPT when num_bins is not a
- *                    multiple of the XCD count. */
-typedef enum { SA_ORDER_LPT = 0, SA_ORDER_NAIVE = 1, SA_ORDER_LPT_XCD = 2 } sa_order;
+ *                    multiple of the XCD count.
+ *  SA_ORDER_LPT_DEVICE: round-based LPT made on the GPU, for runtime masks (the
+ *                    post notes that they add planning overhead): items in LPT
+ *                    order are handed out num_bins per round, the round's j-th
+ *                    item to the j-th least-loaded bin (lower index on ties).
+ *                    Block plans only; at most 16384 (b, h, Q-block) items and
+ *                    1024 bins (else SA_ERR_UNSUPPORTED).  The plan call then
+ *                    never waits for the device: popcount and every list
+ *                    (full range and each chunk) are made on `stream`, and
+ *                    sparse_attn_plan_info waits for them to read the statistics. */
+typedef enum { SA_ORDER_LPT = 0, SA_ORDER_NAIVE = 1, SA_ORDER_LPT_XCD = 2, SA_ORDER_LPT_DEVICE = 3 } sa_order;
 typedef enum { SA_LAYOUT_CONTIGUOUS = 0, SA_LAYOUT_STRIPED = 1 } sa_layout;
 typedef enum { SA_KIND_BLOCK = 0, SA_KIND_TOPK = 1, SA_KIND_INDEX = 2 } sa_kind;
 
@@ -123,6 +132,7 @@ typedef struct {
   int64_t load_sum;     /* sum of the full-range item loads (= total_live for BLOCK) */
   int64_t makespan;     /* max bin load of the full-range list */
   int64_t lower_bound;  /* max(max item load, ceil(load_sum / num_bins)) */
+                        /* (SA_ORDER_LPT_DEVICE: the call waits for the plan to read these) */
   int32_t groups;       /* bin groups of SA_ORDER_LPT_XCD (XCDs), 1 otherwise */
   int32_t reserved;
 } sa_plan_info;
@@ -148,7 +158,9 @@ typedef enum {
  *  the list for the persistent kernel.  The list of a single chunk c (used by
  *  sparse_attn_fwd over [c, c+1), one ring step) is built from the same counts
  *  on its first use (that forward call, which then waits for its upload once,
- *  or sparse_attn_plan_copy).  This kind synchronises the stream once.
+ *  or sparse_attn_plan_copy).  This kind synchronises the stream once, except
+ *  with SA_ORDER_LPT_DEVICE, where every list is made on the GPU behind the
+ *  popcount and the call returns without waiting.
  *  TOPK: runs the indexer and top-k selection on the GPU; asynchronous.
  *  All kinds: the plan's device arrays are written on `stream`; sparse_attn_fwd
  *  makes its own stream wait for them, so a plan may be built on a side stream

@@ -31,6 +31,10 @@ struct sa_plan {
   int32_t* d_crow = nullptr;         // [B*H*C*nQ]
   int32_t* d_items = nullptr;        // [(C+1)][n_items]: list 0 = full range, list 1+c = chunk c
   int32_t* d_bin_ptr = nullptr;      // [(C+1)][num_bins+1]
+  // SA_ORDER_LPT_DEVICE: every list is made on the device; loads and statistics stay there
+  bool device_lists = false;
+  int64_t* d_bin_load = nullptr;     // [(C+1)][num_bins]
+  int64_t* d_stats = nullptr;        // [(C+1)][4]: load sum, max item load, makespan, lower bound
   std::vector<int32_t> h_items, h_bin_ptr;
   std::vector<int64_t> h_bin_load;   // [(C+1)][num_bins]
   // The full-range list is built by the plan call; the list of chunk c (used by forward calls
@@ -132,8 +136,8 @@ sa_status dalloc(T** ptr, size_t n) {
 void free_plan(sa_plan* p) {
   if (!p) return;
   (void)hipDeviceSynchronize();
-  void* ptrs[] = {p->d_mask, p->d_row, p->d_col, p->d_crow, p->d_items,
-                  p->d_bin_ptr, p->d_idx, p->d_count, p->d_qp, p->d_kp};
+  void* ptrs[] = {p->d_mask, p->d_row, p->d_col, p->d_crow, p->d_items, p->d_bin_ptr,
+                  p->d_bin_load, p->d_stats, p->d_idx, p->d_count, p->d_qp, p->d_kp};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
   if (p->ready) (void)hipEventDestroy(p->ready);
@@ -181,6 +185,15 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
     return st;
   SA_HIP(hipMemcpyAsync(P->d_mask, sp->mask, mask_bytes, hipMemcpyDeviceToDevice, stream));
   SA_HIP(sa::launch_popcount(P->d_mask, BH, nQ, nK, C, pr.layout, P->d_row, P->d_col, P->d_crow, stream));
+  if (P->order == SA_ORDER_LPT_DEVICE) {
+    // every list on the device, right behind the popcount: nothing waits for the host
+    if ((st = dalloc(&P->d_bin_load, (size_t)(C + 1) * P->num_bins)) || (st = dalloc(&P->d_stats, (size_t)(C + 1) * 4)))
+      return st;
+    SA_HIP(sa::launch_plan_rounds(P->d_row, P->d_crow, BH, nQ, C, P->num_bins, P->d_items, P->d_bin_ptr,
+                                  P->d_bin_load, P->d_stats, stream));
+    P->device_lists = true;
+    return SA_OK;
+  }
   std::vector<int32_t> row((size_t)BH * nQ), crow((size_t)BH * C * nQ);
   SA_HIP(hipMemcpyAsync(row.data(), P->d_row, row.size() * 4, hipMemcpyDeviceToHost, stream));
   SA_HIP(hipMemcpyAsync(crow.data(), P->d_crow, crow.size() * 4, hipMemcpyDeviceToHost, stream));
@@ -226,6 +239,7 @@ void build_chunk_list(sa_plan* P, int list) {
 
 // Device copy of list `list` (built on the host first if needed), ordered on `stream`.
 sa_status ensure_list_on_device(sa_plan* P, int list, hipStream_t stream) {
+  if (P->device_lists) return SA_OK;  // made on the device by the plan call
   build_chunk_list(P, list);
   std::lock_guard<std::mutex> lock(P->upload_mutex);
   if (P->list_uploaded[list]) return SA_OK;
@@ -304,7 +318,7 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
     return fail(SA_ERR_INVALID, "unknown sparsity kind %d", sp->kind);
   sa_status st = validate_problem(prob, sp->kind == SA_KIND_BLOCK);
   if (st) return st;
-  if (order != SA_ORDER_LPT && order != SA_ORDER_NAIVE && order != SA_ORDER_LPT_XCD)
+  if (order != SA_ORDER_LPT && order != SA_ORDER_NAIVE && order != SA_ORDER_LPT_XCD && order != SA_ORDER_LPT_DEVICE)
     return fail(SA_ERR_INVALID, "unknown order %d", order);
   if (num_bins < 0) return fail(SA_ERR_INVALID, "num_bins %d < 0", num_bins);
   sa_plan* P = new (std::nothrow) sa_plan();
@@ -317,6 +331,15 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
     return fail(SA_ERR_HIP, "hipGetDevice failed");
   }
   P->num_bins = num_bins ? num_bins : default_bins(*prob, P->device);
+  if (order == SA_ORDER_LPT_DEVICE && sp->kind == SA_KIND_BLOCK) {
+    const int64_t nQ = (prob->S + prob->block - 1) / prob->block;
+    const int64_t n_items = (int64_t)prob->B * prob->H * nQ;
+    if (n_items > sa::kDevicePlanMaxItems || P->num_bins > sa::kDevicePlanMaxBins) {
+      delete P;
+      return fail(SA_ERR_UNSUPPORTED, "device planning takes at most %d items and %d bins (got %lld, %d)",
+                  sa::kDevicePlanMaxItems, sa::kDevicePlanMaxBins, (long long)n_items, num_bins ? num_bins : 0);
+    }
+  }
   if (order == SA_ORDER_LPT_XCD) {
     P->groups = xcd_count(P->device);
     if (P->num_bins % P->groups != 0) P->groups = 1;  // groups must split the bins evenly
@@ -425,6 +448,14 @@ sa_status sparse_attn_plan_info(const sa_plan* P, sa_plan_info* out) {
   out->load_sum = P->load_sum;
   out->makespan = P->makespan;
   out->lower_bound = P->lower_bound;
+  if (P->device_lists) {  // statistics of list 0 live on the device: wait for the plan, then read them
+    int64_t s[4];
+    SA_HIP(hipEventSynchronize(P->ready));
+    SA_HIP(hipMemcpy(s, P->d_stats, sizeof(s), hipMemcpyDeviceToHost));
+    out->total_live = out->load_sum = s[0];
+    out->makespan = s[2];
+    out->lower_bound = s[3];
+  }
   out->groups = P->groups;
   return SA_OK;
 }
@@ -440,7 +471,8 @@ sa_status sparse_attn_plan_copy(const sa_plan* P, int32_t what, int32_t chunk, v
     if (chunk < -1 || chunk >= C) return fail(SA_ERR_INVALID, "chunk %d outside [-1, %d)", chunk, C);
   }
   const int list = chunk + 1;
-  if (block && list > 0 && (what == SA_PLAN_ITEMS || what == SA_PLAN_BIN_PTR || what == SA_PLAN_BIN_LOAD))
+  if (block && !P->device_lists && list > 0 &&
+      (what == SA_PLAN_ITEMS || what == SA_PLAN_BIN_PTR || what == SA_PLAN_BIN_LOAD))
     build_chunk_list(const_cast<sa_plan*>(P), list);
   const void* src = nullptr;
   bool device = true;
@@ -450,11 +482,25 @@ sa_status sparse_attn_plan_copy(const sa_plan* P, int32_t what, int32_t chunk, v
     case SA_PLAN_ROW: src = P->d_row; count = block ? BH * P->nQ : 0; break;
     case SA_PLAN_COL: src = P->d_col; count = block ? BH * P->nK : 0; break;
     case SA_PLAN_CROW: src = P->d_crow; count = block ? BH * C * P->nQ : 0; break;
-    case SA_PLAN_ITEMS: src = P->h_items.data() + (size_t)list * P->n_items; count = P->n_items; device = false; break;
+    case SA_PLAN_ITEMS:
+      device = P->device_lists;
+      src = device ? (const void*)(P->d_items + (size_t)list * P->n_items)
+                   : (const void*)(P->h_items.data() + (size_t)list * P->n_items);
+      count = P->n_items;
+      break;
     case SA_PLAN_BIN_PTR:
-      src = P->h_bin_ptr.data() + (size_t)list * (P->num_bins + 1); count = P->num_bins + 1; device = false; break;
+      device = P->device_lists;
+      src = device ? (const void*)(P->d_bin_ptr + (size_t)list * (P->num_bins + 1))
+                   : (const void*)(P->h_bin_ptr.data() + (size_t)list * (P->num_bins + 1));
+      count = P->num_bins + 1;
+      break;
     case SA_PLAN_BIN_LOAD:
-      src = P->h_bin_load.data() + (size_t)list * P->num_bins; count = P->num_bins; device = false; esize = 8; break;
+      device = P->device_lists;
+      src = device ? (const void*)(P->d_bin_load + (size_t)list * P->num_bins)
+                   : (const void*)(P->h_bin_load.data() + (size_t)list * P->num_bins);
+      count = P->num_bins;
+      esize = 8;
+      break;
     case SA_PLAN_TOPK_IDX: src = P->d_idx; count = block ? 0 : BH * pr.S * P->top_k; break;
     case SA_PLAN_TOPK_COUNT: src = P->d_count; count = block ? 0 : BH * pr.S; break;
     default: return fail(SA_ERR_INVALID, "unknown plan array %d", what);

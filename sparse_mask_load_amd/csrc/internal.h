@@ -14,6 +14,8 @@ namespace sa {
 // Limits of the compiled kernels (checked before any launch).
 constexpr int kMaxTilesPerRow = 2048;  // nK <= 2048: per-item tile list lives in LDS
 constexpr int kMaxChunks = 64;
+constexpr int kDevicePlanMaxItems = 16384;  // B*H*nQ of a plan made on the device (LDS sort buffer)
+constexpr int kDevicePlanMaxBins = 1024;    // one bin key per thread of the planning workgroup
 constexpr int kMaxMergeParts = 64;
 
 // Tile descriptor packed in an int32 (per-item tile list):
@@ -84,6 +86,11 @@ struct MergeArgs {
 // Kernel launchers (defined in the .hip files).  Return hipSuccess or the launch error.
 hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_chunks, int layout,
                            int32_t* row, int32_t* col, int32_t* crow, hipStream_t stream);
+// Round-based LPT of every list of a block plan on the device: list 0 from row, list 1 + c
+// from chunk c of crow; items [(C+1)][BH*nQ], bin_ptr [(C+1)][m+1], bin_load [(C+1)][m],
+// stats [(C+1)][4] = (load sum, max item load, makespan, lower bound).
+hipError_t launch_plan_rounds(const int32_t* row, const int32_t* crow, int BH, int nQ, int C, int m, int32_t* items,
+                              int32_t* bin_ptr, int64_t* bin_load, int64_t* stats, hipStream_t stream);
 hipError_t launch_attn_bf16(const FwdArgs& a, int D, int block, hipStream_t stream);
 int attn_bf16_wg_per_cu(int block);  // workgroups the bf16 kernel keeps resident per CU
 hipError_t launch_attn_f32(const FwdArgs& a, int D, int block, hipStream_t stream);

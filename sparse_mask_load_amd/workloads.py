@@ -209,13 +209,14 @@ def make(cfg: int, seed: int = 0, layout: str = "contiguous", with_data: bool = 
 def make_custom(B: int, H: int, S: int, D: int, block: int = 0, n_chunks: int = 1,
                 dtype: str = "bf16", pattern: str = "bernoulli", density: float = 0.5,
                 seed: int = 0, layout: str = "contiguous", top_k: int = 0, rank: int = 32,
-                causal: bool = True, diag: bool = True) -> Workload:
+                causal: bool = True, diag: bool = True, mask_only: bool = False) -> Workload:
     """Smaller workloads of the same families (for parity cases and edge cases).
 
     ``pattern``: "bernoulli" (per-entry live with probability ``density``), "causal"
     (lower-triangular), "ones", "empty" (no live tile at all), "zipf" (the skewed
     rank-profile recipe with density ``density``), or "topk" (no block mask; a rank
-    ``rank`` indexer with ``top_k`` keys per query).
+    ``rank`` indexer with ``top_k`` keys per query).  ``mask_only`` skips Q, K and V
+    (left None) for cases that need only the mask; the mask is drawn first either way.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     if pattern == "topk":
@@ -252,6 +253,6 @@ def make_custom(B: int, H: int, S: int, D: int, block: int = 0, n_chunks: int = 
         raise ValueError(pattern)
     if diag and pattern in ("bernoulli",):
         mask = _force_diag(mask)
-    q, k, v = _qkv(rng, B, H, S, D, dtype)
+    q, k, v = (None, None, None) if mask_only else _qkv(rng, B, H, S, D, dtype)
     return Workload(f"{pattern}-custom-{seed}", B, H, S, D, dtype, q, k, v, block=block,
                     n_chunks=n_chunks, layout=layout, mask=mask)
