@@ -24,6 +24,7 @@ struct sa_plan {
   int32_t groups = 1;  // bin groups of SA_ORDER_LPT_XCD (one per XCD), else 1
   int32_t nQ = 0, nK = 0, n_items = 0, top_k = 0, rank = 0, causal = 0;
   int device = 0;
+  int32_t n_xcd = 1;  // L2 domains (XCDs) of the device
   // BLOCK
   uint8_t* d_mask = nullptr;         // [B][H][nQ][nK] copy of the caller's mask
   int32_t* d_row = nullptr;          // [B*H*nQ]
@@ -297,6 +298,7 @@ sa_status plan_topk(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   a.qp = P->d_qp; a.kp = P->d_kp; a.idx = P->d_idx; a.count = P->d_count;
   a.B = pr.B; a.H = pr.H; a.S = pr.S; a.D = pr.D; a.rank = P->rank; a.top_k = P->top_k; a.causal = P->causal;
   a.sb = pr.sb; a.sh = pr.sh; a.ss = pr.ss;
+  a.n_xcd = P->n_xcd;
   SA_HIP(sa::launch_indexer(a, stream));
   // selected pairs are known in closed form: min(top_k, #candidates) per query
   int64_t tot = 0;
@@ -331,6 +333,7 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
     return fail(SA_ERR_HIP, "hipGetDevice failed");
   }
   P->num_bins = num_bins ? num_bins : default_bins(*prob, P->device);
+  P->n_xcd = xcd_count(P->device);
   if (order == SA_ORDER_LPT_DEVICE && sp->kind == SA_KIND_BLOCK) {
     const int64_t nQ = (prob->S + prob->block - 1) / prob->block;
     const int64_t n_items = (int64_t)prob->B * prob->H * nQ;

@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "kernel_common.h"
 
 namespace sa {
 namespace {
@@ -141,8 +142,11 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
   const int blocks_per_bh = (a.S + kRows - 1) / kRows;
-  const int bh = blockIdx.x / blocks_per_bh;
-  const int i0 = (blockIdx.x % blocks_per_bh) * kRows;
+  // each XCD takes whole heads in turn, so the head's K' blocks that every query block
+  // streams stay in that XCD's L2
+  const int blk = xcd_contiguous(blockIdx.x, gridDim.x, a.n_xcd);
+  const int bh = blk / blocks_per_bh;
+  const int i0 = (blk % blocks_per_bh) * kRows;
   const bool causal = a.causal != 0;
   const bf16* qp = a.qp + (int64_t)bh * a.S * kRank;
   const bf16* kp = a.kp + (int64_t)bh * a.S * kRank;

@@ -71,6 +71,7 @@ struct IndexerArgs {
   int32_t* count;  // [B][H][S]
   int32_t B, H, S, D, rank, top_k, causal;
   int64_t sb, sh, ss;
+  int32_t n_xcd;  // L2 domains of the device (workgroups are dealt to them round-robin)
 };
 
 struct MergeArgs {

@@ -52,6 +52,19 @@ __device__ inline int build_tile_list(const uint8_t* __restrict__ mrow, int nK, 
   return count;
 }
 
+// Workgroup index remapped so that each XCD works through one contiguous range
+// of [0, n) in order.  Workgroups b = 0, 1, ... of a launch are dealt to the
+// n_xcd XCDs round-robin (b mod n_xcd); XCD x then runs logical indices
+// start(x) + b / n_xcd, where start(x) counts the workgroups of the XCDs before
+// it (the first n mod n_xcd XCDs get one more).  A bijection on [0, n).  Work
+// indexed head-major thereby keeps each head on one XCD, in one L2.
+__device__ __forceinline__ int xcd_contiguous(int b, int n, int n_xcd) {
+  if (n_xcd <= 1) return b;
+  const int x = b % n_xcd, s = b / n_xcd;
+  const int per = n / n_xcd, rem = n % n_xcd;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + s;
+}
+
 __device__ inline int64_t realtime_now() { return (int64_t)__builtin_amdgcn_s_memrealtime(); }
 
 // (XCC_ID << 32) | HW_ID of the executing wave: identifies the compute unit.
