@@ -323,6 +323,13 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
   if (order != SA_ORDER_LPT && order != SA_ORDER_NAIVE && order != SA_ORDER_LPT_XCD && order != SA_ORDER_LPT_DEVICE)
     return fail(SA_ERR_INVALID, "unknown order %d", order);
   if (num_bins < 0) return fail(SA_ERR_INVALID, "num_bins %d < 0", num_bins);
+  if (order == SA_ORDER_LPT_DEVICE && sp->kind == SA_KIND_BLOCK) {
+    const int64_t nQ = (prob->S + prob->block - 1) / prob->block;
+    const int64_t n_items = (int64_t)prob->B * prob->H * nQ;
+    if (n_items > sa::kDevicePlanMaxItems || num_bins > sa::kDevicePlanMaxBins)
+      return fail(SA_ERR_UNSUPPORTED, "device planning takes at most %d items and %d bins (got %lld, %d)",
+                  sa::kDevicePlanMaxItems, sa::kDevicePlanMaxBins, (long long)n_items, num_bins);
+  }
   sa_plan* P = new (std::nothrow) sa_plan();
   if (!P) return fail(SA_ERR_NOMEM, "host allocation of the plan failed");
   P->prob = *prob;
@@ -334,14 +341,10 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
   }
   P->num_bins = num_bins ? num_bins : default_bins(*prob, P->device);
   P->n_xcd = xcd_count(P->device);
-  if (order == SA_ORDER_LPT_DEVICE && sp->kind == SA_KIND_BLOCK) {
-    const int64_t nQ = (prob->S + prob->block - 1) / prob->block;
-    const int64_t n_items = (int64_t)prob->B * prob->H * nQ;
-    if (n_items > sa::kDevicePlanMaxItems || P->num_bins > sa::kDevicePlanMaxBins) {
-      delete P;
-      return fail(SA_ERR_UNSUPPORTED, "device planning takes at most %d items and %d bins (got %lld, %d)",
-                  sa::kDevicePlanMaxItems, sa::kDevicePlanMaxBins, (long long)n_items, num_bins ? num_bins : 0);
-    }
+  if (order == SA_ORDER_LPT_DEVICE && sp->kind == SA_KIND_BLOCK && P->num_bins > sa::kDevicePlanMaxBins) {
+    delete P;  // the default bin count of this device is above the planner's limit
+    return fail(SA_ERR_UNSUPPORTED, "device planning takes at most %d bins (default here: %d)",
+                sa::kDevicePlanMaxBins, P->num_bins);
   }
   if (order == SA_ORDER_LPT_XCD) {
     P->groups = xcd_count(P->device);

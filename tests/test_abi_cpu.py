@@ -100,7 +100,7 @@ def test_host_assign_errors():
 
 
 def _problem(**kw):
-    base = dict(B=1, H=2, S=256, D=64, block=64, n_chunks=2, layout=0, dtype=bd.SA_BF16, scale=0.0, pad0=0,
+    base = dict(B=1, H=2, S=256, D=64, block=64, n_chunks=2, layout=0, dtype=bd.SA_BF16, scale=0.0, token_causal=0,
                 sb=2 * 256 * 64, sh=256 * 64, ss=64)
     base.update(kw)
     return bd.sa_problem(**base)
@@ -125,6 +125,36 @@ def test_plan_rejects_bad_problems_before_touching_the_gpu(kw, status):
     st = bd.lib().sparse_attn_plan(ctypes.byref(prob), ctypes.byref(sp), 0, 0, ctypes.byref(out), None)
     assert st == status, bd.sa_last_error()
     assert out.value is None
+
+
+def _plan_status(prob, kind=bd.SA_KIND_BLOCK, order=0, num_bins=0):
+    import ctypes
+    sp = bd.sa_sparsity(kind, 32, 8, 1, 1, 1, 1, 1, 1, None, None)
+    out = ctypes.c_void_p()
+    st = bd.lib().sparse_attn_plan(ctypes.byref(prob), ctypes.byref(sp), num_bins, order, ctypes.byref(out), None)
+    assert out.value is None
+    return st
+
+
+def test_problem_fields_are_the_declared_ones():
+    # a misspelt keyword would become a plain Python attribute and leave the field at 0
+    names = [n for n, _ in bd.sa_problem._fields_]
+    assert names == ["B", "H", "S", "D", "block", "n_chunks", "layout", "dtype", "scale", "token_causal",
+                     "sb", "sh", "ss"]
+
+
+def test_token_causal_only_for_block_plans():
+    assert _plan_status(_problem(token_causal=1), kind=bd.SA_KIND_TOPK) == bd.SA_ERR_INVALID
+    assert "token_causal" in bd.sa_last_error()
+
+
+def test_device_order_limits_checked_before_the_gpu():
+    # 65 heads of 256 Q-blocks = 16640 items, above the device planner's 16384
+    big = _problem(H=65, S=16384, sb=65 * 16384 * 64, sh=16384 * 64, n_chunks=1)
+    assert _plan_status(big, order=bd.SA_ORDER_LPT_DEVICE) == bd.SA_ERR_UNSUPPORTED
+    assert "16384" in bd.sa_last_error()
+    assert _plan_status(_problem(), order=bd.SA_ORDER_LPT_DEVICE, num_bins=1025) == bd.SA_ERR_UNSUPPORTED
+    assert _plan_status(_problem(), order=4) == bd.SA_ERR_INVALID
 
 
 def test_fwd_and_merge_argument_errors():
