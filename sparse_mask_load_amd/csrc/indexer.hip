@@ -124,7 +124,8 @@ __device__ __forceinline__ f32x16 tile_scores(const KFrag& kf, const bf16x8 (&qf
                                               bool causal, bool edge, int lane) {
   f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.k0, qf[0], f32x16{}, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.k1, qf[1], acc, 0, 0, 0);
-  if (edge) {
+  // wave-uniform, and rare (diagonal and last blocks): a branch, not predicated code
+  if (__builtin_expect(__builtin_amdgcn_readfirstlane((int)edge) != 0, 0)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = kb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -255,7 +256,9 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
             bits |= (sc[r] > t_filter ? 1u : 0u) << r;
             tie |= sc[r] == t_filter;
           }
-          if (tie) {
+          // exact ties with the threshold are rare: branch on the whole wave, so that the key
+          // compares below do not run (predicated) for every block
+          if (__builtin_expect(__ballot(tie) != 0, 0) && tie) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int j = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
