@@ -2,12 +2,12 @@
 
 One step = one pass of the whole path over one batch of the causal long-sequence
 workload (B1 H16 S16384 d128, block 128, lower-triangular block mask, KV in 4 contiguous
-chunks, two-level LPT over one bin per compute unit: heads to the XCDs, then Q-blocks to
-each XCD's bins):
+chunks, one bin per compute unit):
 
-  1. sparse_attn_plan: GPU popcount of the mask + host LPT + upload of the work lists
-     (the mask is a runtime input, so every step re-plans; the plan is built on a side
-     stream, so its host part overlaps the previous step's attention);
+  1. sparse_attn_plan: GPU popcount of the mask and the work lists, by default with the
+     device planner (round-based LPT made on the GPU; --order lpt_xcd / lpt / naive plan
+     on the host instead).  The mask is a runtime input, so every step re-plans, on a
+     side stream; the forward call waits for the plan's event;
   2. sparse_attn_fwd in partial mode over chunks [0, 4): one (O, m, l) partial per chunk;
   3. chunk_merge: online-softmax merge of the 4 partials into O (bf16).
 
@@ -165,7 +165,7 @@ def main() -> int:
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="causal")
     ap.add_argument("--mode", choices=["merged", "fused"], default="merged",
                     help="merged: partial chunks + chunk_merge (default); fused: chunks folded in-kernel")
-    ap.add_argument("--order", choices=["lpt_xcd", "lpt", "naive", "lpt_device"], default="lpt_xcd",
+    ap.add_argument("--order", choices=["lpt_xcd", "lpt", "naive", "lpt_device"], default="lpt_device",
                     help="work order: two-level LPT (heads to XCDs, then Q-blocks), one-level LPT, round-robin, "
                          "round-based LPT made on the GPU")
     ap.add_argument("--bins", type=int, default=0, help="persistent workgroups (0: one per resident slot)")
@@ -295,9 +295,9 @@ def main() -> int:
         merge_ms = e0.elapsed_time(e1) / reps
         merge_bytes = rows * (C * (D * 4 + 8) + D * (2 if w.dtype == "bf16" else 4))
         t_plan = time.perf_counter()
-        for _ in range(reps):
-            bd.sparse_attn_plan(prob, "block", mask=mask, order=args.order).close()
-        plan_ms = (time.perf_counter() - t_plan) * 1e3 / reps
+        for _ in range(reps):  # host planner (waits for the counts, LPT on the host)
+            bd.sparse_attn_plan(prob, "block", mask=mask, order="lpt_xcd").close()
+        plan_host_ms = (time.perf_counter() - t_plan) * 1e3 / reps
         # device planner: host cost of the call (it returns without waiting) and its GPU time
         t_plan = time.perf_counter()
         dplans = [bd.sparse_attn_plan(prob, "block", mask=mask, order="lpt_device") for _ in range(reps)]
@@ -314,16 +314,17 @@ def main() -> int:
             gpu_ms.append(e0.elapsed_time(e1))
             p_d.close()
         plan_device_gpu_ms = float(np.median(gpu_ms))
-        # whole steps with device plans (same loop as the timed one)
+        # whole steps with the other planner (same loop as the timed one)
         order_main = args.order
-        args.order = "lpt_device"
+        other_order = "lpt_xcd" if order_main == "lpt_device" else "lpt_device"
+        args.order = other_order
         for _ in range(2):
             step(False).close()
         torch.cuda.synchronize()
         t_dev = time.perf_counter()
         dplans = [step(False) for _ in range(args.steps)]
         torch.cuda.synchronize()
-        step_device_plan_ms = (time.perf_counter() - t_dev) * 1e3 / args.steps
+        step_other_ms = (time.perf_counter() - t_dev) * 1e3 / args.steps
         for p_d in dplans:
             p_d.close()
         args.order = order_main
@@ -349,7 +350,7 @@ def main() -> int:
         p_tc.close()
 
         result["breakdown"] = {
-            "plan_ms": round(plan_ms, 4), "fwd_partial_ms": round(kernel_ms, 4),
+            "plan_host_ms": round(plan_host_ms, 4), "fwd_partial_ms": round(kernel_ms, 4),
             "fwd_fused_ms": round(fused_ms, 4), "fused_tflops": round(flop / fused_ms / 1e9, 2),
             "fused_pct_bf16_peak": round(100 * flop / fused_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
             "merge_ms": round(merge_ms, 4), "merge_gbs": round(merge_bytes / merge_ms / 1e6, 1),
@@ -358,7 +359,7 @@ def main() -> int:
             "xcd_groups": alt_ms["lpt_xcd"][1]["groups"],
             "fwd_fused_token_causal_ms": round(tc_ms, 4),
             "plan_device_call_ms": round(plan_device_call_ms, 4), "plan_device_gpu_ms": round(plan_device_gpu_ms, 4),
-            "ms_per_step_device_plan": round(step_device_plan_ms, 4),
+            "ms_per_step_by_planner": {order_main: round(ms_per_step, 4), other_order: round(step_other_ms, 4)},
         }
     plan.close()
 
