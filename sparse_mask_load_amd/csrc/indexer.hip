@@ -23,9 +23,11 @@
 //    moves it (by the normal-model distance between the observed and the
 //    target count, then by bisection of the key space, which ends because one
 //    more unit of the threshold removes at most one key).  Finally
-//    a wave per row picks the exact top_k from its buffer by bisection on the
-//    importance bits and, for ties, on the key index.  The order of the
-//    indices within a row's list is unspecified.
+//    a wave per row picks the exact top_k from its buffer: a radix select of
+//    the top_k-th largest importance bits, 8 bits per round (a histogram of the
+//    next byte among the entries that match the bytes fixed so far), then, for
+//    ties, bisection on the key index.  The order of the indices within a
+//    row's list is unspecified.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -356,38 +358,53 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
     uint32_t t_ord = 0;   // selected: ord > t_ord, plus ord == t_ord with index <= t_j
     int t_j = -1;
     if (n > need) {
-      // Bracket lo < h <= hi of the need-th largest ord h: count(> lo) >= need > count(> hi).
-      // Interpolation steps (the counts are close to linear in ord within the bracket)
-      // alternate with bisection, which bounds the worst case at about 64 steps.
-      uint32_t omin = 0xFFFFFFFFu, omax = 0;
+      // Radix select of the need-th largest ord, 8 bits at a time from the top: a histogram
+      // of the next digit among the entries that match the digits fixed so far, then the
+      // digit where the count from the top reaches the keys still needed.  The histogram
+      // lives in this row's score buffer, whose entries are now in registers (a wave's LDS
+      // accesses complete in order, so the reads above precede these writes).
+      uint32_t* hist = (uint32_t*)sh.score[row];
+      uint32_t prefix = 0, pmask = 0;
+      int remaining = need;  // keys still to take among the entries matching prefix
+      for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
-      for (int e = 0; e < kPer; ++e)
-        if (e * 64 + lane < n) {
-          omin = min(omin, o[e]);
-          omax = max(omax, o[e]);
+        for (int q = 0; q < 4; ++q) hist[q * 64 + lane] = 0u;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+          if (e * 64 + lane < n && (o[e] & pmask) == prefix) atomicAdd(&hist[(o[e] >> shift) & 255u], 1u);
+        // lane L holds digits 4L .. 4L+3; counts of larger digits come from the lanes above
+        const uint32_t cnt[4] = {hist[4 * lane], hist[4 * lane + 1], hist[4 * lane + 2], hist[4 * lane + 3]};
+        const uint32_t mine = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+        uint32_t above = mine;  // inclusive suffix sum over lanes >= this one
+#pragma unroll
+        for (int w = 1; w < 64; w <<= 1) {
+          const uint32_t v = (uint32_t)__shfl_down((int)above, w);
+          if (lane + w < 64) above += v;
         }
-      for (int w = 32; w >= 1; w >>= 1) {
-        omin = min(omin, (uint32_t)__shfl_xor((int)omin, w));
-        omax = max(omax, (uint32_t)__shfl_xor((int)omax, w));
+        above -= mine;  // entries with a digit above this lane's four
+        // find the digit d with count(> d) < remaining <= count(>= d); exactly one lane has it
+        int found = -1;
+        uint32_t gt_found = 0;
+        uint32_t ge = above;
+#pragma unroll
+        for (int k = 3; k >= 0; --k) {
+          const uint32_t gt = ge;
+          ge += cnt[k];
+          if (found < 0 && gt < (uint32_t)remaining && ge >= (uint32_t)remaining) {
+            found = 4 * lane + k;
+            gt_found = gt;
+          }
+        }
+        const uint64_t who = __ballot(found >= 0);
+        const int src = __builtin_ctzll(who);
+        const int digit = __shfl(found, src);
+        const uint32_t gt_d = (uint32_t)__shfl((int)gt_found, src);
+        prefix |= (uint32_t)digit << shift;
+        pmask |= 255u << shift;
+        remaining -= (int)gt_d;
       }
-      uint32_t lo = omin - 1, hi = omax;  // entries' ords are >= 0x00800000, so omin - 1 does not wrap
-      int c_lo = n, c_hi = 0;
-      for (int step = 0; hi - lo > 1; ++step) {
-        uint32_t mid = lo + (hi - lo) / 2;
-        if ((step & 1) == 0) {
-          const float f = (float)(c_lo - need) + 0.5f;
-          const uint32_t guess = lo + (uint32_t)((float)(hi - lo) * (f / (float)(c_lo - c_hi)));
-          mid = min(max(guess, lo + 1), hi - 1);
-        }
-        const int c = count_if([&](uint32_t ov, int) { return ov > mid; });
-        if (c >= need) {
-          lo = mid;
-          c_lo = c;
-        } else {
-          hi = mid;
-          c_hi = c;
-        }
-      }
+      const uint32_t hi = prefix;  // the need-th largest ord
+      const int c_hi = need - remaining;  // entries strictly above it
       t_ord = hi;
       const int ties_needed = need - c_hi;
       if (count_if([&](uint32_t ov, int) { return ov == hi; }) == ties_needed) {
