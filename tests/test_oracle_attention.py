@@ -236,3 +236,27 @@ def test_token_causal_row_sampling_matches_full():
     for n, (b, h, i) in enumerate(rows):
         assert np.abs(Os[n] - O[b, h, i]).max() < 1e-13
         assert (np.isneginf(ls[n]) and np.isneginf(lse[b, h, i])) or abs(ls[n] - lse[b, h, i]) < 1e-12
+
+
+def test_merge_of_random_uneven_key_splits_equals_unchunked():
+    """Split the KV blocks into random groups of uneven sizes (not the chunk layouts), take each
+    group's normalised result as a partial (O, m = lse, l = 1; empty rows (0, -inf, 0)), and fold
+    them in a random order: the merge must give the unsplit result."""
+    rng = np.random.default_rng(31)
+    w = W.make_custom(1, 2, 320, 16, block=32, pattern="bernoulli", density=0.5, dtype="f32", seed=31)
+    ref, ref_lse = A.masked_attention(w.q, w.k, w.v, w.mask, 32)
+    nK = w.mask.shape[-1]
+    for trial in range(5):
+        cuts = np.sort(rng.choice(np.arange(1, nK), size=rng.integers(1, 5), replace=False))
+        groups = np.split(rng.permutation(nK), cuts)
+        parts = []
+        for g in groups:
+            m_g = np.zeros_like(w.mask)
+            m_g[..., g] = w.mask[..., g]
+            O_g, lse_g = A.masked_attention(w.q, w.k, w.v, m_g, 32)
+            parts.append((O_g, lse_g, np.where(np.isneginf(lse_g), 0.0, 1.0)))
+        order = rng.permutation(len(parts))
+        O, lse = A.merge([parts[i] for i in order])
+        assert np.abs(O - ref).max() < 1e-12
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(fin, np.isfinite(lse)) and np.abs(lse[fin] - ref_lse[fin]).max() < 1e-12
