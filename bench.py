@@ -329,8 +329,14 @@ def main() -> int:
             p_d.close()
         args.order = order_main
         alt_ms = {}
-        for alt in ("naive", "lpt", "lpt_xcd", "lpt_device"):
-            p_alt = bd.sparse_attn_plan(prob, "block", mask=mask, order=alt)
+        # persistent orders over one bin per resident workgroup, then one item per workgroup
+        # (a plain grid that the hardware dispatches as compute units free up), in id order
+        # and in LPT order
+        n_items = info["n_items"]
+        alts = [(o_, o_, 0) for o_ in ("naive", "lpt", "lpt_xcd", "lpt_device")]
+        alts += [("grid_id_order", "naive", n_items), ("grid_lpt_order", "lpt", n_items)]
+        for alt, alt_order, alt_bins in alts:
+            p_alt = bd.sparse_attn_plan(prob, "block", mask=mask, order=alt_order, num_bins=alt_bins)
             e0.record(stream)
             for _ in range(reps):
                 bd.sparse_attn_fwd(p_alt, q, k, v, 0, C, o=out)
