@@ -467,12 +467,11 @@ void attn_bf16_kernel(FwdArgs a) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x4 v4 = {st.acc[d][4 * g], st.acc[d][4 * g + 1], st.acc[d][4 * g + 2], st.acc[d][4 * g + 3]};
-            // streamed once into the merge: non-temporal, so that it does not evict K and V
-            __builtin_nontemporal_store(v4, (f32x4*)(op + d * 32 + 8 * g + 4 * h2));
+            *(f32x4*)(op + d * 32 + 8 * g + 4 * h2) = v4;
           }
         if (h2 == 0) {
-          __builtin_nontemporal_store(m == kNegInf ? kNegInf : m * kLn2, a.m_part + prow);
-          __builtin_nontemporal_store(l_row, a.l_part + prow);
+          a.m_part[prow] = m == kNegInf ? kNegInf : m * kLn2;
+          a.l_part[prow] = l_row;
         }
       }
       reset(st);
