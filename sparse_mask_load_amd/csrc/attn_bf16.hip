@@ -451,14 +451,10 @@ void attn_bf16_kernel(FwdArgs a) {
     int cur_chunk = a.c0;
 
     // Merges the two key halves and writes chunk `chunk`'s partial (O in the
-    // true-max basis, m in natural-log units, l), then resets the state.  A
-    // chunk without tiles (the same for every wave) writes the empty partial
-    // (0, -inf, 0) from the reset state, with no exchange between the halves.
-    bool chunk_live = false;  // a tile of the current chunk has been processed
+    // true-max basis, m in natural-log units, l), then resets the state.
     auto flush_partial = [&](int chunk, float* kscr, float* mscr) {
-      float m = kNegInf, l_row = 0.f;
-      if (chunk_live) merge_halves<D, BLK>(st, m, l_row, kscr, mscr, rg, kh, lane);
-      chunk_live = false;
+      float m, l_row;
+      merge_halves<D, BLK>(st, m, l_row, kscr, mscr, rg, kh, lane);
       if (kh == 0 && qrow < a.S) {
         const int64_t prow = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + qrow;
         float* op = a.o_part + prow * D;
@@ -537,7 +533,6 @@ void attn_bf16_kernel(FwdArgs a) {
       if (!full) {
         const int tchunk = (desc >> kDescChunkShift) & 63;
         while (cur_chunk < tchunk) flush_partial(cur_chunk++, (float*)kfree, (float*)vfree);
-        chunk_live = true;
       }
       // K of tile t+2 and V of tile t+1 are loaded in slices, one per key block,
       // so that no wave stalls on a full memory-request queue.  Near the end of
