@@ -452,24 +452,49 @@ void attn_bf16_kernel(FwdArgs a) {
 
     // Merges the two key halves and writes chunk `chunk`'s partial (O in the
     // true-max basis, m in natural-log units, l), then resets the state.
+    // The merged O rows are staged through the two free tile buffers (rows
+    // [0, BLK/2) in kscr, the rest in mscr, 16-byte chunks XOR-swizzled by
+    // row) and then stored by all waves as whole rows, so that each store
+    // instruction writes contiguous rows instead of 32-byte pieces of 32 rows.
     auto flush_partial = [&](int chunk, float* kscr, float* mscr) {
+      constexpr int CH = D / 4;                // 16-byte chunks per fp32 row
+      constexpr int HALF = BLK / 2;            // rows per staging buffer
+      constexpr int RPS = 64 / CH;             // rows per store instruction
+      constexpr int NST = BLK / SH::NW / RPS;  // store instructions per wave
+      static_assert(HALF * D * 4 <= SH::TILE * 2, "staging half must fit in a tile buffer");
+      static_assert(NST * RPS * SH::NW == BLK, "store rows must cover the block");
       float m, l_row;
       merge_halves<D, BLK>(st, m, l_row, kscr, mscr, rg, kh, lane);
-      if (kh == 0 && qrow < a.S) {
-        const int64_t prow = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + qrow;
-        float* op = a.o_part + prow * D;
+      const int64_t prow0 = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK;
+      if (kh == 0) {
+        const int r = rg * 32 + l32;  // a wave's 32 rows lie in one staging buffer
+        float* const rowp = (rg * 32 < HALF ? kscr : mscr) + (r % HALF) * D;
 #pragma unroll
         for (int d = 0; d < ND; ++d)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
+            const int c = 8 * d + 2 * g + h2;
             const f32x4 v4 = {st.acc[d][4 * g], st.acc[d][4 * g + 1], st.acc[d][4 * g + 2], st.acc[d][4 * g + 3]};
-            *(f32x4*)(op + d * 32 + 8 * g + 4 * h2) = v4;
+            *(f32x4*)(rowp + 4 * (c ^ (r & (CH - 1)))) = v4;
           }
-        if (h2 == 0) {
-          a.m_part[prow] = m == kNegInf ? kNegInf : m * kLn2;
-          a.l_part[prow] = l_row;
+        if (h2 == 0 && qrow < a.S) {
+          a.m_part[prow0 + r] = m == kNegInf ? kNegInf : m * kLn2;
+          a.l_part[prow0 + r] = l_row;
         }
       }
+      __syncthreads();
+      {
+        // rows [wave*NST*RPS, (wave+1)*NST*RPS) of one staging buffer
+        const float* const buf = (wave * NST * RPS < HALF ? kscr : mscr);
+        const int c = lane % CH;
+#pragma unroll 1
+        for (int i = 0; i < NST; ++i) {
+          const int r = (wave * NST + i) * RPS + lane / CH;
+          const f32x4 v4 = *(const f32x4*)(buf + (r % HALF) * D + 4 * (c ^ (r & (CH - 1))));
+          if (qb * BLK + r < a.S) *(f32x4*)(a.o_part + (prow0 + r) * D + 4 * c) = v4;
+        }
+      }
+      __syncthreads();  // the staging buffers are free again (tile loads go there next)
       reset(st);
     };
     // live bits of this wave's key blocks of a tile
