@@ -26,17 +26,37 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(MergeArgs a) {
   const int dq = (threadIdx.x % TPR) * 4;
   float m_acc = kNegInf, l_acc = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int p = 0; p < a.n_parts; ++p) {
-    const float mp = a.m[p][row];
-    if (mp == kNegInf) continue;
-    const float lp = a.l[p][row];
-    const float m_new = fmaxf(m_acc, mp);
-    const float alpha = expf(m_acc - m_new);
-    const float beta = expf(mp - m_new);
-    const f32x4 op = *(const f32x4*)(a.o[p] + row * D + dq);
-    o = alpha * o + beta * op;
-    l_acc = alpha * l_acc + beta * lp;
-    m_acc = m_new;
+  // Parts are read in groups of G: the statistics of the group first, then
+  // the O vectors of its non-empty parts, all in flight together; the fold
+  // itself runs in part order.
+  constexpr int G = 4;
+  for (int p0 = 0; p0 < a.n_parts; p0 += G) {
+    float mp[G], lp[G];
+    f32x4 op[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      mp[i] = p0 + i < a.n_parts ? a.m[p0 + i][row] : kNegInf;
+      lp[i] = p0 + i < a.n_parts ? a.l[p0 + i][row] : 0.f;
+    }
+    // the statistics are complete here; passing them through an empty asm
+    // keeps the compiler from waiting on loads in flight at each test below
+#pragma unroll
+    for (int i = 0; i < G; ++i) asm volatile("" : "+v"(mp[i]));
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      op[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (mp[i] != kNegInf) op[i] = *(const f32x4*)(a.o[p0 + i] + row * D + dq);
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (mp[i] == kNegInf) continue;
+      const float m_new = fmaxf(m_acc, mp[i]);
+      const float alpha = expf(m_acc - m_new);
+      const float beta = expf(mp[i] - m_new);
+      o = alpha * o + beta * op[i];
+      l_acc = alpha * l_acc + beta * lp[i];
+      m_acc = m_new;
+    }
   }
   const float inv = l_acc > 0.f ? 1.f / l_acc : 0.f;
   OutT* out = (OutT*)a.out + row * D + dq;
