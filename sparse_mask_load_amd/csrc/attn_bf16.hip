@@ -209,9 +209,56 @@ __device__ __forceinline__ void reset(RowState<ND>& st) {
 }
 
 // Per-lane LDS operand geometry (independent of tile, key block and step);
-// key block j of a wave is block kb0 + j of the tile.
+// key block j of a wave is block kb0 + j of the tile.  PINNED: the element
+// offsets of every read are formed once and pinned, so that each read is one
+// register plus an immediate (the buffer's address and the key-block offset)
+// with no address arithmetic left per tile (measured faster in the full-tile
+// variant); otherwise the row base and the swizzle are combined per read
+// (measured faster where scores are masked per element).
+template <int D, bool PINNED>
+struct OperandLanes;
+
 template <int D>
-struct OperandLanes {
+struct OperandLanes<D, true> {
+  int k_ofs[D / 16];     // K rows at k-step ks
+  int v_ofs[D / 32][2];  // the two V^T row quads of head-dim block d
+  __device__ __forceinline__ void init(int lane, int kb0) {
+    const int h2 = lane >> 5;
+    const int l32 = lane & 31;
+    const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);  // bits 2,3 swapped
+    const int k_swz = chunk_swizzle<D>(krow);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      k_ofs[ks] = (kb0 * 32 + krow) * D + (((2 * ks + h2) ^ k_swz) << 3);
+      asm volatile("" : "+v"(k_ofs[ks]));
+    }
+    const int v_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int vrow = 8 * h2 + 4 * rr + ((lane & 15) >> 2);
+      const int v_swz = chunk_swizzle<D>(vrow);
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) {
+        v_ofs[d][rr] = (kb0 * 32 + vrow) * D + 4 * (lane & 1) + (((4 * d + v_chunk) ^ v_swz) << 3);
+        asm volatile("" : "+v"(v_ofs[d][rr]));
+      }
+    }
+  }
+  // K rows of 32-key block kb at k-step ks (A operand of S^T).
+  __device__ __forceinline__ bf16x8 k_frag(const bf16* Kt, int kb, int ks) const {
+    return *(const bf16x8*)(Kt + kb * 32 * D + k_ofs[ks]);
+  }
+  // V^T rows of head-dim block d for the 16-key step `half` of key block kb (A operand of O^T).
+  __device__ __forceinline__ bf16x8 v_frag(const bf16* Vt, int kb, int half, int d) const {
+    const bf16* vp = Vt + (kb * 32 + 16 * half) * D;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_ofs[d][0]));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vp + v_ofs[d][1]));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
+template <int D>
+struct OperandLanes<D, false> {
   int k_off, k_swz, h2;
   int v_off[2], v_swz[2], v_chunk;
   __device__ __forceinline__ void init(int lane, int kb0) {
@@ -228,11 +275,9 @@ struct OperandLanes {
     }
     v_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   }
-  // K rows of 32-key block kb at k-step ks (A operand of S^T).
   __device__ __forceinline__ bf16x8 k_frag(const bf16* Kt, int kb, int ks) const {
     return *(const bf16x8*)(Kt + kb * 32 * D + k_off + (((2 * ks + h2) ^ k_swz) << 3));
   }
-  // V^T rows of head-dim block d for the 16-key step `half` of key block kb (A operand of O^T).
   __device__ __forceinline__ bf16x8 v_frag(const bf16* Vt, int kb, int half, int d) const {
     const bf16* vp = Vt + (kb * 32 + 16 * half) * D;
     const int ch = 4 * d + v_chunk;
@@ -245,9 +290,9 @@ struct OperandLanes {
 // S^T = K Q^T of the wave's key blocks of one tile, k-step major: one MFMA per
 // live 32-key block per step, the K fragments of the next step read while the
 // current MFMAs run.
-template <int D, int BLK, bool GENERAL>
+template <int D, int BLK, bool GENERAL, class OL>
 __device__ __forceinline__ void tile_scores(const bf16* __restrict__ Kt, const bf16x8 (&qf)[D / 16],
-                                            const OperandLanes<D>& ol, int live_w, f32x16 (&s)[BLK / 64]) {
+                                            const OL& ol, int live_w, f32x16 (&s)[BLK / 64]) {
   using SH = Shape<D, BLK>;
   constexpr int NB = SH::NKBW, NKS = SH::NKS;
   auto live = [&](int j) { return !GENERAL || ((live_w >> j) & 1); };
@@ -287,12 +332,29 @@ __device__ __forceinline__ float tile_max(f32x16 (&s)[BLK / 64], RowState<D / 32
       for (int r = 0; r < 16; ++r)
         if (j * 32 + 16 * (r >> 3) + (r & 7) > off_max) s[j][r] = kNegInf;
   }
-  float mx = kNegInf;
+  float mx;
+  if constexpr (!MASKED) {
+    // two running maxima, each taking two scores per step (one v_max3 each)
+    float mx0 = kNegInf, mx1 = kNegInf;
 #pragma unroll
-  for (int j = 0; j < SH::NKBW; ++j) {
-    if (!live(j)) continue;
+    for (int j = 0; j < SH::NKBW; ++j) {
+      if (!live(j)) continue;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[j][r], s[j][r + 1]));
+      for (int r = 0; r < 16; r += 4) {
+        mx0 = fmaxf(fmaxf(mx0, s[j][r]), s[j][r + 1]);
+        mx1 = fmaxf(fmaxf(mx1, s[j][r + 2]), s[j][r + 3]);
+      }
+    }
+    mx = fmaxf(mx0, mx1);
+  } else {
+    // pairwise form: measured faster in the variants that mask scores per element
+    mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < SH::NKBW; ++j) {
+      if (!live(j)) continue;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[j][r], s[j][r + 1]));
+    }
   }
   mx = fmaxf(mx, other_half(mx)) * sl2;
   st.m_true = fmaxf(st.m_true, mx);
@@ -413,7 +475,7 @@ void attn_bf16_kernel(FwdArgs a) {
   TileLoader<D, BLK> loader;
   loader.init(wave, lane);
   loader.set_stride(striped ? (int)(a.ss * a.n_chunks) : (int)a.ss);
-  OperandLanes<D> ol;
+  OperandLanes<D, !MASKED> ol;
   ol.init(lane, kb0);
   const bf16* __restrict__ gQ = (const bf16*)a.q;
   const bf16* __restrict__ gK = (const bf16*)a.k;
