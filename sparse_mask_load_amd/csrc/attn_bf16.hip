@@ -359,14 +359,19 @@ __device__ __forceinline__ float tile_max(f32x16 (&s)[BLK / 64], RowState<D / 32
   mx = fmaxf(mx, other_half(mx)) * sl2;
   st.m_true = fmaxf(st.m_true, mx);
   if (__builtin_amdgcn_ballot_w64(mx > st.m_ref + kRescaleSlack)) {
+    // while every lane's reference is -inf the state is still all zeros (nothing
+    // has been accumulated), so the first move of the reference needs no rescale
+    const bool fresh = !__builtin_amdgcn_ballot_w64(st.m_ref != kNegInf);
     const float m_new = (mx > st.m_ref + kRescaleSlack) ? st.m_true : st.m_ref;
     // a lane with no finite score yet (possible only under token-level causality) keeps
     // its zero state: alpha = 1 instead of exp2(-inf - -inf)
     const float alpha = (MASKED && m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
     st.m_ref = m_new;
-    st.l *= alpha;
+    if (!fresh) {
+      st.l *= alpha;
 #pragma unroll
-    for (int d = 0; d < SH::ND; ++d) st.acc[d] *= alpha;
+      for (int d = 0; d < SH::ND; ++d) st.acc[d] *= alpha;
+    }
   }
   return (MASKED && st.m_ref == kNegInf) ? 0.f : st.m_ref;
 }
@@ -390,7 +395,9 @@ __device__ __forceinline__ void tile_probs(const f32x16& s, float sl2, float m_r
 // waves of the workgroup at the same point (it has barriers); kscr and mscr are
 // LDS buffers that no wave reads or loads into meanwhile.  On return the
 // half-0 wave holds, in the true-max basis, acc (unnormalised O^T), m (true row
-// max, log2 units, -inf for a row without keys) and l_row (full row sum).
+// max, log2 units, -inf for a row without keys) and l_row (full row sum).  Each
+// half's move from its lazy reference to its true max (corr) is folded into
+// the merge factors, so the accumulators are scaled once.
 template <int D, int BLK>
 __device__ __forceinline__ void merge_halves(RowState<D / 32>& st, float& m, float& l_row, float* kscr, float* mscr,
                                              int rg, int kh, int lane) {
@@ -400,8 +407,6 @@ __device__ __forceinline__ void merge_halves(RowState<D / 32>& st, float& m, flo
   const float corr = any ? __builtin_amdgcn_exp2f(st.m_ref - st.m_true) : 0.f;
   m = st.m_true;
   l_row = (st.l + other_half(st.l)) * corr;
-#pragma unroll
-  for (int d = 0; d < ND; ++d) st.acc[d] *= corr;
   const int l32 = lane & 31;
   float fa = 1.f, fb = 0.f;
 #pragma unroll
@@ -416,17 +421,23 @@ __device__ __forceinline__ void merge_halves(RowState<D / 32>& st, float& m, flo
                             st.acc[round * RB + i][4 * g + 2], st.acc[round * RB + i][4 * g + 3]};
           *(f32x4*)(kscr + (((rg * RB + i) * 4 + g) * 64 + lane) * 4) = v4;
         }
-      if (round == 0) mscr[rg * 64 + lane] = lane < 32 ? m : l_row;
+      // mscr layout: [row group][m of 32 rows | l of 32 rows | corr of 32 rows]
+      if (round == 0) {
+        mscr[rg * 96 + lane] = lane < 32 ? m : l_row;
+        if (lane < 32) mscr[rg * 96 + 64 + lane] = corr;
+      }
     }
     __syncthreads();
     if (kh == 0) {
       if (round == 0) {
-        const float mo = mscr[rg * 64 + l32], lo = mscr[rg * 64 + 32 + l32];
+        const float mo = mscr[rg * 96 + l32], lo = mscr[rg * 96 + 32 + l32], co = mscr[rg * 96 + 64 + l32];
         const float mn = fmaxf(m, mo);
         fa = mn == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - mn);
         fb = mn == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
         l_row = l_row * fa + lo * fb;
         m = mn;
+        fa *= corr;  // this half's accumulators are still relative to its lazy reference
+        fb *= co;    // and so are the other half's
       }
 #pragma unroll
       for (int i = 0; i < RB; ++i)
@@ -454,7 +465,7 @@ void attn_bf16_kernel(FwdArgs a) {
   static_assert(SH::NW * 64 == BLK * 4, "launch bounds");
   constexpr int NKB = SH::NKB, NB = SH::NKBW, ND = SH::ND, NKS = SH::NKS, NRG = SH::NRG;
   static_assert(SH::TILE * 2 >= NRG * SH::RB * 4096, "merge round must fit in a K buffer");
-  static_assert(SH::TILE * 2 >= NRG * 64 * 4, "merge statistics must fit in a V buffer");
+  static_assert(SH::TILE * 2 >= NRG * 96 * 4, "merge statistics must fit in a V buffer");
   // Four separate LDS arrays (not one indexed array): the compiler can then
   // prove that operand reads of one buffer do not alias the tile loads in
   // flight into another, and need not wait for those loads to land.
