@@ -261,6 +261,37 @@ def test_chunk_merge_against_oracle_with_empty_parts():
         G.assert_close(got_lse[fin], ref_lse[fin], (1e-5, 1e-6), "merge lse")
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 7, 9, 64])
+@pytest.mark.parametrize("D", [64, 128])
+def test_chunk_merge_part_counts(n, D):
+    """Part counts around the merge's groups of four reads (and the 64-part limit), with empty parts anywhere."""
+    rng = np.random.default_rng(100 + n + D)
+    rows = 777
+    O = rng.standard_normal((n, rows, D)).astype(np.float32)
+    M = (rng.standard_normal((n, rows)) * 4).astype(np.float32)
+    L = rng.uniform(0.25, 50, (n, rows)).astype(np.float32)
+    empty = rng.random((n, rows)) < 0.3
+    empty[:, 11] = True  # a row without any key
+    empty[0, 12] = True  # first part empty
+    empty[-1, 13] = True  # last part empty
+    M[empty] = -np.inf
+    L[empty] = 0
+    O[empty] = 0
+    ref, ref_lse = A.merge([(O[i], M[i], L[i]) for i in range(n)])
+    op, mp, lp = (torch.from_numpy(x).cuda() for x in (O, M, L))
+    out = torch.empty((rows, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    bd.chunk_merge([op[i] for i in range(n)], [mp[i] for i in range(n)], [lp[i] for i in range(n)], rows, D,
+                   out, "f32", lse)
+    torch.cuda.synchronize()
+    G.assert_close(G.to64(out), ref, (1e-5, 1e-6), f"merge n={n} D={D}")
+    got_lse = G.to64(lse)
+    assert np.isneginf(got_lse[11]) and (G.to64(out)[11] == 0).all()
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(got_lse), fin)
+    G.assert_close(got_lse[fin], ref_lse[fin], (1e-5, 1e-6), "merge lse")
+
+
 def test_trace_covers_every_item_once():
     w = W.make_custom(1, 4, 2048, 128, block=128, n_chunks=2, dtype="bf16", pattern="zipf", density=0.4, seed=3)
     q, k, v = G.upload(w)
