@@ -278,14 +278,19 @@ def main() -> int:
         bd.sparse_attn_fwd(plan, q, k, v, 0, C, o=out, trace=trace)
         torch.cuda.synchronize()
         result["per_cu_work"].update(per_cu_balance(trace.cpu().numpy()))
-        # fused (in-kernel chunk fold) forward and the merge alone
+        # fused (in-kernel chunk fold) forward and the merge alone; every timed loop below
+        # starts after one untimed launch of the same call (clock ramp after host work, an
+        # asynchronous plan's completion)
         reps = 10
+        bd.sparse_attn_fwd(plan, q, k, v, 0, C, o=out)
         e0.record(stream)
         for _ in range(reps):
             bd.sparse_attn_fwd(plan, q, k, v, 0, C, o=out)
         e1.record(stream)
         torch.cuda.synchronize()
         fused_ms = e0.elapsed_time(e1) / reps
+        bd.chunk_merge([o_part[c] for c in range(C)], [m_part[c] for c in range(C)], [l_part[c] for c in range(C)],
+                       rows, D, out, w.dtype)
         e0.record(stream)
         for _ in range(reps):
             bd.chunk_merge([o_part[c] for c in range(C)], [m_part[c] for c in range(C)], [l_part[c] for c in range(C)],
@@ -337,6 +342,7 @@ def main() -> int:
         alts += [("grid_id_order", "naive", n_items), ("grid_lpt_order", "lpt", n_items)]
         for alt, alt_order, alt_bins in alts:
             p_alt = bd.sparse_attn_plan(prob, "block", mask=mask, order=alt_order, num_bins=alt_bins)
+            bd.sparse_attn_fwd(p_alt, q, k, v, 0, C, o=out)
             e0.record(stream)
             for _ in range(reps):
                 bd.sparse_attn_fwd(p_alt, q, k, v, 0, C, o=out)
@@ -347,6 +353,7 @@ def main() -> int:
         # the same mask with token-level causality inside the live tiles
         p_tc = bd.sparse_attn_plan(bd.make_problem(q, w.block, C, w.layout, token_causal=True), "block",
                                    mask=mask, order=args.order)
+        bd.sparse_attn_fwd(p_tc, q, k, v, 0, C, o=out)
         e0.record(stream)
         for _ in range(reps):
             bd.sparse_attn_fwd(p_tc, q, k, v, 0, C, o=out)
