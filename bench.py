@@ -93,6 +93,20 @@ def cpu_baseline(w, n_heads: int):
                       f"{dt:.1f} s wall"}
 
 
+def peak_clock_mhz(device: int):
+    """The GPU's peak engine clock from the HIP runtime (hipDeviceAttributeClockRate, in kHz), or None."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        khz = ctypes.c_int(0)
+        hip_device_attribute_clock_rate = 5  # position of hipDeviceAttributeClockRate in hipDeviceAttribute_t
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), hip_device_attribute_clock_rate, device) != 0:
+            return None
+        return khz.value // 1000 or None
+    except OSError:
+        return None
+
+
 def per_cu_balance(trace: np.ndarray):
     """Busy time per compute unit (hardware XCC / SE / CU id of each item) and per workgroup."""
     start, end, hw, binitem = trace[:, 0], trace[:, 1], trace[:, 2], trace[:, 3]
@@ -362,8 +376,33 @@ def main() -> int:
         tc_ms = e0.elapsed_time(e1) / reps
         p_tc.close()
 
+        # the partial-mode forward with cold caches: a 512 MiB write first evicts the L2s and
+        # the Infinity Cache (256 MiB), so Q, K and V come from HBM (median of 3)
+        evict = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+        cold = []
+        for _ in range(3):
+            evict.fill_(1.0)
+            e0.record(stream)
+            bd.sparse_attn_fwd(plan, q, k, v, 0, C, o_part=o_part, m_part=m_part, l_part=l_part)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del evict
+        partial_cold_ms = float(np.median(cold))
+        # measured per-CU balance of the round-robin order, beside the step's planner above
+        p_naive = bd.sparse_attn_plan(prob, "block", mask=mask, order="naive")
+        tr_naive = torch.zeros((info["n_items"], 4), dtype=torch.int64, device=dev)
+        bd.sparse_attn_fwd(p_naive, q, k, v, 0, C, o=out, trace=tr_naive)
+        torch.cuda.synchronize()
+        naive_balance = per_cu_balance(tr_naive.cpu().numpy())
+        p_naive.close()
+        props = torch.cuda.get_device_properties(dev)
+        result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                            "compute_units": props.multi_processor_count, "peak_clock_mhz": peak_clock_mhz(dev.index or 0)}
+        result["per_cu_work"]["naive_measured_cu_max_over_mean"] = naive_balance["measured_cu_max_over_mean"]
         result["breakdown"] = {
             "plan_host_ms": round(plan_host_ms, 4), "fwd_partial_ms": round(kernel_ms, 4),
+            "fwd_partial_cold_ms": round(partial_cold_ms, 4),
             "fwd_fused_ms": round(fused_ms, 4), "fused_tflops": round(flop / fused_ms / 1e9, 2),
             "fused_pct_bf16_peak": round(100 * flop / fused_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
             "merge_ms": round(merge_ms, 4), "merge_gbs": round(merge_bytes / merge_ms / 1e6, 1),
