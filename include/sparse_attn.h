@@ -187,10 +187,11 @@ sa_status sparse_attn_fwd(const sa_plan* plan, const void* q, const void* k, con
                           int32_t chunk_begin, int32_t chunk_end, void* o, float* o_part,
                           float* m_part, float* l_part, int64_t* trace, hipStream_t stream);
 
-/* Online-softmax merge of n_parts partials (6D notes, section 2.1):
- *  m_new = max(m_acc, m_p); alpha = exp(m_acc - m_new); beta = exp(m_p - m_new);
- *  l = alpha*l + beta*l_p; O = alpha*O + beta*O_p; folded in part order, then
- *  O / l.  Parts with m_p = -inf are the identity and their O_p is not read.
+/* Online-softmax merge of n_parts partials (6D notes, section 2.1): per row,
+ *  the parts are taken in order into one running (O, m, l); at each step the
+ *  running maximum becomes the larger of m and m_p and both sides' O and l are
+ *  scaled by exp(their maximum - the new maximum) before they are added; the
+ *  result is O / l.  Parts with m_p = -inf add nothing and their O_p is not read.
  *  o_parts, m_parts, l_parts (host arrays of n_parts device pointers): O_p is
  *  fp32 [rows][D], m_p and l_p fp32 [rows].  o_out: [rows][D] dense in out_dtype.
  *  lse_out (nullable): fp32 [rows], m + log(l), -inf for empty rows.

@@ -17,13 +17,14 @@ Definitions followed:
   UNNORMALISED ``sum exp(s - m) v`` (the pseudocode marks the accumulator as
   unnormalised and divides once at the end).  Rows with no live key in the
   chunk give ``(O, m, l) = (0, -inf, 0)``.
-* Merge = the same section's online-softmax update, folded over the partials
-  in order, with the multiplication signs that the page lost restored:
-  ``m_new = max(m_acc, m_step)``, ``alpha = exp(m_acc - m_new)``,
-  ``beta = exp(m_step - m_new)``, ``l = alpha*l + beta*l_step``,
-  ``O = alpha*O + beta*O_step``; the result is ``O_acc / l_acc``.  The page is
-  silent on rows where both maxima are -inf; there ``alpha = beta = 0`` so the
-  state stays ``(0, -inf, 0)``.
+* Merge of partials over disjoint key sets (the same section's online-softmax
+  update, whose multiplication signs the page lost): every partial holds its
+  exponentials relative to its own maximum, so with ``M = max_p m_p`` the
+  combined row is ``sum_p exp(m_p - M) O_p / sum_p exp(m_p - M) l_p`` and its
+  log-sum-exp is ``M + log(sum_p exp(m_p - M) l_p)``.  The page folds the parts
+  one at a time; the fold reaches exactly this closed form, which is what is
+  written here.  Parts with ``m_p = -inf`` have weight 0; a row whose every
+  part is empty gives O = 0 and lse = -inf (the page is silent on such rows).
 * Token-level causality (option ``token_causal``): the mask above decides which
   tiles exist; inside them key j is also dropped for query i when ``j > i``
   (positions in the original sequence, also for striped chunks).  With an
@@ -133,15 +134,33 @@ def masked_attention(q, k, v, mask, block: int, scale: Optional[float] = None,
 
 
 def chunk_partial(q, k, v, mask, block: int, n_chunks: int, layout: str, c: int,
-                  scale: Optional[float] = None, token_causal: bool = False):
+                  scale: Optional[float] = None, token_causal: bool = False,
+                  rows: Optional[Sequence[Tuple[int, int, int]]] = None):
     """One ring step's partial ``(O_unnormalised, m, l)`` over the KV tokens of chunk ``c``.
 
-    Shapes: O [B, H, S, D], m and l [B, H, S], fp64.
+    Shapes: O [B, H, S, D], m and l [B, H, S], fp64; or [len(rows), D] and
+    [len(rows)] when ``rows`` (a list of (b, h, token)) selects individual rows.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, S, D = q.shape
     sc = default_scale(D) if scale is None else float(scale)
     toks = chunk_token_ids(S, block, n_chunks, layout, c)
+    if rows is not None:
+        O = np.zeros((len(rows), D))
+        M = np.full(len(rows), NEG_INF)
+        L = np.zeros(len(rows))
+        for n, (b, h, i) in enumerate(rows):
+            kt = toks[_key_live(mask[b, h, i // block], block, S)[toks]]
+            if token_causal:
+                kt = kt[kt <= i]
+            if kt.shape[0] == 0:
+                continue
+            s = sc * (k[b, h, kt] @ q[b, h, i])
+            M[n] = s.max()
+            p = np.exp(s - M[n])
+            L[n] = p.sum()
+            O[n] = p @ v[b, h, kt]
+        return O, M, L
     O = np.zeros((B, H, S, D))
     M = np.full((B, H, S), NEG_INF)
     L = np.zeros((B, H, S))
@@ -165,29 +184,23 @@ def chunk_partial(q, k, v, mask, block: int, n_chunks: int, layout: str, c: int,
 
 
 def merge(parts: List[Tuple[np.ndarray, np.ndarray, np.ndarray]]):
-    """Fold per-chunk partials ``[(O, m, l), ...]`` with the online-softmax update.
+    """Combine per-chunk partials ``[(O, m, l), ...]`` into the normalised result.
 
-    O: [..., D]; m, l: [...].  Returns ``(O_normalised, lse)``; rows whose every
-    partial is empty give O = 0 and lse = -inf.
+    O: [..., D]; m, l: [...].  Returns ``(O_normalised, lse)``: each partial is
+    weighted by ``exp(m_p - M)`` with ``M`` the largest of the parts' maxima; rows
+    whose every partial is empty give O = 0 and lse = -inf.
     """
-    O0, m0, _ = parts[0]
-    O_acc = np.zeros(np.shape(O0))
-    m_acc = np.full(np.shape(m0), NEG_INF)
-    l_acc = np.zeros(np.shape(m0))
-    for O_step, m_step, l_step in parts:
-        O_step, m_step, l_step = _f64(O_step), _f64(m_step), _f64(l_step)
-        m_new = np.maximum(m_acc, m_step)
-        empty = np.isneginf(m_new)  # both sides empty: alpha = beta = 0
-        m_ref = np.where(empty, 0.0, m_new)
-        alpha = np.where(empty, 0.0, np.exp(m_acc - m_ref))  # exp(-inf) = 0
-        beta = np.where(empty, 0.0, np.exp(m_step - m_ref))
-        l_acc = alpha * l_acc + beta * l_step
-        O_acc = alpha[..., None] * O_acc + beta[..., None] * O_step
-        m_acc = m_new
-    pos = l_acc > 0
-    O = np.where(pos[..., None], O_acc / np.where(pos, l_acc, 1.0)[..., None], 0.0)
+    m_all = np.stack([_f64(m) for _, m, _ in parts])  # [P, ...]
+    M = m_all.max(axis=0)
+    none = np.isneginf(M)
+    M_safe = np.where(none, 0.0, M)
+    weight = np.exp(m_all - M_safe)  # exp(-inf) = 0 for empty parts
+    den = sum(w * _f64(l) for w, (_, _, l) in zip(weight, parts))
+    num = sum(w[..., None] * _f64(O) for w, (O, _, _) in zip(weight, parts))
+    pos = den > 0
+    O = np.where(pos[..., None], num / np.where(pos, den, 1.0)[..., None], 0.0)
     with np.errstate(divide="ignore"):
-        lse = np.where(pos, m_acc + np.log(np.where(pos, l_acc, 1.0)), NEG_INF)
+        lse = np.where(pos, M_safe + np.log(np.where(pos, den, 1.0)), NEG_INF)
     return O, lse
 
 

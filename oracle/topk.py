@@ -4,13 +4,13 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  fp64 numpy.
 
 Follows the 6D-parallel notes, section 7.1 (DeepSeek Sparse Attention):
 
-1. indexer: a cheap low-rank importance ``I = (Q Wq)(K Wk)^T`` (the page's
-   ``low_rank_matmul``, "O(n^2) but the matrices are small");
-2. ``top_k`` keys per query by importance (``topk(...).indices``, shape
+1. indexer: importance of every (query, key) pair from low-rank projections,
+   ``I = (Q Wq)(K Wk)^T``; quadratic in the sequence length, but over rank-r
+   vectors, so cheap next to the attention it prunes;
+2. the ``top_k`` keys of each query by importance (an index array shaped
    [B, H, n, k]);
-3. gather K and V at those indices;
-4. scores ``q . k_sel``, softmax, weighted sum of ``v_sel`` — "standard
-   attention on the top-k only".
+3. K and V gathered at those indices;
+4. ordinary scaled softmax attention of each query over its selected keys.
 
 Readings where the page is silent:
 

@@ -1,9 +1,12 @@
-// Online-softmax merge of per-chunk partials (6D-parallel notes, section 2.1):
-// per row, fold the parts in order with m_new = max(m_acc, m_p),
-// alpha = exp(m_acc - m_new), beta = exp(m_p - m_new), l = alpha*l + beta*l_p,
-// O = alpha*O + beta*O_p, then divide by l.  A part with m_p = -inf is the
-// identity of the fold (alpha = 1, beta = 0), so it is skipped and its O_p is
-// never read; a row whose every part is empty yields O = 0, lse = -inf.
+// Online-softmax merge of per-chunk partials (6D-parallel notes, section 2.1).
+// Each part holds (O_p, m_p, l_p): its unnormalised output and row sum taken
+// relative to its own row maximum m_p.  A row keeps one running triple; taking
+// in the next part raises the running maximum to the larger of the two and
+// scales both sides' O and l by the exponential of their distance below it
+// before adding them.  After the last part the row is O / l, and
+// lse = m + log l.  A part with m_p = -inf contributes nothing, so it is
+// skipped and its O_p is never read; a row whose every part is empty yields
+// O = 0, lse = -inf.
 //
 // HBM-bound: D/4 threads per row, each folding one 16-byte fp32 vector per part.
 #include <hip/hip_runtime.h>

@@ -260,3 +260,69 @@ def test_merge_of_random_uneven_key_splits_equals_unchunked():
         assert np.abs(O - ref).max() < 1e-12
         fin = np.isfinite(ref_lse)
         assert np.array_equal(fin, np.isfinite(lse)) and np.abs(lse[fin] - ref_lse[fin]).max() < 1e-12
+
+
+@pytest.mark.parametrize("layout,token_causal,scale", [("contiguous", False, None), ("striped", False, 1.0),
+                                                        ("contiguous", True, 0.7), ("striped", True, None)])
+def test_chunk_partial_each_of_o_m_l_pure_python_loops(layout, token_causal, scale):
+    """Each of a chunk partial's O, m and l on its own, by a pure-Python loop over the chunk's
+    live keys: m is the row maximum over the keys of that chunk only (not over the Q-block or
+    the whole row), l = sum exp(s - m) and O = sum exp(s - m) v, unnormalised."""
+    S, D, blk, C = 32, 4, 8, 2
+    w = W.make_custom(1, 2, S, D, block=blk, pattern="bernoulli", density=0.6, dtype="f32", seed=17,
+                      layout=layout)
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    for c in range(C):
+        O, M, L = A.chunk_partial(w.q, w.k, w.v, w.mask, blk, C, layout, c, scale=scale,
+                                  token_causal=token_causal)
+        rows = [(0, h, i) for h in range(2) for i in range(S)]
+        Or, Mr, Lr = A.chunk_partial(w.q, w.k, w.v, w.mask, blk, C, layout, c, scale=scale,
+                                     token_causal=token_causal, rows=rows)
+        for n, (_, h, i) in enumerate(rows):
+            if layout == "contiguous":
+                keys = range(c * (S // C), (c + 1) * (S // C))
+            else:
+                keys = range(c, S, C)
+            keys = [j for j in keys if w.mask[0, h, i // blk, j // blk] and not (token_causal and j > i)]
+            if not keys:
+                assert M[0, h, i] == -math.inf and L[0, h, i] == 0 and (O[0, h, i] == 0).all()
+                assert Mr[n] == -math.inf and Lr[n] == 0 and (Or[n] == 0).all()
+                continue
+            s = [sc * sum(float(w.q[0, h, i, d]) * float(w.k[0, h, j, d]) for d in range(D)) for j in keys]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            for got_m, got_l, got_o in ((M[0, h, i], L[0, h, i], O[0, h, i]), (Mr[n], Lr[n], Or[n])):
+                assert abs(got_m - m) < 1e-12
+                assert abs(got_l - sum(e)) < 1e-12
+                for d in range(D):
+                    assert abs(got_o[d] - sum(e[t] * float(w.v[0, h, j, d]) for t, j in enumerate(keys))) < 1e-12
+
+
+def test_merge_equals_sequential_online_softmax_fold():
+    """The merge's closed form equals the 6D notes' one-part-at-a-time update (section 2.1,
+    with the lost multiplications restored), run here as a pure-Python loop, including empty
+    parts at the start, in the middle and at the end."""
+    rng = np.random.default_rng(23)
+    n_parts, rows, D = 5, 7, 3
+    O = rng.standard_normal((n_parts, rows, D))
+    m = rng.standard_normal((n_parts, rows)) * 3
+    l = rng.uniform(0.5, 4, (n_parts, rows))
+    for p, r in ((0, 1), (2, 1), (4, 1), (0, 2), (1, 2), (2, 2), (3, 2), (4, 2), (4, 5)):
+        O[p, r], m[p, r], l[p, r] = 0.0, -math.inf, 0.0
+    got, got_lse = A.merge([(O[p], m[p], l[p]) for p in range(n_parts)])
+    for r in range(rows):
+        acc_o, acc_m, acc_l = [0.0] * D, -math.inf, 0.0
+        for p in range(n_parts):
+            new_m = max(acc_m, m[p, r])
+            if new_m == -math.inf:
+                continue  # both sides hold nothing yet
+            a, b = math.exp(acc_m - new_m), math.exp(m[p, r] - new_m)
+            acc_l = a * acc_l + b * l[p, r]
+            acc_o = [a * acc_o[d] + b * O[p, r, d] for d in range(D)]
+            acc_m = new_m
+        if acc_l == 0:
+            assert (got[r] == 0).all() and got_lse[r] == -math.inf
+            continue
+        for d in range(D):
+            assert abs(got[r, d] - acc_o[d] / acc_l) < 1e-12
+        assert abs(got_lse[r] - (acc_m + math.log(acc_l))) < 1e-12
