@@ -143,6 +143,33 @@ def test_causal_striped_equals_contiguous_and_chunked(causal_w):
         del op, mp, lp
 
 
+def test_causal_bench_path_against_oracle(causal_w):
+    """bench.py's step exactly: the device-planned LPT order over the default bins, the
+    partial-mode forward over all 4 chunks, then chunk_merge.  Sampled rows of the merged output
+    and lse, and of every chunk partial (m, l, O / l), are compared with the oracle directly."""
+    w = causal_w
+    q, k, v = G.upload(w)
+    plan = G.plan_block(w, q, order="lpt_device")
+    C = w.n_chunks
+    op, mp, lp = G.run_partial(plan, q, k, v, 0, C)
+    om, lse = G.merge(op, mp, lp)
+    rows = G.sample_rows(w, 128, seed=7)
+    idx = tuple(np.array(rows).T)
+    ref, ref_lse = A.masked_attention(w.q, w.k, w.v, w.mask, w.block, rows=rows)
+    G.assert_close(G.to64(om)[idx], ref, G.BF16_TOL, "bench path merged")
+    G.assert_close(G.to64(lse)[idx], ref_lse, G.ROWSUM_TOL, "bench path lse")
+    for c in range(C):
+        Oc, Mc, Lc = A.chunk_partial(w.q, w.k, w.v, w.mask, w.block, C, w.layout, c, rows=rows)
+        got_m, got_l, got_o = G.to64(mp[c])[idx], G.to64(lp[c])[idx], G.to64(op[c])[idx]
+        assert np.array_equal(np.isneginf(got_m), np.isneginf(Mc))
+        fin = np.isfinite(Mc)
+        G.assert_close(got_m[fin], Mc[fin], (2e-3, 1e-4), f"m chunk {c}")
+        G.assert_close(got_l[fin] / Lc[fin], np.ones(fin.sum()), G.ROWSUM_TOL, f"l chunk {c}")
+        G.assert_close(got_o[fin] / got_l[fin][:, None], Oc[fin] / Lc[fin][:, None], G.BF16_TOL, f"O/l chunk {c}")
+        assert (got_o[~fin] == 0).all() and (got_l[~fin] == 0).all()
+    del op, mp, lp
+
+
 # ---------------------------------------------------------------- workload 4: skewed video
 
 def test_skewed_plan_full_and_chunked():

@@ -1,0 +1,26 @@
+"""The GPU rescale cases really take the bf16 kernel's online-softmax rescale branch.
+
+The kernel moves its exponent reference only when a row maximum grows by more than 8 log2
+units, so N(0,1) inputs at the default scale never rescale a non-empty state (checked here on
+a small causal case).  Every case of ``tests/lazy_rescale.RESCALE_CASES`` must rescale rows in
+both full mode and partial mode (where the state restarts at every chunk), by the CPU replay of
+the kernel's rule.
+"""
+import pytest
+
+from sparse_mask_load_amd import workloads as W
+from tests import lazy_rescale as LR
+
+
+@pytest.mark.parametrize("n", range(len(LR.RESCALE_CASES)), ids=[LR.rescale_case_id(c) for c in LR.RESCALE_CASES])
+def test_case_crosses_the_rescale_threshold(n):
+    w, scale, tc = LR.make_rescale_case(n)
+    for full in (True, False):
+        events = LR.count_rescales(w, scale, full=full, token_causal=tc)
+        assert events >= 100, f"case {n} full={full}: only {events} rescales of a non-empty row"
+
+
+def test_default_scale_inputs_do_not_rescale():
+    w = W.make_custom(1, 2, 2048, 128, block=128, n_chunks=4, pattern="causal", seed=105, layout="striped")
+    assert LR.count_rescales(w, None, full=True) == 0
+    assert LR.count_rescales(w, None, full=False) == 0
