@@ -713,13 +713,359 @@ void attn_bf16_kernel(FwdArgs a) {
   }
 }
 
+// Probabilities of one 32-key block that wait for their P V product, with the
+// reference they were taken against.
+struct PBlock {
+  bf16x8 p[2];  // B operands of O^T += V^T P^T: keys 16*half + 8*h2 + 0..7
+  float ref;    // reference subtracted in the exponent (log2 units)
+  float lsum;   // this lane's share of the block's row sum of the rounded P
+};
+
+// One 32-key block's step of the online softmax for rows whose scores are all
+// finite: the block's row max (both half-waves), its fold into the running
+// true max, the lazy move of the reference (a row whose block max exceeds its
+// reference by more than the slack takes its running max) and the block's
+// rounded probabilities with their row sum.  Returns the ballot of the rows
+// whose reference moved.
+__device__ __forceinline__ uint64_t block_softmax(const f32x16& s, float sl2, float& ref, float& m_true,
+                                                  PBlock& pb) {
+  float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
+  float b = fmaxf(fmaxf(s[8], s[9]), s[10]);
+  a = fmaxf(fmaxf(a, s[3]), s[4]);
+  b = fmaxf(fmaxf(b, s[11]), s[12]);
+  a = fmaxf(fmaxf(a, s[5]), s[6]);
+  b = fmaxf(fmaxf(b, s[13]), s[14]);
+  float mx = fmaxf(fmaxf(a, s[7]), fmaxf(b, s[15]));
+  mx = fmaxf(mx, other_half(mx)) * sl2;
+  m_true = fmaxf(m_true, mx);
+  const bool up = mx > ref + kRescaleSlack;
+  ref = up ? m_true : ref;
+  pb.ref = ref;
+  float l0 = 0.f, l1 = 0.f;
+  tile_probs(s, sl2, ref, pb.p, l0, l1);
+  pb.lsum = l0 + l1;
+  return __builtin_amdgcn_ballot_w64(up);
+}
+
+// Full-tile kernel for 128-key blocks (contiguous chunks, S a multiple of the
+// block, no token-level causality), software-pipelined per 32-key block.  The
+// wave's work is a stream of blocks b (two per tile): the S MFMAs of block
+// b+2 and the P V MFMAs of block b issue while the vector units take block
+// b+1's row max and exponentials, so neither waits for the other.  The
+// reference max therefore moves per block, one block ahead of the P V product
+// that consumes it; before block b's P V the accumulators are brought to
+// block b's reference (a rescale only when some row's reference moved, which
+// the lazy rule makes rare).  MFMA operands are read from LDS a few MFMAs
+// ahead of their use, in the order given by the scheduling groups at the end
+// of each section.
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_pipe_kernel(FwdArgs a) {
+  constexpr int BLK = 128;
+  using SH = Shape<D, BLK>;
+  constexpr int NB = SH::NKBW, ND = SH::ND, NKS = SH::NKS, NRG = SH::NRG;
+  static_assert(NB == 2, "two 32-key blocks per wave and tile");
+  static_assert(SH::NW * 64 == 512, "launch bounds");
+  static_assert(SH::TILE * 2 >= NRG * SH::RB * 4096, "merge round must fit in a K buffer");
+  static_assert(SH::TILE * 2 >= NRG * 96 * 4, "merge statistics must fit in a V buffer");
+  constexpr int NOPS = NKS + 2 * ND;  // MFMAs of one section: S of one block, then P V of one block
+  constexpr int AHEAD = 4;            // operands read this many MFMAs ahead
+  constexpr int LPS = SH::IPW;        // tile-load instructions per section (K and V slices)
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[SH::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[SH::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[SH::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[SH::TILE];
+  __shared__ int sList[kMaxTilesPerRow];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave % NRG, kh = wave / NRG;
+  const int kb0 = kh * NB;
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const bool full = a.o != nullptr;
+  TileLoader<D, BLK> loader;
+  loader.init(wave, lane);
+  loader.set_stride((int)a.ss);
+  OperandLanes<D, true> ol;
+  ol.init(lane, kb0);
+  const bf16* __restrict__ gQ = (const bf16*)a.q;
+  const bf16* __restrict__ gK = (const bf16*)a.k;
+  const bf16* __restrict__ gV = (const bf16*)a.v;
+  const int bin = blockIdx.x;
+  const int p_begin = a.bin_ptr[bin], p_end = a.bin_ptr[bin + 1];
+  const float sl2 = a.scale_log2;
+
+  for (int pos = p_begin; pos < p_end; ++pos) {
+    const int64_t t_start = realtime_now();
+    const int item = a.items[pos];
+    const int qb = item % a.nQ;
+    const int bh = item / a.nQ;
+    const int b = bh / a.H, h = bh % a.H;
+    const int64_t bh_base = (int64_t)b * a.sb + (int64_t)h * a.sh;
+    const int qrow = qb * BLK + rg * 32 + l32;
+
+    bf16x8 qf[NKS];
+    {
+      const bf16* qp = gQ + bh_base + (int64_t)qrow * a.ss + 8 * h2;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
+    }
+
+    __syncthreads();  // every wave is done with the previous item's list, tiles and merge buffers
+    const int n_tiles = build_tile_list(a.mask + (int64_t)item * a.nK, a.nK, a.n_chunks, SA_LAYOUT_CONTIGUOUS, a.c0,
+                                        a.c1, sList, wave == 0);
+    __syncthreads();
+
+    RowState<ND> st;  // acc and l relative to st.m_ref (the reference of the last consumed block)
+    reset(st);
+    int cur_chunk = a.c0;
+
+    // Same flush as the general kernel: merge the key halves, write chunk
+    // `chunk`'s partial through the staging buffers, reset the state.
+    auto flush_partial = [&](int chunk, float* kscr, float* mscr) {
+      constexpr int CH = D / 4;
+      constexpr int HALF = BLK / 2;
+      constexpr int RPS = 64 / CH;
+      constexpr int NST = BLK / SH::NW / RPS;
+      static_assert(HALF * D * 4 <= SH::TILE * 2, "staging half must fit in a tile buffer");
+      static_assert(NST * RPS * SH::NW == BLK, "store rows must cover the block");
+      float m, l_row;
+      merge_halves<D, BLK>(st, m, l_row, kscr, mscr, rg, kh, lane);
+      const int64_t prow0 = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK;
+      if (kh == 0) {
+        const int r = rg * 32 + l32;
+        float* const rowp = (rg * 32 < HALF ? kscr : mscr) + (r % HALF) * D;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = 8 * d + 2 * g + h2;
+            const f32x4 v4 = {st.acc[d][4 * g], st.acc[d][4 * g + 1], st.acc[d][4 * g + 2], st.acc[d][4 * g + 3]};
+            *(f32x4*)(rowp + 4 * (c ^ (r & (CH - 1)))) = v4;
+          }
+        if (h2 == 0) {
+          a.m_part[prow0 + r] = m == kNegInf ? kNegInf : m * kLn2;
+          a.l_part[prow0 + r] = l_row;
+        }
+      }
+      __syncthreads();
+      {
+        const float* const buf = (wave * NST * RPS < HALF ? kscr : mscr);
+        const int c = lane % CH;
+#pragma unroll 1
+        for (int i = 0; i < NST; ++i) {
+          const int r = (wave * NST + i) * RPS + lane / CH;
+          const f32x4 v4 = *(const f32x4*)(buf + (r % HALF) * D + 4 * (c ^ (r & (CH - 1))));
+          *(f32x4*)(a.o_part + (prow0 + r) * D + 4 * c) = v4;
+        }
+      }
+      __syncthreads();
+      reset(st);
+    };
+    auto src_of = [&](int desc) { return tile_source(desc, bh_base, a.ss, a.S, SA_LAYOUT_CONTIGUOUS, a.n_chunks, BLK); };
+    auto chunk_of = [&](int desc) { return (desc >> kDescChunkShift) & 63; };
+
+    f32x16 sc[NB];       // scores of the two blocks of the next tile to be exponentiated
+    PBlock pb[NB];       // probabilities waiting for their P V product
+    uint64_t moved[NB];  // rows whose reference moved with that block
+    float ref_cur = kNegInf;  // reference of the latest block exponentiated
+    float m_next = kNegInf;   // running max of a chunk that starts with the next tile (partial mode)
+    if (n_tiles > 0) {
+      const int d0 = __builtin_amdgcn_readfirstlane(sList[0]);
+      loader.template issue<false>(gK, src_of(d0), sK0, wave);
+      loader.template issue<false>(gV, src_of(d0), sV0, wave);
+      if (n_tiles > 1) loader.template issue<false>(gK, src_of(__builtin_amdgcn_readfirstlane(sList[1])), sK1, wave);
+      wait_vm();
+      __syncthreads();
+      tile_scores<D, BLK, false>(sK0, qf, ol, 0, sc);
+      // block 0 starts an accumulation: its running max goes to m_next, which
+      // the first tile takes over (after flushing any empty leading chunks)
+      moved[0] = block_softmax(sc[0], sl2, ref_cur, m_next, pb[0]);
+    }
+
+    // Brings the accumulators and row sum to the reference of block pb, then
+    // adds the block's row sum (its P V follows).
+    auto consume = [&](const PBlock& p, uint64_t mv) {
+      if (mv) {
+        const float alpha = __builtin_amdgcn_exp2f(st.m_ref - p.ref);
+        st.l *= alpha;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) st.acc[d] *= alpha;
+      }
+      st.m_ref = p.ref;
+      st.l += p.lsum;
+    };
+
+    auto tile = [&](int t, auto parity) {
+      constexpr int P = decltype(parity)::value;
+      bf16* const kfree = P ? sK1 : sK0;
+      bf16* const vfree = P ? sV0 : sV1;
+      const bf16* const Kt1 = P ? sK0 : sK1;
+      const bf16* const Vt = P ? sV1 : sV0;
+      const int desc = __builtin_amdgcn_readfirstlane(sList[t]);
+      const bool has_next = t + 1 < n_tiles;
+      const int desc1 = has_next ? __builtin_amdgcn_readfirstlane(sList[t + 1]) : desc;
+      // the next tile starts a new accumulation (a chunk of its own in partial mode)
+      const bool next_new = !full && has_next && chunk_of(desc1) != chunk_of(desc);
+
+      wait_vm();
+      __syncthreads();
+      bool fresh = t == 0;  // block 0 of this tile opens an accumulation
+      if (!full && cur_chunk < chunk_of(desc)) {
+        while (cur_chunk < chunk_of(desc)) flush_partial(cur_chunk++, (float*)kfree, (float*)vfree);
+        fresh = true;
+      }
+      if (fresh) st.m_true = m_next;
+      const TileSrc srcK = src_of(__builtin_amdgcn_readfirstlane(sList[min(t + 2, n_tiles - 1)]));
+      const TileSrc srcV = src_of(desc1);
+
+      // The tile's MFMA stream: section j = S of block j of tile t+1 (NKS MFMAs, K
+      // fragments), then P V of block j of tile t (2*ND MFMAs, V^T fragments).
+      bf16x8 fr[2 * NOPS];
+      auto rd = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int j = i / NOPS, k = i % NOPS;
+        if constexpr (k < NKS)
+          fr[i] = ol.k_frag(Kt1, j, k);
+        else
+          fr[i] = ol.v_frag(Vt, j, (k - NKS) / ND, (k - NKS) % ND);
+      };
+      auto mm = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int j = i / NOPS, k = i % NOPS;
+        if constexpr (k < NKS) {
+          sc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], qf[k], k == 0 ? f32x16{} : sc[j], 0, 0, 0);
+        } else {
+          constexpr int half = (k - NKS) / ND, d = (k - NKS) % ND;
+          st.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pb[j].p[half], st.acc[d], 0, 0, 0);
+        }
+      };
+      static_for<AHEAD>([&](auto ic) { rd(ic); });
+
+      static_for<NB>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        consume(pb[j], moved[j]);
+        // vector work of this section, in stages: block 1 of tile t (section 0), or
+        // block 0 of tile t+1 (section 1, on the scores of section 0's S MFMAs)
+        constexpr int SRC = j == 0 ? 1 : 0;
+        const f32x16& s = sc[SRC];
+        PBlock& out = pb[SRC];
+        float mx_a, mx_b, mx, run, l0, l1;
+        auto stage = [&](auto sc_) {
+          constexpr int g = decltype(sc_)::value;
+          if constexpr (g == 0) {
+            mx_a = fmaxf(fmaxf(s[0], s[1]), s[2]);
+            mx_a = fmaxf(fmaxf(mx_a, s[3]), s[4]);
+            mx_a = fmaxf(fmaxf(mx_a, s[5]), s[6]);
+          } else if constexpr (g == 1) {
+            mx_b = fmaxf(fmaxf(s[8], s[9]), s[10]);
+            mx_b = fmaxf(fmaxf(mx_b, s[11]), s[12]);
+            mx_b = fmaxf(fmaxf(mx_b, s[13]), s[14]);
+            mx = fmaxf(fmaxf(mx_a, s[7]), fmaxf(mx_b, s[15]));
+          } else if constexpr (g == 2) {
+            mx = fmaxf(mx, other_half(mx)) * sl2;
+          } else if constexpr (g == 3) {
+            if constexpr (j == 0) {
+              run = st.m_true;
+            } else {
+              ref_cur = next_new ? kNegInf : ref_cur;
+              run = next_new ? kNegInf : st.m_true;
+            }
+            run = fmaxf(run, mx);
+            const bool up = mx > ref_cur + kRescaleSlack;
+            ref_cur = up ? run : ref_cur;
+            out.ref = ref_cur;
+            moved[SRC] = __builtin_amdgcn_ballot_w64(up);
+            if constexpr (j == 0) {
+              st.m_true = run;
+            } else {
+              m_next = run;
+              st.m_true = (has_next && !next_new) ? run : st.m_true;
+            }
+            l0 = 0.f;
+            l1 = 0.f;
+          } else if constexpr (g < 12) {
+            constexpr int r = 2 * (g - 4);
+            out.p[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[r], sl2, -ref_cur));
+            out.p[r >> 3][(r & 7) + 1] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[r + 1], sl2, -ref_cur));
+          } else {
+            constexpr int h = g - 12;
+            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+            float& acc_l = h ? l1 : l0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc_l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{out.p[h][2 * e], out.p[h][2 * e + 1]}, ones, acc_l, false);
+            if constexpr (h == 1) out.lsum = l0 + l1;
+          }
+        };
+        constexpr int NSTAGE = 14;
+        constexpr int SPS = (NSTAGE + NOPS - 1) / NOPS;  // stages per MFMA slot
+        static_for<NOPS>([&](auto kc) {
+          constexpr int k = decltype(kc)::value, i = j * NOPS + k;
+          if constexpr (i + AHEAD < 2 * NOPS) rd(std::integral_constant<int, i + AHEAD>{});
+          mm(std::integral_constant<int, i>{});
+          static_for<SPS>([&](auto uc) {
+            constexpr int g = k * SPS + decltype(uc)::value;
+            if constexpr (g < NSTAGE) stage(std::integral_constant<int, g>{});
+          });
+          if constexpr (k < LPS / 2) {
+            loader.template issue<false, j * LPS / 2 + k, j * LPS / 2 + k + 1>(gK, srcK, kfree, wave);
+            loader.template issue<false, j * LPS / 2 + k, j * LPS / 2 + k + 1>(gV, srcV, vfree, wave);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        // keep the section's vector results in this section (they are consumed one
+        // section later)
+        asm volatile("" : "+v"(out.p[0]), "+v"(out.p[1]), "+v"(out.lsum), "+v"(out.ref), "+v"(ref_cur));
+      });
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+      tile(t, std::integral_constant<int, 0>{});
+      if (t + 1 < n_tiles) tile(t + 1, std::integral_constant<int, 1>{});
+    }
+
+    wait_vm();
+    __syncthreads();
+    if (!full) {
+      while (cur_chunk < a.c1) flush_partial(cur_chunk++, (float*)sK0, (float*)sV0);
+    } else {
+      float m, l_row;
+      merge_halves<D, BLK>(st, m, l_row, (float*)sK0, (float*)sV0, rg, kh, lane);
+      const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+      if (kh == 0) {
+        bf16* op = (bf16*)a.o + bh_base + (int64_t)qrow * a.ss;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const bf16x4 v4 = {(bf16)(st.acc[d][4 * g] * inv), (bf16)(st.acc[d][4 * g + 1] * inv),
+                               (bf16)(st.acc[d][4 * g + 2] * inv), (bf16)(st.acc[d][4 * g + 3] * inv)};
+            *(bf16x4*)(op + d * 32 + 8 * g + 4 * h2) = v4;
+          }
+      }
+    }
+    if (a.trace && tid == 0) {
+      int64_t* tr = a.trace + (int64_t)pos * 4;
+      tr[0] = t_start;
+      tr[1] = realtime_now();
+      tr[2] = hw_location();
+      tr[3] = ((int64_t)bin << 32) | (int64_t)(uint32_t)item;
+    }
+  }
+}
+
 template <int D, int BLK>
 hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
   const bool general = a.layout == SA_LAYOUT_STRIPED || a.S % BLK != 0;
   const dim3 grid(a.num_bins), block(Shape<D, BLK>::NW * 64);
   if (general)
     hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, true, false>), grid, block, 0, stream, a);
-  else if (a.token_causal)
+  else if constexpr (BLK == 128) {
+    if (a.token_causal)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_bf16_pipe_kernel<D>), grid, block, 0, stream, a);
+  } else if (a.token_causal)
     hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false, true>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false, false>), grid, block, 0, stream, a);
