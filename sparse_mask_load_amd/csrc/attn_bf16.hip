@@ -113,6 +113,13 @@ __device__ __forceinline__ float other_half(float x) {
   return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// The value of x, opaque to the compiler: computations derived from it stay
+// where they are written instead of being hoisted (and kept live) elsewhere.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Where the rows of one K/V tile live in global memory: row r of the tile is
@@ -536,8 +543,10 @@ void attn_bf16_kernel(FwdArgs a) {
       constexpr int NST = BLK / SH::NW / RPS;  // store instructions per wave
       static_assert(HALF * D * 4 <= SH::TILE * 2, "staging half must fit in a tile buffer");
       static_assert(NST * RPS * SH::NW == BLK, "store rows must cover the block");
+      // lane-derived addresses are formed here, not kept live across the tile loop
+      const int ln = opaque(lane), l32 = ln & 31, h2 = ln >> 5;
       float m, l_row;
-      merge_halves<D, BLK>(st, m, l_row, kscr, mscr, rg, kh, lane);
+      merge_halves<D, BLK>(st, m, l_row, kscr, mscr, rg, kh, ln);
       const int64_t prow0 = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK;
       if (kh == 0) {
         const int r = rg * 32 + l32;  // a wave's 32 rows lie in one staging buffer
@@ -559,10 +568,10 @@ void attn_bf16_kernel(FwdArgs a) {
       {
         // rows [wave*NST*RPS, (wave+1)*NST*RPS) of one staging buffer
         const float* const buf = (wave * NST * RPS < HALF ? kscr : mscr);
-        const int c = lane % CH;
+        const int c = ln % CH;
 #pragma unroll 1
         for (int i = 0; i < NST; ++i) {
-          const int r = (wave * NST + i) * RPS + lane / CH;
+          const int r = (wave * NST + i) * RPS + ln / CH;
           const f32x4 v4 = *(const f32x4*)(buf + (r % HALF) * D + 4 * (c ^ (r & (CH - 1))));
           if (qb * BLK + r < a.S) *(f32x4*)(a.o_part + (prow0 + r) * D + 4 * c) = v4;
         }
@@ -688,8 +697,9 @@ void attn_bf16_kernel(FwdArgs a) {
     if (!full) {
       while (cur_chunk < a.c1) flush_partial(cur_chunk++, (float*)sK0, (float*)sV0);
     } else {
+      const int ln = opaque(lane), h2 = ln >> 5;
       float m, l_row;
-      merge_halves<D, BLK>(st, m, l_row, (float*)sK0, (float*)sV0, rg, kh, lane);
+      merge_halves<D, BLK>(st, m, l_row, (float*)sK0, (float*)sV0, rg, kh, ln);
       const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
       if (kh == 0 && qrow < a.S) {
         bf16* op = (bf16*)a.o + bh_base + (int64_t)qrow * a.ss;
@@ -781,7 +791,6 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave % NRG, kh = wave / NRG;
   const int kb0 = kh * NB;
-  const int h2 = lane >> 5, l32 = lane & 31;
   const bool full = a.o != nullptr;
   TileLoader<D, BLK> loader;
   loader.init(wave, lane);
@@ -802,11 +811,11 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
     const int bh = item / a.nQ;
     const int b = bh / a.H, h = bh % a.H;
     const int64_t bh_base = (int64_t)b * a.sb + (int64_t)h * a.sh;
-    const int qrow = qb * BLK + rg * 32 + l32;
+    const int qrow = qb * BLK + rg * 32 + (lane & 31);
 
     bf16x8 qf[NKS];
     {
-      const bf16* qp = gQ + bh_base + (int64_t)qrow * a.ss + 8 * h2;
+      const bf16* qp = gQ + bh_base + (int64_t)qrow * a.ss + 8 * (lane >> 5);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
     }
@@ -829,8 +838,10 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       constexpr int NST = BLK / SH::NW / RPS;
       static_assert(HALF * D * 4 <= SH::TILE * 2, "staging half must fit in a tile buffer");
       static_assert(NST * RPS * SH::NW == BLK, "store rows must cover the block");
+      // lane-derived addresses are formed here, not kept live across the tile loop
+      const int ln = opaque(lane), l32 = ln & 31, h2 = ln >> 5;
       float m, l_row;
-      merge_halves<D, BLK>(st, m, l_row, kscr, mscr, rg, kh, lane);
+      merge_halves<D, BLK>(st, m, l_row, kscr, mscr, rg, kh, ln);
       const int64_t prow0 = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK;
       if (kh == 0) {
         const int r = rg * 32 + l32;
@@ -851,10 +862,10 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       __syncthreads();
       {
         const float* const buf = (wave * NST * RPS < HALF ? kscr : mscr);
-        const int c = lane % CH;
+        const int c = ln % CH;
 #pragma unroll 1
         for (int i = 0; i < NST; ++i) {
-          const int r = (wave * NST + i) * RPS + lane / CH;
+          const int r = (wave * NST + i) * RPS + ln / CH;
           const f32x4 v4 = *(const f32x4*)(buf + (r % HALF) * D + 4 * (c ^ (r & (CH - 1))));
           *(f32x4*)(a.o_part + (prow0 + r) * D + 4 * c) = v4;
         }
@@ -1029,8 +1040,9 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
     if (!full) {
       while (cur_chunk < a.c1) flush_partial(cur_chunk++, (float*)sK0, (float*)sV0);
     } else {
+      const int ln = opaque(lane), h2 = ln >> 5;
       float m, l_row;
-      merge_halves<D, BLK>(st, m, l_row, (float*)sK0, (float*)sV0, rg, kh, lane);
+      merge_halves<D, BLK>(st, m, l_row, (float*)sK0, (float*)sV0, rg, kh, ln);
       const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
       if (kh == 0) {
         bf16* op = (bf16*)a.o + bh_base + (int64_t)qrow * a.ss;
