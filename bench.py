@@ -18,7 +18,14 @@ rank-32 indexer, top-k 512, causal): the TOPK plan (projections + importance + p
 top-k) and the gather attention over the selected keys, reported as times and rates.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode merged|fused]
-       [--workload causal|video|skewed|tiny] [--no-cpu-baseline] [--calibrate-copy MiB]
+       [--workload causal|video|skewed|tiny] [--layout contiguous|striped] [--no-cpu-baseline]
+       [--no-extras] [--no-workloads] [--no-topk] [--calibrate-copy MiB]
+
+Each step's plan is destroyed inside the timed loop right after the next step is issued (the
+library returns its buffers to a cache and reuses them once the kernels that read them are done,
+so no step allocates or synchronises).  The untimed extras also time the other block-sparse
+workloads: the causal one in the other chunk layout, the video and the skewed workload, each as a
+whole step and in LPT and round-robin order with measured per-CU balance.
 Prints one JSON line.  Only one GPU is used: --gpus > 1 exits with a message.
 """
 from __future__ import annotations
@@ -171,12 +178,152 @@ def topk_path(bd, W, torch, dev, reps: int = 5) -> dict:
     }
 
 
+class WorkloadRun:
+    """One block-sparse workload resident on the GPU: Q, K, V, mask, chunk partials, output."""
+
+    def __init__(self, bd, torch, dev, w, layout=None):
+        self.bd, self.torch, self.w = bd, torch, w
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.q, self.k, self.v = (torch.from_numpy(x).to(dev, dt) for x in (w.q, w.k, w.v))
+        self.mask = torch.from_numpy(w.mask).to(dev)
+        self.layout = layout or w.layout
+        B, H, S, D = self.q.shape
+        C = w.n_chunks
+        self.B, self.H, self.S, self.D, self.C = B, H, S, D, C
+        self.prob = bd.make_problem(self.q, w.block, C, self.layout)
+        self.o_part = torch.empty((C, B, H, S, D), dtype=torch.float32, device=dev)
+        self.m_part = torch.empty((C, B, H, S), dtype=torch.float32, device=dev)
+        self.l_part = torch.empty((C, B, H, S), dtype=torch.float32, device=dev)
+        self.out = torch.empty_like(self.q)
+        self.rows = B * H * S
+
+    def plan(self, order, bins=0, stream=None, prob=None):
+        return self.bd.sparse_attn_plan(prob or self.prob, "block", mask=self.mask, order=order, num_bins=bins,
+                                        stream=stream)
+
+    def fwd_partial(self, plan):
+        self.bd.sparse_attn_fwd(plan, self.q, self.k, self.v, 0, self.C, o_part=self.o_part, m_part=self.m_part,
+                                l_part=self.l_part)
+
+    def fwd_fused(self, plan, trace=None):
+        self.bd.sparse_attn_fwd(plan, self.q, self.k, self.v, 0, self.C, o=self.out, trace=trace)
+
+    def merge(self):
+        C = self.C
+        self.bd.chunk_merge([self.o_part[c] for c in range(C)], [self.m_part[c] for c in range(C)],
+                            [self.l_part[c] for c in range(C)], self.rows, self.D, self.out, self.w.dtype)
+
+    def merge_bytes(self):
+        """HBM bytes the merge moves: m and l of every part, O of the parts whose row has a key
+        (the merge skips O of empty parts), and the output written once."""
+        nonempty = int(self.torch.isfinite(self.m_part).sum().item())
+        out_b = 2 if self.w.dtype == "bf16" else 4
+        return self.rows * self.C * 8 + nonempty * self.D * 4 + self.rows * self.D * out_b
+
+    def flop(self, total_live):
+        return 4.0 * self.w.block * self.w.block * self.D * total_live
+
+    def timed(self, fn, reps):
+        """Mean time of fn() over reps launches (HIP events on the current stream, one untimed launch first)."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def steps(self, order, n, warmup=2):
+        """ms per whole step (plan on a side stream, partial forward, merge), the previous step's plan
+        destroyed inside the loop, and the forward's mean time from HIP events."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        plan_stream = torch.cuda.Stream()
+        fwd = []
+
+        def one(record):
+            plan = self.plan(order, stream=plan_stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            self.fwd_partial(plan)
+            e1.record(stream)
+            self.merge()
+            if record:
+                fwd.append((e0, e1))
+            return plan
+
+        prev = None
+        for _ in range(warmup):
+            p = one(False)
+            if prev is not None:
+                prev.close()
+            prev = p
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            p = one(True)
+            prev.close()  # the previous step's plan: its buffers are reused once its kernels are done
+            prev = p
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        prev.close()
+        return (t1 - t0) * 1e3 / n, float(np.mean([a.elapsed_time(b) for a, b in fwd]))
+
+    def order_summary(self, order, reps):
+        """Fused and partial forward time of one work order, its planned and measured per-CU balance."""
+        bd, torch = self.bd, self.torch
+        p = self.plan(order)
+        info = bd.sparse_attn_plan_info(p)
+        bl = bd.sparse_attn_plan_copy(p, bd.SA_PLAN_BIN_LOAD, info["num_bins"])
+        trace = torch.zeros((info["n_items"], 4), dtype=torch.int64, device=self.q.device)
+        self.fwd_fused(p, trace=trace)
+        torch.cuda.synchronize()
+        bal = per_cu_balance(trace.cpu().numpy())
+        fused = self.timed(lambda: self.fwd_fused(p), reps)
+        partial = self.timed(lambda: self.fwd_partial(p), reps)
+        p.close()
+        return {"fwd_fused_ms": round(fused, 4), "fwd_partial_ms": round(partial, 4),
+                "fused_tflops": round(self.flop(info["total_live"]) / fused / 1e9, 2),
+                "planned_makespan_tiles": info["makespan"], "lower_bound_tiles": info["lower_bound"],
+                "planned_bin_max_over_mean": round(float(bl.max() / bl.mean()), 4),
+                "measured_cu_max_over_mean": round(bal["measured_cu_max_over_mean"], 4)}
+
+
+def workload_summary(bd, W, torch, dev, cfg, layout="contiguous", steps=10, reps=5):
+    """Untimed extra: another workload's whole step (device plan, partial forward over every chunk,
+    merge) and its forward in device-planned LPT, host LPT and round-robin order."""
+    w = W.make(cfg, layout=layout)
+    run = WorkloadRun(bd, torch, dev, w)
+    p = run.plan("lpt_device")
+    info = bd.sparse_attn_plan_info(p)
+    p.close()
+    flop = run.flop(info["total_live"])
+    step_ms, fwd_ms = run.steps("lpt_device", steps)
+    merge_ms = run.timed(run.merge, reps)
+    out = {"workload": f"{w.name} B{run.B} H{run.H} S{run.S} d{run.D} block {w.block}, {run.C} {layout} chunks",
+           "live_tiles": info["total_live"], "flop": flop,
+           "ms_per_step": round(step_ms, 4), "step_tflops": round(flop / step_ms / 1e9, 2),
+           "step_pct_bf16_peak": round(100 * flop / step_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+           "fwd_partial_ms": round(fwd_ms, 4), "fwd_partial_tflops": round(flop / fwd_ms / 1e9, 2),
+           "merge_ms": round(merge_ms, 4), "merge_gbs": round(run.merge_bytes() / merge_ms / 1e6, 1),
+           "by_order": {o: run.order_summary(o, reps) for o in ("lpt_device", "lpt", "naive")}}
+    del run
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="causal")
+    ap.add_argument("--layout", choices=["contiguous", "striped"], default="contiguous",
+                    help="KV chunk layout: contiguous blocks, or striped (token i in chunk i mod C)")
     ap.add_argument("--mode", choices=["merged", "fused"], default="merged",
                     help="merged: partial chunks + chunk_merge (default); fused: chunks folded in-kernel")
     ap.add_argument("--order", choices=["lpt_xcd", "lpt", "naive", "lpt_device"], default="lpt_device",
@@ -187,6 +334,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the untimed breakdown runs")
     ap.add_argument("--no-topk", action="store_true", help="skip the token top-k path measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other block-sparse workloads (striped causal, video, skewed)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -208,18 +357,11 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    w = W.make(WORKLOADS[args.workload])
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    q, k, v = (torch.from_numpy(x).to(dev, dt) for x in (w.q, w.k, w.v))
-    mask = torch.from_numpy(w.mask).to(dev)
-    B, H, S, D = q.shape
-    C = w.n_chunks
-    prob = bd.make_problem(q, w.block, C, w.layout)
-    o_part = torch.empty((C, B, H, S, D), dtype=torch.float32, device=dev)
-    m_part = torch.empty((C, B, H, S), dtype=torch.float32, device=dev)
-    l_part = torch.empty((C, B, H, S), dtype=torch.float32, device=dev)
-    out = torch.empty_like(q)
-    rows = B * H * S
+    w = W.make(WORKLOADS[args.workload], layout=args.layout)
+    run = WorkloadRun(bd, torch, dev, w)
+    q, k, v, mask, out = run.q, run.k, run.v, run.mask, run.out
+    B, H, S, D, C = run.B, run.H, run.S, run.D, run.C
+    prob = run.prob
     stream = torch.cuda.current_stream()
     # the plan of a step is built on a side stream: its host part (counts, LPT, uploads) then
     # overlaps the previous step's attention on the main stream, and the forward call waits
@@ -228,57 +370,62 @@ def main() -> int:
     fwd_events = []
 
     def step(record: bool):
-        plan = bd.sparse_attn_plan(prob, "block", mask=mask, order=args.order, num_bins=args.bins, stream=plan_stream)
+        plan = run.plan(args.order, args.bins, stream=plan_stream)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         if args.mode == "merged":
-            bd.sparse_attn_fwd(plan, q, k, v, 0, C, o_part=o_part, m_part=m_part, l_part=l_part)
+            run.fwd_partial(plan)
             e1.record(stream)
-            bd.chunk_merge([o_part[c] for c in range(C)], [m_part[c] for c in range(C)],
-                           [l_part[c] for c in range(C)], rows, D, out, w.dtype)
+            run.merge()
         else:
-            bd.sparse_attn_fwd(plan, q, k, v, 0, C, o=out)
+            run.fwd_fused(plan)
             e1.record(stream)
         if record:
             fwd_events.append((e0, e1))
         return plan
 
+    prev = None
     for _ in range(args.warmup):
-        step(False).close()
+        p = step(False)
+        if prev is not None:
+            prev.close()
+        prev = p
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    plans = []  # destroyed after the timed region (destroying a plan synchronises the device)
     for _ in range(args.steps):
-        plans.append(step(True))
+        p = step(True)
+        if prev is not None:
+            prev.close()  # step i-1's plan, inside the timed loop (its buffers return to the cache)
+        prev = p
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for p in plans:
-        p.close()
+    prev.close()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in fwd_events]))
 
-    plan = bd.sparse_attn_plan(prob, "block", mask=mask, order=args.order, num_bins=args.bins)
+    plan = run.plan(args.order, args.bins)
     info = bd.sparse_attn_plan_info(plan)
-    flop = 4.0 * w.block * w.block * D * info["total_live"]
+    flop = run.flop(info["total_live"])
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (kernel_ms * 1e-3) / 1e12
     bin_load = bd.sparse_attn_plan_copy(plan, bd.SA_PLAN_BIN_LOAD, info["num_bins"])
+    traffic_key = args.workload if args.layout == "contiguous" else f"{args.workload}_{args.layout}"
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name} block-sparse MHA B{B} H{H} S{S} d{D} block {w.block}, "
-                               f"{C} {w.layout} KV chunks {'merged by chunk_merge' if args.mode == 'merged' else 'folded in-kernel'}, "
+                               f"{C} {args.layout} KV chunks {'merged by chunk_merge' if args.mode == 'merged' else 'folded in-kernel'}, "
                                f"{ {'lpt_xcd': 'two-level LPT (heads to XCDs, then Q-blocks)', 'lpt': 'LPT', 'naive': 'round-robin', 'lpt_device': 'round-based LPT made on the GPU'}[args.order]} over {info['num_bins']} bins",
-                   "B": B, "H": H, "S": S, "D": D, "block": w.block, "n_chunks": C, "layout": w.layout,
+                   "B": B, "H": H, "S": S, "D": D, "block": w.block, "n_chunks": C, "layout": args.layout,
                    "mask": {"tiny": "Bernoulli(0.5)+diag", "video": "frame band / Bernoulli",
                             "causal": "block lower-triangular", "skewed": "Zipf(1.2) rows"}[args.workload],
                    "live_tiles": info["total_live"], "mode": args.mode, "order": args.order},
         "pct_bf16_peak_step": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": read_counter_traffic(args.workload),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": read_counter_traffic(traffic_key),
                      "kernel": KERNEL_NAME, "kernel_ms": round(kernel_ms, 4),
                      "kernel_source_hash": kernel_source_hash()},
         "per_cu_work": {"planned_bin_max_over_mean": round(float(bin_load.max() / bin_load.mean()), 4),
@@ -286,96 +433,54 @@ def main() -> int:
     }
 
     if not args.no_extras:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
         # per-CU busy time from the in-kernel trace (one untimed launch)
         trace = torch.zeros((info["n_items"], 4), dtype=torch.int64, device=dev)
-        bd.sparse_attn_fwd(plan, q, k, v, 0, C, o=out, trace=trace)
+        run.fwd_fused(plan, trace=trace)
         torch.cuda.synchronize()
         result["per_cu_work"].update(per_cu_balance(trace.cpu().numpy()))
-        # fused (in-kernel chunk fold) forward and the merge alone; every timed loop below
-        # starts after one untimed launch of the same call (clock ramp after host work, an
-        # asynchronous plan's completion)
-        reps = 10
-        bd.sparse_attn_fwd(plan, q, k, v, 0, C, o=out)
-        e0.record(stream)
-        for _ in range(reps):
-            bd.sparse_attn_fwd(plan, q, k, v, 0, C, o=out)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        fused_ms = e0.elapsed_time(e1) / reps
-        bd.chunk_merge([o_part[c] for c in range(C)], [m_part[c] for c in range(C)], [l_part[c] for c in range(C)],
-                       rows, D, out, w.dtype)
-        e0.record(stream)
-        for _ in range(reps):
-            bd.chunk_merge([o_part[c] for c in range(C)], [m_part[c] for c in range(C)], [l_part[c] for c in range(C)],
-                           rows, D, out, w.dtype)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        merge_ms = e0.elapsed_time(e1) / reps
-        merge_bytes = rows * (C * (D * 4 + 8) + D * (2 if w.dtype == "bf16" else 4))
+        fused_ms = run.timed(lambda: run.fwd_fused(plan), reps)
+        merge_ms = run.timed(run.merge, reps)
+        merge_gbs = run.merge_bytes() / merge_ms / 1e6
         t_plan = time.perf_counter()
         for _ in range(reps):  # host planner (waits for the counts, LPT on the host)
-            bd.sparse_attn_plan(prob, "block", mask=mask, order="lpt_xcd").close()
+            run.plan("lpt_xcd").close()
         plan_host_ms = (time.perf_counter() - t_plan) * 1e3 / reps
         # device planner: host cost of the call (it returns without waiting) and its GPU time
         t_plan = time.perf_counter()
-        dplans = [bd.sparse_attn_plan(prob, "block", mask=mask, order="lpt_device") for _ in range(reps)]
+        dplans = [run.plan("lpt_device") for _ in range(reps)]
         plan_device_call_ms = (time.perf_counter() - t_plan) * 1e3 / reps
         torch.cuda.synchronize()
         for p_d in dplans:
             p_d.close()
         gpu_ms = []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for _ in range(reps):  # device-side latency: mask copy, popcount and the planning kernel
             e0.record(stream)
-            p_d = bd.sparse_attn_plan(prob, "block", mask=mask, order="lpt_device", stream=stream)
+            p_d = run.plan("lpt_device", stream=stream)
             e1.record(stream)
             torch.cuda.synchronize()
             gpu_ms.append(e0.elapsed_time(e1))
             p_d.close()
         plan_device_gpu_ms = float(np.median(gpu_ms))
         # whole steps with the other planner (same loop as the timed one)
-        order_main = args.order
-        other_order = "lpt_xcd" if order_main == "lpt_device" else "lpt_device"
-        args.order = other_order
-        for _ in range(2):
-            step(False).close()
-        torch.cuda.synchronize()
-        t_dev = time.perf_counter()
-        dplans = [step(False) for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        step_other_ms = (time.perf_counter() - t_dev) * 1e3 / args.steps
-        for p_d in dplans:
-            p_d.close()
-        args.order = order_main
-        alt_ms = {}
+        other_order = "lpt_xcd" if args.order == "lpt_device" else "lpt_device"
+        step_other_ms, _ = run.steps(other_order, args.steps)
         # persistent orders over one bin per resident workgroup, then one item per workgroup
         # (a plain grid that the hardware dispatches as compute units free up), in id order
         # and in LPT order
+        alt_ms = {}
         n_items = info["n_items"]
         alts = [(o_, o_, 0) for o_ in ("naive", "lpt", "lpt_xcd", "lpt_device")]
         alts += [("grid_id_order", "naive", n_items), ("grid_lpt_order", "lpt", n_items)]
         for alt, alt_order, alt_bins in alts:
-            p_alt = bd.sparse_attn_plan(prob, "block", mask=mask, order=alt_order, num_bins=alt_bins)
-            bd.sparse_attn_fwd(p_alt, q, k, v, 0, C, o=out)
-            e0.record(stream)
-            for _ in range(reps):
-                bd.sparse_attn_fwd(p_alt, q, k, v, 0, C, o=out)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            alt_ms[alt] = (e0.elapsed_time(e1) / reps, bd.sparse_attn_plan_info(p_alt))
+            p_alt = run.plan(alt_order, alt_bins)
+            alt_ms[alt] = (run.timed(lambda: run.fwd_fused(p_alt), reps), bd.sparse_attn_plan_info(p_alt))
             p_alt.close()
         # the same mask with token-level causality inside the live tiles
-        p_tc = bd.sparse_attn_plan(bd.make_problem(q, w.block, C, w.layout, token_causal=True), "block",
-                                   mask=mask, order=args.order)
-        bd.sparse_attn_fwd(p_tc, q, k, v, 0, C, o=out)
-        e0.record(stream)
-        for _ in range(reps):
-            bd.sparse_attn_fwd(p_tc, q, k, v, 0, C, o=out)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        tc_ms = e0.elapsed_time(e1) / reps
+        p_tc = run.plan(args.order, prob=bd.make_problem(q, w.block, C, args.layout, token_causal=True))
+        tc_ms = run.timed(lambda: run.fwd_fused(p_tc), reps)
         p_tc.close()
-
         # the partial-mode forward with cold caches: a 512 MiB write first evicts the L2s and
         # the Infinity Cache (256 MiB), so Q, K and V come from HBM (median of 3)
         evict = torch.empty(128 << 20, dtype=torch.float32, device=dev)
@@ -383,16 +488,16 @@ def main() -> int:
         for _ in range(3):
             evict.fill_(1.0)
             e0.record(stream)
-            bd.sparse_attn_fwd(plan, q, k, v, 0, C, o_part=o_part, m_part=m_part, l_part=l_part)
+            run.fwd_partial(plan)
             e1.record(stream)
             torch.cuda.synchronize()
             cold.append(e0.elapsed_time(e1))
         del evict
         partial_cold_ms = float(np.median(cold))
         # measured per-CU balance of the round-robin order, beside the step's planner above
-        p_naive = bd.sparse_attn_plan(prob, "block", mask=mask, order="naive")
+        p_naive = run.plan("naive")
         tr_naive = torch.zeros((info["n_items"], 4), dtype=torch.int64, device=dev)
-        bd.sparse_attn_fwd(p_naive, q, k, v, 0, C, o=out, trace=tr_naive)
+        run.fwd_fused(p_naive, trace=tr_naive)
         torch.cuda.synchronize()
         naive_balance = per_cu_balance(tr_naive.cpu().numpy())
         p_naive.close()
@@ -405,13 +510,14 @@ def main() -> int:
             "fwd_partial_cold_ms": round(partial_cold_ms, 4),
             "fwd_fused_ms": round(fused_ms, 4), "fused_tflops": round(flop / fused_ms / 1e9, 2),
             "fused_pct_bf16_peak": round(100 * flop / fused_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-            "merge_ms": round(merge_ms, 4), "merge_gbs": round(merge_bytes / merge_ms / 1e6, 1),
+            "merge_ms": round(merge_ms, 4), "merge_gbs": round(merge_gbs, 1),
+            "merge_frac_hbm_peak": round(merge_gbs / HBM_PEAK_GBS, 4),
             "fwd_fused_ms_by_order": {o: round(t, 4) for o, (t, _) in alt_ms.items()},
             "makespan_tiles_by_order": {o: i["makespan"] for o, (_, i) in alt_ms.items()},
             "xcd_groups": alt_ms["lpt_xcd"][1]["groups"],
             "fwd_fused_token_causal_ms": round(tc_ms, 4),
             "plan_device_call_ms": round(plan_device_call_ms, 4), "plan_device_gpu_ms": round(plan_device_gpu_ms, 4),
-            "ms_per_step_by_planner": {order_main: round(ms_per_step, 4), other_order: round(step_other_ms, 4)},
+            "ms_per_step_by_planner": {args.order: round(ms_per_step, 4), other_order: round(step_other_ms, 4)},
         }
     plan.close()
 
@@ -423,10 +529,21 @@ def main() -> int:
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = 4 * n
 
-    if not args.no_extras and not args.no_topk:
-        del q, k, v, o_part, m_part, l_part, out
+    if not args.no_extras:
+        del q, k, v, out, run
         torch.cuda.empty_cache()
-        result["topk_path"] = topk_path(bd, W, torch, dev)
+        if not args.no_workloads:
+            # the other block-sparse workloads: the causal one in the other layout, the video and
+            # the skewed workload (LPT against round-robin order, with measured per-CU balance)
+            others = {}
+            if args.workload == "causal":
+                other_layout = "striped" if args.layout == "contiguous" else "contiguous"
+                others[f"causal_{other_layout}"] = workload_summary(bd, W, torch, dev, 3, other_layout)
+            others["video"] = workload_summary(bd, W, torch, dev, 2)
+            others["skewed"] = workload_summary(bd, W, torch, dev, 4)
+            result["workloads"] = others
+        if not args.no_topk:
+            result["topk_path"] = topk_path(bd, W, torch, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.H))

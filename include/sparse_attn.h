@@ -26,7 +26,8 @@
  *    gets (O, m, l) = (0, -inf, 0).
  *  - A row with no live key at all gets O = 0 (and lse = -inf).
  *  - Every call is asynchronous on the given stream unless stated otherwise;
- *    no call allocates device memory except sparse_attn_plan.
+ *    no call allocates device memory except sparse_attn_plan (which takes its
+ *    buffers from the library's cache of destroyed plans' buffers first).
  *  - Errors are negative sa_status codes; no C++ exception crosses the ABI.
  *    Arguments are validated before anything is launched.  On SA_ERR_HIP the
  *    HIP error text is available from sa_last_error() (thread-local).
@@ -225,7 +226,16 @@ sa_status sparse_attn_assign_host_grouped(const int64_t* loads, int32_t n_heads,
                                           int32_t groups, int32_t* items_out, int32_t* bin_ptr_out,
                                           int64_t* bin_load_out);
 
-/* Free a plan.  Synchronises the device first.  NULL is a no-op. */
+/* Free a plan.  NULL is a no-op.  Does not wait for the device: the plan's
+ *  device buffers go to a per-device cache of the library together with events
+ *  that mark the end of the plan's own construction and of the last
+ *  sparse_attn_fwd call on every stream that used it; a later plan that takes a
+ *  buffer makes its stream wait for those events, so buffers are reused only
+ *  after every kernel that read them has finished (no host synchronisation; a
+ *  step that re-plans a runtime mask allocates nothing once the cache is warm).
+ *  The call waits only for the plan's own construction work to finish (it
+ *  frees the host arrays that work may read from).  The plan must not be used
+ *  afterwards; kernels already enqueued with it may still be running. */
 void sparse_attn_plan_destroy(sa_plan* plan);
 
 /* Static description of a status code. */

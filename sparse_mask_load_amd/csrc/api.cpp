@@ -53,6 +53,11 @@ struct sa_plan {
   // recorded on the plan's stream once its device arrays are complete; every forward call
   // makes its own stream wait for it, so a plan may be built on a side stream
   hipEvent_t ready = nullptr;
+  // device buffers of the plan (pointer, capacity in bytes), returned to the buffer cache
+  std::vector<std::pair<void*, size_t>> allocs;
+  // one event per stream that ran a forward call with the plan, re-recorded after each call
+  std::mutex use_mutex;
+  std::vector<std::pair<hipStream_t, hipEvent_t>> uses;
 };
 
 namespace {
@@ -121,27 +126,108 @@ sa_status validate_problem(const sa_problem* p, bool block_kind) {
 
 float effective_scale(const sa_problem& p) { return p.scale > 0.f ? p.scale : 1.f / std::sqrt((float)p.D); }
 
+// Device buffers of destroyed plans, kept per device for reuse by later plans (a step that
+// re-plans a runtime mask then allocates nothing once the cache holds its buffers).  A buffer
+// goes back with the events that mark the end of every use its plan made of it: the plan's
+// own construction (its ready event) and the last forward call on each stream.  A plan that
+// takes the buffer makes its stream wait for those events first, so reuse is ordered on the
+// device and neither destroying nor re-planning waits on the host.
+struct UseEvents {
+  std::vector<hipEvent_t> ev;
+  ~UseEvents() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+};
+struct CachedBuf {
+  int device;
+  void* ptr;
+  size_t bytes;
+  std::shared_ptr<UseEvents> uses;
+};
+constexpr size_t kCacheMaxBytes = size_t(2) << 30;  // beyond this, returned buffers are freed
+constexpr size_t kCacheMaxBufs = 512;
+struct BufCache {
+  std::mutex mu;
+  std::vector<CachedBuf> bufs;
+  size_t bytes = 0;
+};
+BufCache& buf_cache() {
+  static BufCache* c = new BufCache();  // never destroyed: no HIP calls during process teardown
+  return *c;
+}
+
+// Device buffer of at least n elements for plan P, from the cache (ordered after its previous
+// users on `stream`) or from hipMalloc.
 template <typename T>
-sa_status dalloc(T** ptr, size_t n) {
+sa_status dalloc(sa_plan* P, T** ptr, size_t n, hipStream_t stream) {
   *ptr = nullptr;
-  if (n == 0) n = 1;
-  hipError_t e = hipMalloc((void**)ptr, n * sizeof(T));
+  const size_t need = ((std::max<size_t>(n, 1) * sizeof(T)) + 255) & ~size_t(255);
+  CachedBuf hit{-1, nullptr, 0, nullptr};
+  {
+    BufCache& c = buf_cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    size_t best = SIZE_MAX;
+    for (size_t i = 0; i < c.bufs.size(); ++i) {
+      const CachedBuf& b = c.bufs[i];
+      if (b.device == P->device && b.bytes >= need && b.bytes <= 2 * need + 4096 &&
+          (best == SIZE_MAX || b.bytes < c.bufs[best].bytes))
+        best = i;
+    }
+    if (best != SIZE_MAX) {
+      hit = c.bufs[best];
+      c.bufs[best] = c.bufs.back();
+      c.bufs.pop_back();
+      c.bytes -= hit.bytes;
+    }
+  }
+  if (hit.ptr) {
+    P->allocs.emplace_back(hit.ptr, hit.bytes);
+    for (hipEvent_t e : hit.uses->ev) {
+      const hipError_t err = hipStreamWaitEvent(stream, e, 0);
+      if (err != hipSuccess) return hip_fail(err, "hipStreamWaitEvent on a reused plan buffer");
+    }
+    *ptr = (T*)hit.ptr;
+    return SA_OK;
+  }
+  hipError_t e = hipMalloc((void**)ptr, need);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     *ptr = nullptr;
-    return fail(SA_ERR_NOMEM, "hipMalloc of %zu bytes failed: %s", n * sizeof(T), hipGetErrorString(e));
+    return fail(SA_ERR_NOMEM, "hipMalloc of %zu bytes failed: %s", need, hipGetErrorString(e));
   }
+  P->allocs.emplace_back((void*)*ptr, need);
   return SA_OK;
 }
 
+// Frees a plan without waiting for the device: its buffers go to the cache together with
+// the events of their last uses (buffers beyond the cache's limits are freed once those
+// events have completed).
 void free_plan(sa_plan* p) {
   if (!p) return;
-  (void)hipDeviceSynchronize();
-  void* ptrs[] = {p->d_mask, p->d_row, p->d_col, p->d_crow, p->d_items, p->d_bin_ptr,
-                  p->d_bin_load, p->d_stats, p->d_idx, p->d_count, p->d_qp, p->d_kp};
-  for (void* q : ptrs)
-    if (q) (void)hipFree(q);
-  if (p->ready) (void)hipEventDestroy(p->ready);
+  auto uses = std::make_shared<UseEvents>();
+  if (p->ready) {
+    // host copies the plan uploaded from are freed below: let its own work finish first
+    (void)hipEventSynchronize(p->ready);
+    uses->ev.push_back(p->ready);
+  }
+  for (auto& u : p->uses) uses->ev.push_back(u.second);
+  std::vector<std::pair<void*, size_t>> spill;
+  {
+    BufCache& c = buf_cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    for (auto& a : p->allocs) {
+      if (c.bytes + a.second <= kCacheMaxBytes && c.bufs.size() < kCacheMaxBufs) {
+        c.bufs.push_back(CachedBuf{p->device, a.first, a.second, uses});
+        c.bytes += a.second;
+      } else {
+        spill.push_back(a);
+      }
+    }
+  }
+  if (!spill.empty()) {
+    for (hipEvent_t e : uses->ev) (void)hipEventSynchronize(e);
+    for (auto& a : spill) (void)hipFree(a.first);
+  }
   delete p;
 }
 
@@ -179,16 +265,17 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   if (!sp->mask) return fail(SA_ERR_INVALID, "mask is NULL");
   const size_t mask_bytes = (size_t)BH * nQ * nK;
   sa_status st;
-  if ((st = dalloc(&P->d_mask, mask_bytes)) || (st = dalloc(&P->d_row, (size_t)BH * nQ)) ||
-      (st = dalloc(&P->d_col, (size_t)BH * nK)) || (st = dalloc(&P->d_crow, (size_t)BH * C * nQ)) ||
-      (st = dalloc(&P->d_items, (size_t)(C + 1) * P->n_items)) ||
-      (st = dalloc(&P->d_bin_ptr, (size_t)(C + 1) * (P->num_bins + 1))))
+  if ((st = dalloc(P, &P->d_mask, mask_bytes, stream)) || (st = dalloc(P, &P->d_row, (size_t)BH * nQ, stream)) ||
+      (st = dalloc(P, &P->d_col, (size_t)BH * nK, stream)) || (st = dalloc(P, &P->d_crow, (size_t)BH * C * nQ, stream)) ||
+      (st = dalloc(P, &P->d_items, (size_t)(C + 1) * P->n_items, stream)) ||
+      (st = dalloc(P, &P->d_bin_ptr, (size_t)(C + 1) * (P->num_bins + 1), stream)))
     return st;
   SA_HIP(hipMemcpyAsync(P->d_mask, sp->mask, mask_bytes, hipMemcpyDeviceToDevice, stream));
   SA_HIP(sa::launch_popcount(P->d_mask, BH, nQ, nK, C, pr.layout, P->d_row, P->d_col, P->d_crow, stream));
   if (P->order == SA_ORDER_LPT_DEVICE) {
     // every list on the device, right behind the popcount: nothing waits for the host
-    if ((st = dalloc(&P->d_bin_load, (size_t)(C + 1) * P->num_bins)) || (st = dalloc(&P->d_stats, (size_t)(C + 1) * 4)))
+    if ((st = dalloc(P, &P->d_bin_load, (size_t)(C + 1) * P->num_bins, stream)) ||
+        (st = dalloc(P, &P->d_stats, (size_t)(C + 1) * 4, stream)))
       return st;
     SA_HIP(sa::launch_plan_rounds(P->d_row, P->d_crow, BH, nQ, C, P->num_bins, P->d_items, P->d_bin_ptr,
                                   P->d_bin_load, P->d_stats, stream));
@@ -255,6 +342,22 @@ sa_status ensure_list_on_device(sa_plan* P, int list, hipStream_t stream) {
   return SA_OK;
 }
 
+// Marks the end of a forward call's use of the plan's buffers on `stream` (the plan's cache
+// entry waits for it before the buffers serve another plan).
+sa_status note_use(const sa_plan* cP, hipStream_t stream) {
+  sa_plan* P = const_cast<sa_plan*>(cP);  // logically const: only the use bookkeeping changes
+  std::lock_guard<std::mutex> lock(P->use_mutex);
+  hipEvent_t ev = nullptr;
+  for (auto& u : P->uses)
+    if (u.first == stream) ev = u.second;
+  if (!ev) {
+    SA_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    P->uses.emplace_back(stream, ev);
+  }
+  SA_HIP(hipEventRecord(ev, stream));
+  return SA_OK;
+}
+
 sa_status plan_topk(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   const sa_problem& pr = P->prob;
   if (pr.dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "top-k kinds are bf16 only");
@@ -264,7 +367,7 @@ sa_status plan_topk(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   const size_t rows = (size_t)pr.B * pr.H * pr.S;
   P->n_items = (int32_t)rows;
   sa_status st;
-  if ((st = dalloc(&P->d_idx, rows * P->top_k)) || (st = dalloc(&P->d_count, rows))) return st;
+  if ((st = dalloc(P, &P->d_idx, rows * P->top_k, stream)) || (st = dalloc(P, &P->d_count, rows, stream))) return st;
   if (P->kind == SA_KIND_INDEX) {
     if (!sp->idx || !sp->count) return fail(SA_ERR_INVALID, "idx or count is NULL");
     std::vector<int32_t> idx(rows * P->top_k), cnt(rows);
@@ -292,7 +395,7 @@ sa_status plan_topk(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
     return fail(SA_ERR_UNSUPPORTED, "indexer top_k %d above %d", P->top_k, sa::kIndexerMaxTopK);
   if (pr.S > 65536) return fail(SA_ERR_UNSUPPORTED, "indexer sequence length %d above 65536", pr.S);
   P->rank = sp->rank;
-  if ((st = dalloc(&P->d_qp, rows * P->rank)) || (st = dalloc(&P->d_kp, rows * P->rank))) return st;
+  if ((st = dalloc(P, &P->d_qp, rows * P->rank, stream)) || (st = dalloc(P, &P->d_kp, rows * P->rank, stream))) return st;
   sa::IndexerArgs a{};
   a.q = sp->q; a.k = sp->k; a.wq = sp->wq; a.wk = sp->wk;
   a.qp = P->d_qp; a.kp = P->d_kp; a.idx = P->d_idx; a.count = P->d_count;
@@ -382,7 +485,7 @@ sa_status sparse_attn_fwd(const sa_plan* P, const void* q, const void* k, const 
     a.sb = pr.sb; a.sh = pr.sh; a.ss = pr.ss;
     a.scale_log2 = effective_scale(pr) * 1.4426950408889634f;
     SA_HIP(sa::launch_gather_attn(a, stream));
-    return SA_OK;
+    return note_use(P, stream);
   }
   if (chunk_begin < 0 || chunk_end > pr.n_chunks || chunk_begin >= chunk_end)
     return fail(SA_ERR_INVALID, "chunk range [%d, %d) not inside [0, %d)", chunk_begin, chunk_end, pr.n_chunks);
@@ -411,7 +514,7 @@ sa_status sparse_attn_fwd(const sa_plan* P, const void* q, const void* k, const 
   hipError_t e = pr.dtype == SA_BF16 ? sa::launch_attn_bf16(a, pr.D, pr.block, stream)
                                      : sa::launch_attn_f32(a, pr.D, pr.block, stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-  return SA_OK;
+  return note_use(P, stream);
 }
 
 sa_status chunk_merge(int32_t n_parts, const float* const* o_parts, const float* const* m_parts,
@@ -515,7 +618,7 @@ sa_status sparse_attn_plan_copy(const sa_plan* P, int32_t what, int32_t chunk, v
   if (n_elems != count) return fail(SA_ERR_INVALID, "array %d has %lld elements, caller asked for %lld", what,
                                     (long long)count, (long long)n_elems);
   if (device) {
-    SA_HIP(hipDeviceSynchronize());
+    if (P->ready) SA_HIP(hipEventSynchronize(P->ready));  // the plan's arrays are complete
     SA_HIP(hipMemcpy(dst, src, (size_t)count * esize, hipMemcpyDeviceToHost));
   } else {
     std::memcpy(dst, src, (size_t)count * esize);

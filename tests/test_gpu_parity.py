@@ -375,3 +375,35 @@ def test_xcd_order_plan_and_output(cfg):
     o2 = G.run_full(plan2, q, k, v)
     # the order changes which workgroup runs an item, not the arithmetic of the item
     assert torch.equal(o, o2)
+
+
+def test_plan_buffers_reused_only_after_their_last_use():
+    """A destroyed plan's buffers return to the library's cache while its forward call may still
+    be running; the next plan (same sizes, a different mask, on another stream) takes them over
+    ordered after that call.  Both outputs must match the oracle."""
+    w = W.make(3)
+    q, k, v = G.upload(w)
+    o1 = G.empty_like_qkv(q)
+    plan1 = G.plan_block(w, q, order="lpt_device")
+    torch.cuda.synchronize()
+    for _ in range(3):  # a queue of work that keeps plan 1's buffers in use for a while
+        bd.sparse_attn_fwd(plan1, q, k, v, 0, w.n_chunks, o=o1)
+    plan1.close()  # returns at once; the kernels above still read the plan's lists
+    w2 = W.make_custom(w.B, w.H, w.S, w.D, block=w.block, n_chunks=w.n_chunks, pattern="bernoulli", density=0.3,
+                       seed=77, mask_only=True)
+    w2.q, w2.k, w2.v = w.q, w.k, w.v
+    side = torch.cuda.Stream()
+    mask2 = torch.from_numpy(np.ascontiguousarray(w2.mask)).cuda()
+    plan2 = bd.sparse_attn_plan(bd.make_problem(q, w.block, w.n_chunks, w.layout), "block", mask=mask2,
+                                order="lpt_device", stream=side)
+    o2 = G.empty_like_qkv(q)
+    with torch.cuda.stream(side):
+        bd.sparse_attn_fwd(plan2, q, k, v, 0, w.n_chunks, o=o2)
+    torch.cuda.synchronize()
+    rows = G.sample_rows(w, 64, seed=9)
+    idx = tuple(np.array(rows).T)
+    ref1, _ = A.masked_attention(w.q, w.k, w.v, w.mask, w.block, rows=rows)
+    ref2, _ = A.masked_attention(w.q, w.k, w.v, w2.mask, w.block, rows=rows)
+    G.assert_close(G.to64(o1)[idx], ref1, G.BF16_TOL, "plan 1 (destroyed while running)")
+    G.assert_close(G.to64(o2)[idx], ref2, G.BF16_TOL, "plan 2 (reused buffers)")
+    plan2.close()
