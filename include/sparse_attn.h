@@ -188,6 +188,26 @@ sa_status sparse_attn_fwd(const sa_plan* plan, const void* q, const void* k, con
                           int32_t chunk_begin, int32_t chunk_end, void* o, float* o_part,
                           float* m_part, float* l_part, int64_t* trace, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ *  tight serving loops, harnesses that forbid allocation): plan and forward in
+ *  one call that allocates nothing.  The result equals that of
+ *  sparse_attn_plan(prob, SA_KIND_BLOCK mask, num_bins, SA_ORDER_LPT_DEVICE)
+ *  followed by sparse_attn_fwd over [chunk_begin, chunk_end) with the same o or
+ *  (o_part, m_part, l_part).  The counts and the work list are kept in a
+ *  2 MiB device array of the library, one per GPU, held until the process
+ *  ends; calls that overlap on one GPU (other streams, other host threads)
+ *  race on it, calls ordered on one stream do not.  All launches go to
+ *  `stream`; the call never waits for the device.
+ *  mask: uint8 [B][H][nQ][nK] as for a block plan, 16-byte aligned, read on
+ *  the stream (keep it alive until the work is done); it is not copied.
+ *  Limits: B*H*nQ <= 16384 and num_bins <= 1024 (as for SA_ORDER_LPT_DEVICE),
+ *  and the counts and list must fit the array (about B*H*nQ*(n_chunks + 3)*4
+ *  bytes); beyond them SA_ERR_UNSUPPORTED.  Other arguments as for
+ *  sparse_attn_plan and sparse_attn_fwd. */
+sa_status sparse_attn_fwd_noalloc(const sa_problem* prob, const uint8_t* mask, int32_t num_bins, const void* q,
+                                  const void* k, const void* v, int32_t chunk_begin, int32_t chunk_end, void* o,
+                                  float* o_part, float* m_part, float* l_part, hipStream_t stream);
+
 /* Online-softmax merge of n_parts partials (6D notes, section 2.1): per row,
  *  the parts are taken in order into one running (O, m, l); at each step the
  *  running maximum becomes the larger of m and m_p and both sides' O and l are

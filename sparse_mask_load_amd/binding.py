@@ -63,6 +63,8 @@ _SIGNATURES = {
     "sparse_attn_plan": (ctypes.c_int32, [ctypes.POINTER(sa_problem), ctypes.POINTER(sa_sparsity), ctypes.c_int32,
                                           ctypes.c_int32, ctypes.POINTER(_P), _P]),
     "sparse_attn_fwd": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
+    "sparse_attn_fwd_noalloc": (ctypes.c_int32, [ctypes.POINTER(sa_problem), _P, ctypes.c_int32, _P, _P, _P,
+                                                 ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P]),
     "chunk_merge": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
                                      ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]),
     "sparse_attn_plan_info": (ctypes.c_int32, [_P, ctypes.POINTER(sa_plan_info)]),
@@ -167,6 +169,16 @@ def sparse_attn_fwd(plan: Plan, q, k, v, chunk_begin: int = 0, chunk_end: Option
     _check(lib().sparse_attn_fwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), chunk_begin, chunk_end, _ptr(o),
                                  _ptr(o_part), _ptr(m_part), _ptr(l_part), _ptr(trace), _stream(stream)),
            "sparse_attn_fwd")
+
+
+def sparse_attn_fwd_noalloc(problem: sa_problem, mask, q, k, v, chunk_begin: int = 0,
+                            chunk_end: Optional[int] = None, o=None, o_part=None, m_part=None, l_part=None,
+                            num_bins: int = 0, stream=None) -> None:
+    if chunk_end is None:
+        chunk_end = max(1, problem.n_chunks)
+    _check(lib().sparse_attn_fwd_noalloc(ctypes.byref(problem), _ptr(mask), num_bins, _ptr(q), _ptr(k), _ptr(v),
+                                         chunk_begin, chunk_end, _ptr(o), _ptr(o_part), _ptr(m_part),
+                                         _ptr(l_part), _stream(stream)), "sparse_attn_fwd_noalloc")
 
 
 def chunk_merge(o_parts: Sequence, m_parts: Sequence, l_parts: Sequence, rows: int, D: int, o_out,

@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
 
 SOURCES = ["api.cpp", "lpt.cpp", "popcount.hip", "attn_bf16.hip", "attn_f32.hip", "merge.hip",
-           "gather_attn.hip", "indexer.hip", "plan_device.hip"]
+           "gather_attn.hip", "indexer.hip", "plan_device.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -412,6 +412,23 @@ sa_status plan_topk(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
 
 }  // namespace
 
+namespace sa {
+
+sa_status set_error(sa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+sa_status validate_block_problem(const sa_problem* p) { return validate_problem(p, true); }
+int default_num_bins(const sa_problem& p, int device) { return default_bins(p, device); }
+float softmax_scale(const sa_problem& p) { return effective_scale(p); }
+
+}  // namespace sa
+
 extern "C" {
 
 sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_t num_bins, int32_t order,

@@ -87,17 +87,25 @@ struct MergeArgs {
 // Kernel launchers (defined in the .hip files).  Return hipSuccess or the launch error.
 hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_chunks, int layout,
                            int32_t* row, int32_t* col, int32_t* crow, hipStream_t stream);
-// Round-based LPT of every list of a block plan on the device: list 0 from row, list 1 + c
-// from chunk c of crow; items [(C+1)][BH*nQ], bin_ptr [(C+1)][m+1], bin_load [(C+1)][m],
-// stats [(C+1)][4] = (load sum, max item load, makespan, lower bound).
+// Round-based LPT of the lists of a block plan on the device: list 0 from row, list 1 + c
+// from chunk c of crow.  Lists [list0, list0 + n_lists) are made (n_lists < 0: through list
+// C), list list0 + s written to slot s of items [.][BH*nQ], bin_ptr [.][m+1], bin_load [.][m]
+// and stats [.][4] = (load sum, max item load, makespan, lower bound).
 hipError_t launch_plan_rounds(const int32_t* row, const int32_t* crow, int BH, int nQ, int C, int m, int32_t* items,
-                              int32_t* bin_ptr, int64_t* bin_load, int64_t* stats, hipStream_t stream);
+                              int32_t* bin_ptr, int64_t* bin_load, int64_t* stats, hipStream_t stream,
+                              int list0 = 0, int n_lists = -1);
 hipError_t launch_attn_bf16(const FwdArgs& a, int D, int block, hipStream_t stream);
 int attn_bf16_wg_per_cu(int block);  // workgroups the bf16 kernel keeps resident per CU
 hipError_t launch_attn_f32(const FwdArgs& a, int D, int block, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int D, int out_dtype, hipStream_t stream);
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
 hipError_t launch_gather_attn(const GatherArgs& a, hipStream_t stream);
+
+// Host helpers of the C ABI (api.cpp), shared by the entry points in other files.
+sa_status set_error(sa_status st, const char* fmt, ...);       // records the last-error text
+sa_status validate_block_problem(const sa_problem* p);          // as for a block plan
+int default_num_bins(const sa_problem& p, int device);          // one bin per resident workgroup
+float softmax_scale(const sa_problem& p);                       // scale, or 1/sqrt(D) when <= 0
 
 // Host LPT / round-robin (lpt.cpp).  Items are 0..n-1 with loads[i] >= 0.
 //   LPT: sort by (load desc, id asc); each item goes to the least-loaded bin,

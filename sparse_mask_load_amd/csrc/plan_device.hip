@@ -41,14 +41,15 @@ __global__ __launch_bounds__(kThreads) void plan_rounds_kernel(const int32_t* __
                                                                int C, int m, int32_t* __restrict__ items,
                                                                int32_t* __restrict__ bin_ptr,
                                                                int64_t* __restrict__ bin_load,
-                                                               int64_t* __restrict__ stats) {
+                                                               int64_t* __restrict__ stats, int list0) {
   __shared__ uint32_t key[kDevicePlanMaxItems];   // sort keys; after the sort, items in LPT order
   __shared__ uint16_t bin_at[kDevicePlanMaxItems];  // bin of the item at each LPT position
   __shared__ uint64_t xch[kThreads];               // bitonic exchange across waves / scan buffer
   __shared__ unsigned long long red_sum;
   __shared__ unsigned int red_max, red_span;
 
-  const int list = blockIdx.x;
+  const int list = list0 + blockIdx.x;  // which list; its outputs go to slot blockIdx.x
+  const int slot = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = BH * nQ;
   int n2 = 2;
@@ -123,13 +124,13 @@ __global__ __launch_bounds__(kThreads) void plan_rounds_kernel(const int32_t* __
   // 3. bin loads and counts: full rounds give every bin one item; the last round's takers one more
   const int full = n / m;
   const int rem = n - full * m;
-  int32_t* const ptr_out = bin_ptr + (int64_t)list * (m + 1);
+  int32_t* const ptr_out = bin_ptr + (int64_t)slot * (m + 1);
   uint32_t* const cnt = (uint32_t*)xch;  // reused: no exchange is pending
   __syncthreads();
   if (tid < m) {
     const int b = (int)(bkey & 0xFFFF);
     const int64_t load = (int64_t)(bkey >> 16);
-    bin_load[(int64_t)list * m + b] = load;
+    bin_load[(int64_t)slot * m + b] = load;
     atomicMax(&red_span, (unsigned int)load);
   }
   for (int b = tid; b < kThreads; b += kThreads) cnt[b] = b < m ? (uint32_t)full : 0u;
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void plan_rounds_kernel(const int32_t* __
   }
   if (tid < m) ptr_out[tid + 1] = (int32_t)v;
   if (tid == 0) ptr_out[0] = 0;
-  int32_t* const items_out = items + (int64_t)list * n;
+  int32_t* const items_out = items + (int64_t)slot * n;
   for (int p = tid; p < n; p += kThreads) {
     const int b = bin_at[p];
     const uint32_t start = b == 0 ? 0u : cnt[b - 1];
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void plan_rounds_kernel(const int32_t* __
   }
   if (tid == 0) {
     const int64_t total = (int64_t)red_sum, pmax = (int64_t)red_max;
-    int64_t* s = stats + (int64_t)list * 4;
+    int64_t* s = stats + (int64_t)slot * 4;
     s[0] = total;
     s[1] = pmax;
     s[2] = (int64_t)red_span;
@@ -167,10 +168,14 @@ __global__ __launch_bounds__(kThreads) void plan_rounds_kernel(const int32_t* __
 }  // namespace
 
 hipError_t launch_plan_rounds(const int32_t* row, const int32_t* crow, int BH, int nQ, int C, int m, int32_t* items,
-                              int32_t* bin_ptr, int64_t* bin_load, int64_t* stats, hipStream_t stream) {
-  if (BH * nQ > kDevicePlanMaxItems || m > kDevicePlanMaxBins || m < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(plan_rounds_kernel, dim3(C + 1), dim3(kThreads), 0, stream, row, crow, BH, nQ, C, m, items,
-                     bin_ptr, bin_load, stats);
+                              int32_t* bin_ptr, int64_t* bin_load, int64_t* stats, hipStream_t stream, int list0,
+                              int n_lists) {
+  if (n_lists < 0) n_lists = C + 1 - list0;
+  if (BH * nQ > kDevicePlanMaxItems || m > kDevicePlanMaxBins || m < 1 || list0 < 0 || n_lists < 1 ||
+      list0 + n_lists > C + 1)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plan_rounds_kernel, dim3(n_lists), dim3(kThreads), 0, stream, row, crow, BH, nQ, C, m, items,
+                     bin_ptr, bin_load, stats, list0);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 """CPU checks of the C ABI: the library loads, exports every declared entry point, its host
 LPT planner is bit-exact against the oracle, and argument errors are reported before any
 GPU work.  No kernel is launched here."""
+import ctypes
 import os
 import re
 
@@ -198,3 +199,25 @@ def test_host_grouped_assign_on_workload_rows(cfg, m):
     for b in range(m):
         bin_of[items[ptr[b]:ptr[b + 1]]] = b
     assert all(len(set((bin_of[h * w.nQ:(h + 1) * w.nQ] % 8).tolist())) == 1 for h in range(heads))
+
+
+def test_noalloc_argument_errors_before_the_gpu():
+    """The allocation-free entry point rejects bad arguments and sizes beyond its work array
+    before any HIP call."""
+    lib = bd.lib()
+    mask = np.ones(4096, np.uint8)
+    ptr = mask.ctypes.data + (-mask.ctypes.data) % 16  # 16-byte aligned host address (never dereferenced)
+    call = lambda prob, m=ptr, bins=0, c0=0, c1=1, o=1: lib.sparse_attn_fwd_noalloc(
+        ctypes.byref(prob), m, bins, 1, 1, 1, c0, c1, o, None, None, None, None)
+    ok = _problem()
+    assert call(ok, m=None) == bd.SA_ERR_INVALID
+    assert call(ok, m=ptr + 1) == bd.SA_ERR_INVALID and "aligned" in bd.sa_last_error()
+    assert call(ok, c0=1, c1=1) == bd.SA_ERR_INVALID
+    assert call(ok, o=None) == bd.SA_ERR_INVALID and "partial mode" in bd.sa_last_error()
+    assert call(ok, bins=-1) == bd.SA_ERR_INVALID
+    assert call(ok, bins=1025) == bd.SA_ERR_UNSUPPORTED
+    big = _problem(H=65, S=16384, sb=65 * 16384 * 64, sh=16384 * 64, n_chunks=1)
+    assert call(big) == bd.SA_ERR_UNSUPPORTED and "16384" in bd.sa_last_error()
+    # 64 heads x 256 Q-blocks x 64 chunks of counts do not fit the 2 MiB work array
+    wide = _problem(H=64, S=16384, sb=64 * 16384 * 64, sh=16384 * 64, n_chunks=64)
+    assert call(wide) == bd.SA_ERR_UNSUPPORTED and "work array" in bd.sa_last_error()
