@@ -107,7 +107,7 @@ def _problem(**kw):
     return bd.sa_problem(**base)
 
 
-@pytest.mark.parametrize("kw,status", [
+BAD_PROBLEMS = [
     (dict(D=96), bd.SA_ERR_UNSUPPORTED),
     (dict(block=32), bd.SA_ERR_UNSUPPORTED),
     (dict(B=0), bd.SA_ERR_INVALID),
@@ -117,7 +117,10 @@ def _problem(**kw):
     (dict(layout=1, n_chunks=4), bd.SA_ERR_UNSUPPORTED),  # block/C = 16 keys < 32
     (dict(layout=7), bd.SA_ERR_INVALID),
     (dict(dtype=bd.SA_F32, block=128), bd.SA_ERR_UNSUPPORTED),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_PROBLEMS)
 def test_plan_rejects_bad_problems_before_touching_the_gpu(kw, status):
     import ctypes
     prob = _problem(**kw)
