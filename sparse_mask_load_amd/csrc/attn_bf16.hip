@@ -738,7 +738,7 @@ struct PBlock {
 // rounded probabilities with their row sum.  Returns the ballot of the rows
 // whose reference moved.
 __device__ __forceinline__ uint64_t block_softmax(const f32x16& s, float sl2, float& ref, float& m_true,
-                                                  PBlock& pb) {
+                                                  PBlock& pb, bool dead = false) {
   float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
   float b = fmaxf(fmaxf(s[8], s[9]), s[10]);
   a = fmaxf(fmaxf(a, s[3]), s[4]);
@@ -747,18 +747,19 @@ __device__ __forceinline__ uint64_t block_softmax(const f32x16& s, float sl2, fl
   b = fmaxf(fmaxf(b, s[13]), s[14]);
   float mx = fmaxf(fmaxf(a, s[7]), fmaxf(b, s[15]));
   mx = fmaxf(mx, other_half(mx)) * sl2;
+  mx = dead ? kNegInf : mx;  // a dead block (striped layout) has no live key
   m_true = fmaxf(m_true, mx);
   const bool up = mx > ref + kRescaleSlack;
   ref = up ? m_true : ref;
   pb.ref = ref;
   float l0 = 0.f, l1 = 0.f;
-  tile_probs(s, sl2, ref, pb.p, l0, l1);
+  tile_probs(s, sl2, dead ? __builtin_huge_valf() : ref, pb.p, l0, l1);  // a dead block's P is 0
   pb.lsum = l0 + l1;
   return __builtin_amdgcn_ballot_w64(up);
 }
 
-// Full-tile kernel for 128-key blocks (contiguous chunks, S a multiple of the
-// block, no token-level causality), software-pipelined per 32-key block.  The
+// Full-tile kernel for 128-key blocks (S a multiple of the block, no
+// token-level causality), software-pipelined per 32-key block.  The
 // wave's work is a stream of blocks b (two per tile): the S MFMAs of block
 // b+2 and the P V MFMAs of block b issue while the vector units take block
 // b+1's row max and exponentials, so neither waits for the other.  The
@@ -766,9 +767,11 @@ __device__ __forceinline__ uint64_t block_softmax(const f32x16& s, float sl2, fl
 // that consumes it; before block b's P V the accumulators are brought to
 // block b's reference (a rescale only when some row's reference moved, which
 // the lazy rule makes rare).  MFMA operands are read from LDS a few MFMAs
-// ahead of their use, in the order given by the scheduling groups at the end
-// of each section.
-template <int D>
+// ahead of their use, one MFMA slot at a time.  STRIPED: chunks of the
+// striped layout, where a tile's 32-key groups come from different KV blocks
+// and a dead group's block takes no part (its row max is -inf and its
+// probabilities are 0; its MFMAs still run).
+template <int D, bool STRIPED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_pipe_kernel(FwdArgs a) {
   constexpr int BLK = 128;
@@ -792,9 +795,11 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
   const int rg = wave % NRG, kh = wave / NRG;
   const int kb0 = kh * NB;
   const bool full = a.o != nullptr;
+  constexpr int LAYOUT = STRIPED ? SA_LAYOUT_STRIPED : SA_LAYOUT_CONTIGUOUS;
+  const int kb_div = SH::NKB / a.n_chunks;  // striped: 32-key blocks per liveness group
   TileLoader<D, BLK> loader;
   loader.init(wave, lane);
-  loader.set_stride((int)a.ss);
+  loader.set_stride(STRIPED ? (int)(a.ss * a.n_chunks) : (int)a.ss);
   OperandLanes<D, true> ol;
   ol.init(lane, kb0);
   const bf16* __restrict__ gQ = (const bf16*)a.q;
@@ -821,8 +826,8 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
     }
 
     __syncthreads();  // every wave is done with the previous item's list, tiles and merge buffers
-    const int n_tiles = build_tile_list(a.mask + (int64_t)item * a.nK, a.nK, a.n_chunks, SA_LAYOUT_CONTIGUOUS, a.c0,
-                                        a.c1, sList, wave == 0);
+    const int n_tiles = build_tile_list(a.mask + (int64_t)item * a.nK, a.nK, a.n_chunks, LAYOUT, a.c0, a.c1, sList,
+                                        wave == 0);
     __syncthreads();
 
     RowState<ND> st;  // acc and l relative to st.m_ref (the reference of the last consumed block)
@@ -873,8 +878,12 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       __syncthreads();
       reset(st);
     };
-    auto src_of = [&](int desc) { return tile_source(desc, bh_base, a.ss, a.S, SA_LAYOUT_CONTIGUOUS, a.n_chunks, BLK); };
+    auto src_of = [&](int desc) { return tile_source(desc, bh_base, a.ss, a.S, LAYOUT, a.n_chunks, BLK); };
     auto chunk_of = [&](int desc) { return (desc >> kDescChunkShift) & 63; };
+    // key block j of this wave in the tile of `desc` has no live key (striped layout only)
+    auto dead_of = [&](int desc, int j) {
+      return STRIPED && !((desc >> (kDescCodeShift + (kb0 + j) / kb_div)) & 1);
+    };
 
     f32x16 sc[NB];       // scores of the two blocks of the next tile to be exponentiated
     PBlock pb[NB];       // probabilities waiting for their P V product
@@ -891,7 +900,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       tile_scores<D, BLK, false>(sK0, qf, ol, 0, sc);
       // block 0 starts an accumulation: its running max goes to m_next, which
       // the first tile takes over (after flushing any empty leading chunks)
-      moved[0] = block_softmax(sc[0], sl2, ref_cur, m_next, pb[0]);
+      moved[0] = block_softmax(sc[0], sl2, ref_cur, m_next, pb[0], dead_of(d0, 0));
     }
 
     // Brings the accumulators and row sum to the reference of block pb, then
@@ -918,6 +927,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       const int desc1 = has_next ? __builtin_amdgcn_readfirstlane(sList[t + 1]) : desc;
       // the next tile starts a new accumulation (a chunk of its own in partial mode)
       const bool next_new = !full && has_next && chunk_of(desc1) != chunk_of(desc);
+      const bool dead_sec[NB] = {dead_of(desc, 1), dead_of(desc1, 0)};  // blocks exponentiated in sections 0, 1
 
       wait_vm();
       __syncthreads();
@@ -961,7 +971,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
         constexpr int SRC = j == 0 ? 1 : 0;
         const f32x16& s = sc[SRC];
         PBlock& out = pb[SRC];
-        float mx_a, mx_b, mx, run, l0, l1;
+        float mx_a, mx_b, mx, run, ref_exp, l0, l1;
         auto stage = [&](auto sc_) {
           constexpr int g = decltype(sc_)::value;
           if constexpr (g == 0) {
@@ -975,6 +985,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
             mx = fmaxf(fmaxf(mx_a, s[7]), fmaxf(mx_b, s[15]));
           } else if constexpr (g == 2) {
             mx = fmaxf(mx, other_half(mx)) * sl2;
+            if constexpr (STRIPED) mx = dead_sec[j] ? kNegInf : mx;
           } else if constexpr (g == 3) {
             if constexpr (j == 0) {
               run = st.m_true;
@@ -986,6 +997,8 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
             const bool up = mx > ref_cur + kRescaleSlack;
             ref_cur = up ? run : ref_cur;
             out.ref = ref_cur;
+            // reference of the exponent: +inf makes a dead block's probabilities 0
+            ref_exp = (STRIPED && dead_sec[j]) ? __builtin_huge_valf() : ref_cur;
             moved[SRC] = __builtin_amdgcn_ballot_w64(up);
             if constexpr (j == 0) {
               st.m_true = run;
@@ -997,8 +1010,8 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
             l1 = 0.f;
           } else if constexpr (g < 12) {
             constexpr int r = 2 * (g - 4);
-            out.p[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[r], sl2, -ref_cur));
-            out.p[r >> 3][(r & 7) + 1] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[r + 1], sl2, -ref_cur));
+            out.p[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[r], sl2, -ref_exp));
+            out.p[r >> 3][(r & 7) + 1] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[r + 1], sl2, -ref_exp));
           } else {
             constexpr int h = g - 12;
             const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
@@ -1070,13 +1083,20 @@ template <int D, int BLK>
 hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
   const bool general = a.layout == SA_LAYOUT_STRIPED || a.S % BLK != 0;
   const dim3 grid(a.num_bins), block(Shape<D, BLK>::NW * 64);
+  if constexpr (BLK == 128) {
+    // striped chunks (S is then a multiple of block * n_chunks) without token-level causality
+    if (a.layout == SA_LAYOUT_STRIPED && !a.token_causal) {
+      hipLaunchKernelGGL((attn_bf16_pipe_kernel<D, true>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (general)
     hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, true, false>), grid, block, 0, stream, a);
   else if constexpr (BLK == 128) {
     if (a.token_causal)
       hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false, true>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_bf16_pipe_kernel<D>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16_pipe_kernel<D, false>), grid, block, 0, stream, a);
   } else if (a.token_causal)
     hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false, true>), grid, block, 0, stream, a);
   else
