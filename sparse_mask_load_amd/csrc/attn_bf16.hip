@@ -731,6 +731,18 @@ struct PBlock {
   float lsum;   // this lane's share of the block's row sum of the rounded P
 };
 
+// Token-level causality on one wave's 32-key block: drops score r (key
+// offset 16*(r/8) + 8*h2 + r%8 within the block, in steps of kstep token
+// positions from the block's first key kpos) when its key lies after the
+// lane's query qpos.
+__device__ __forceinline__ void drop_future(f32x16& s, int qpos, int kpos, int kstep, int h2) {
+  const int rel = qpos - kpos - kstep * 8 * h2;
+  const int off_max = rel < 0 ? -1 : rel / kstep;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (16 * (r >> 3) + (r & 7) > off_max) s[r] = kNegInf;
+}
+
 // One 32-key block's step of the online softmax for rows whose scores are all
 // finite: the block's row max (both half-waves), its fold into the running
 // true max, the lazy move of the reference (a row whose block max exceeds its
@@ -753,7 +765,9 @@ __device__ __forceinline__ uint64_t block_softmax(const f32x16& s, float sl2, fl
   ref = up ? m_true : ref;
   pb.ref = ref;
   float l0 = 0.f, l1 = 0.f;
-  tile_probs(s, sl2, dead ? __builtin_huge_valf() : ref, pb.p, l0, l1);  // a dead block's P is 0
+  // a dead block's P is 0; a row without a finite score yet (token-level causality) takes
+  // reference 0 so that its dropped scores give 0, not exp(-inf + inf)
+  tile_probs(s, sl2, dead ? __builtin_huge_valf() : (ref == kNegInf ? 0.f : ref), pb.p, l0, l1);
   pb.lsum = l0 + l1;
   return __builtin_amdgcn_ballot_w64(up);
 }
@@ -770,8 +784,11 @@ __device__ __forceinline__ uint64_t block_softmax(const f32x16& s, float sl2, fl
 // ahead of their use, one MFMA slot at a time.  STRIPED: chunks of the
 // striped layout, where a tile's 32-key groups come from different KV blocks
 // and a dead group's block takes no part (its row max is -inf and its
-// probabilities are 0; its MFMAs still run).
-template <int D, bool STRIPED>
+// probabilities are 0; its MFMAs still run).  TCAUSAL: token-level causality;
+// a block whose last key lies after the wave's first query drops the scores
+// of keys after each lane's query before its row max (a uniform branch, taken
+// on diagonal tiles only), and rows that have no key yet keep an empty state.
+template <int D, bool STRIPED, bool TCAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_pipe_kernel(FwdArgs a) {
   constexpr int BLK = 128;
@@ -884,6 +901,17 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
     auto dead_of = [&](int desc, int j) {
       return STRIPED && !((desc >> (kDescCodeShift + (kb0 + j) / kb_div)) & 1);
     };
+    // token position of the first key of this wave's block j of the tile of `desc`, and the
+    // step between the wave's keys (striped chunk c's compacted position p is token c + C p)
+    const int kstep = STRIPED ? a.n_chunks : 1;
+    auto kpos_of = [&](int desc, int j) {
+      const int key = (desc & 0xFFFFF) * BLK + (kb0 + j) * 32;
+      return STRIPED ? ((desc >> kDescChunkShift) & 63) + a.n_chunks * key : key;
+    };
+    // block j of the tile of `desc` has a key after the wave's first query
+    auto diag_of = [&](int desc, int j) {
+      return TCAUSAL && kpos_of(desc, j) + kstep * 31 > qb * BLK + rg * 32;
+    };
 
     f32x16 sc[NB];       // scores of the two blocks of the next tile to be exponentiated
     PBlock pb[NB];       // probabilities waiting for their P V product
@@ -900,6 +928,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       tile_scores<D, BLK, false>(sK0, qf, ol, 0, sc);
       // block 0 starts an accumulation: its running max goes to m_next, which
       // the first tile takes over (after flushing any empty leading chunks)
+      if (diag_of(d0, 0)) drop_future(sc[0], qrow, kpos_of(d0, 0), kstep, lane >> 5);
       moved[0] = block_softmax(sc[0], sl2, ref_cur, m_next, pb[0], dead_of(d0, 0));
     }
 
@@ -907,7 +936,8 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
     // adds the block's row sum (its P V follows).
     auto consume = [&](const PBlock& p, uint64_t mv) {
       if (mv) {
-        const float alpha = __builtin_amdgcn_exp2f(st.m_ref - p.ref);
+        // (rows that are still empty on both sides keep factor 1)
+        const float alpha = (TCAUSAL && st.m_ref == p.ref) ? 1.f : __builtin_amdgcn_exp2f(st.m_ref - p.ref);
         st.l *= alpha;
 #pragma unroll
         for (int d = 0; d < ND; ++d) st.acc[d] *= alpha;
@@ -928,6 +958,8 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       // the next tile starts a new accumulation (a chunk of its own in partial mode)
       const bool next_new = !full && has_next && chunk_of(desc1) != chunk_of(desc);
       const bool dead_sec[NB] = {dead_of(desc, 1), dead_of(desc1, 0)};  // blocks exponentiated in sections 0, 1
+      const bool diag_sec[NB] = {diag_of(desc, 1), diag_of(desc1, 0)};
+      const int kpos_sec[NB] = {kpos_of(desc, 1), kpos_of(desc1, 0)};
 
       wait_vm();
       __syncthreads();
@@ -975,6 +1007,8 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
         auto stage = [&](auto sc_) {
           constexpr int g = decltype(sc_)::value;
           if constexpr (g == 0) {
+            if constexpr (TCAUSAL)
+              if (diag_sec[j]) drop_future(sc[SRC], qrow, kpos_sec[j], kstep, lane >> 5);
             mx_a = fmaxf(fmaxf(s[0], s[1]), s[2]);
             mx_a = fmaxf(fmaxf(mx_a, s[3]), s[4]);
             mx_a = fmaxf(fmaxf(mx_a, s[5]), s[6]);
@@ -998,7 +1032,8 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
             ref_cur = up ? run : ref_cur;
             out.ref = ref_cur;
             // reference of the exponent: +inf makes a dead block's probabilities 0
-            ref_exp = (STRIPED && dead_sec[j]) ? __builtin_huge_valf() : ref_cur;
+            ref_exp = (STRIPED && dead_sec[j]) ? __builtin_huge_valf()
+                      : (TCAUSAL && ref_cur == kNegInf) ? 0.f : ref_cur;
             moved[SRC] = __builtin_amdgcn_ballot_w64(up);
             if constexpr (j == 0) {
               st.m_true = run;
@@ -1085,8 +1120,11 @@ hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_bins), block(Shape<D, BLK>::NW * 64);
   if constexpr (BLK == 128) {
     // striped chunks (S is then a multiple of block * n_chunks) without token-level causality
-    if (a.layout == SA_LAYOUT_STRIPED && !a.token_causal) {
-      hipLaunchKernelGGL((attn_bf16_pipe_kernel<D, true>), grid, block, 0, stream, a);
+    if (a.layout == SA_LAYOUT_STRIPED) {
+      if (a.token_causal)
+        hipLaunchKernelGGL((attn_bf16_pipe_kernel<D, true, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_bf16_pipe_kernel<D, true, false>), grid, block, 0, stream, a);
       return hipGetLastError();
     }
   }
@@ -1094,9 +1132,9 @@ hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, true, false>), grid, block, 0, stream, a);
   else if constexpr (BLK == 128) {
     if (a.token_causal)
-      hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16_pipe_kernel<D, false, true>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_bf16_pipe_kernel<D, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_bf16_pipe_kernel<D, false, false>), grid, block, 0, stream, a);
   } else if (a.token_causal)
     hipLaunchKernelGGL((attn_bf16_kernel<D, BLK, false, true>), grid, block, 0, stream, a);
   else
