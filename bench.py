@@ -21,7 +21,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode merged|fused]
        [--workload causal|video|skewed|tiny] [--layout contiguous|striped] [--no-cpu-baseline]
        [--no-extras] [--no-workloads] [--no-topk] [--calibrate-copy MiB]
 
-Each step's plan is destroyed inside the timed loop right after the next step is issued (the
+Before the W warmup steps the step is repeated, untimed, for --settle seconds (0.25 by default):
+from idle the GPU needs about 15 steps to reach its sustained clock.  Each step's plan is
+destroyed inside the timed loop right after the next step is issued (the
 library returns its buffers to a cache and reuses them once the kernels that read them are done,
 so no step allocates or synchronises).  The untimed extras also time the other block-sparse
 workloads: the causal one in the other chunk layout, the video and the skewed workload, each as a
@@ -236,7 +238,7 @@ class WorkloadRun:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    def steps(self, order, n, warmup=2):
+    def steps(self, order, n, warmup=2, settle=0.1):
         """ms per whole step (plan on a side stream, partial forward, merge), the previous step's plan
         destroyed inside the loop, and the forward's mean time from HIP events."""
         torch = self.torch
@@ -257,6 +259,13 @@ class WorkloadRun:
             return plan
 
         prev = None
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < settle:
+            p = one(False)
+            if prev is not None:
+                prev.close()
+            prev = p
+            torch.cuda.synchronize()
         for _ in range(warmup):
             p = one(False)
             if prev is not None:
@@ -321,6 +330,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle", type=float, default=0.25,
+                    help="seconds of untimed steps before the warmup steps (the GPU's clock settles)")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="causal")
     ap.add_argument("--layout", choices=["contiguous", "striped"], default="contiguous",
                     help="KV chunk layout: contiguous blocks, or striped (token i in chunk i mod C)")
@@ -336,6 +347,9 @@ def main() -> int:
     ap.add_argument("--no-topk", action="store_true", help="skip the token top-k path measurement")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other block-sparse workloads (striped causal, video, skewed)")
+    ap.add_argument("--topk-only", action="store_true",
+                    help="diagnostic: run only the token top-k path (for profiling its kernels) and print its "
+                         "figures; no block-sparse step, no metric")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -356,6 +370,10 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.topk_only:
+        print(json.dumps({"topk_path": topk_path(bd, W, torch, dev)}), flush=True)
+        return 0
 
     w = W.make(WORKLOADS[args.workload], layout=args.layout)
     run = WorkloadRun(bd, torch, dev, w)
@@ -386,6 +404,15 @@ def main() -> int:
         return plan
 
     prev = None
+    # untimed: bring the GPU to its sustained clock (it takes about 15 steps from idle), then
+    # the W warmup steps
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        p = step(False)
+        if prev is not None:
+            prev.close()
+        prev = p
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         p = step(False)
         if prev is not None:
