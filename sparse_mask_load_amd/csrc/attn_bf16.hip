@@ -29,20 +29,26 @@
 //    a flash-attention pass over a disjoint key subset) and are merged through
 //    LDS with the same rule that merges chunks, when a chunk is flushed and at
 //    the end of the item.
-//  * Each wave is also software-pipelined: per 32-key block it exponentiates
-//    block kb of tile t, issues the S MFMAs of block kb of tile t+1 and the
-//    P V MFMAs of block kb of tile t, all in one basic block.
+//  * Two kernels share this mapping.  The pipelined kernel (128-key tiles, S a
+//    multiple of the block; contiguous or striped chunks, with or without
+//    token-level causality) runs each wave as a stream of 32-key blocks: one
+//    section per block issues the S MFMAs of the block two ahead and the P V
+//    MFMAs of the current block, each MFMA slot also holding the LDS operand
+//    reads four MFMAs ahead and one stage of the next block's softmax, with
+//    scheduling fences between the slots.  The general kernel (64-key tiles,
+//    ragged S) takes the row max per tile and reads operands just before use.
 //  * K and V tiles are double-buffered in LDS (128 KiB for 128-key tiles, four
 //    separate arrays so that the compiler can tell operand reads from loads in
-//    flight) and filled by global_load_lds_dwordx4 (no VGPR staging) one tile
-//    ahead, in slices spread over the key blocks, with one workgroup barrier
-//    per tile.  16-byte chunks are XOR-swizzled per row so that the operand
-//    reads are free of bank conflicts.
+//    flight) and filled by buffer_load_dwordx4 ... lds (no VGPR staging), with
+//    one workgroup barrier per tile.  16-byte chunks are XOR-swizzled per row
+//    so that the operand reads are free of bank conflicts.
 //  * exp is exp2 on scores pre-multiplied by scale*log2(e).  The reference max
-//    used in the exponent only moves when a row's max grows by more than 2^8
-//    (the result O/l does not depend on the reference), so O is rarely
-//    rescaled; the true row max is tracked and the exported partial is
-//    converted to it, in natural-log units.  The row sum adds the bf16-rounded
+//    used in the exponent only moves when a row's max grows by more than a
+//    factor 2^8 (the result O/l does not depend on the reference), so O is
+//    rarely rescaled (the pipelined kernel checks per 32-key block and brings
+//    the accumulators to a block's reference just before that block's P V);
+//    the true row max is tracked and the exported partial is converted to it,
+//    in natural-log units.  The row sum adds the bf16-rounded
 //    P values that also feed P V (v_dot2c_f32_bf16).
 #include <hip/hip_runtime.h>
 
