@@ -49,7 +49,7 @@ METRIC = "live-block attention TFLOP/s + % bf16 MFMA peak; per-CU max/mean work"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0
 WORKLOADS = {"tiny": 1, "video": 2, "causal": 3, "skewed": 4}
-KERNEL_NAME = "attn_bf16_kernel"
+PAIR_OVERHEAD_MAX = 1.05  # Q-block pairs when the union tiles they compute exceed the live tiles by at most 5%
 KERNEL_SOURCES = ["sparse_mask_load_amd/csrc/attn_bf16.hip", "sparse_mask_load_amd/csrc/kernel_common.h",
                   "sparse_mask_load_amd/csrc/internal.h"]
 
@@ -183,7 +183,7 @@ def topk_path(bd, W, torch, dev, reps: int = 5) -> dict:
 class WorkloadRun:
     """One block-sparse workload resident on the GPU: Q, K, V, mask, chunk partials, output."""
 
-    def __init__(self, bd, torch, dev, w, layout=None):
+    def __init__(self, bd, torch, dev, w, layout=None, q_pairs="auto"):
         self.bd, self.torch, self.w = bd, torch, w
         dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         self.q, self.k, self.v = (torch.from_numpy(x).to(dev, dt) for x in (w.q, w.k, w.v))
@@ -192,7 +192,20 @@ class WorkloadRun:
         B, H, S, D = self.q.shape
         C = w.n_chunks
         self.B, self.H, self.S, self.D, self.C = B, H, S, D, C
-        self.prob = bd.make_problem(self.q, w.block, C, self.layout)
+        self.prob_single = bd.make_problem(self.q, w.block, C, self.layout)
+        # Q-block pair items where the kernel has them and adjacent mask rows share their tiles:
+        # the pairs' union tiles (what the pair kernel computes) against the live tiles
+        self.q_pairs, self.pair_overhead = False, None
+        if q_pairs != "off" and w.dtype == "bf16" and w.block == 128 and self.layout == "contiguous" and S % 128 == 0:
+            prob_p = bd.make_problem(self.q, w.block, C, self.layout, q_pairs=True)
+            p = bd.sparse_attn_plan(prob_p, "block", mask=self.mask, order="lpt")
+            info = bd.sparse_attn_plan_info(p)
+            p.close()
+            self.pair_overhead = 2.0 * info["load_sum"] / max(1, info["total_live"])
+            self.q_pairs = q_pairs == "on" or self.pair_overhead <= PAIR_OVERHEAD_MAX
+        elif q_pairs == "on":
+            raise SystemExit("--q-pairs on needs a bf16 workload with block 128, contiguous chunks, S % 128 == 0")
+        self.prob = bd.make_problem(self.q, w.block, C, self.layout, q_pairs=self.q_pairs)
         self.o_part = torch.empty((C, B, H, S, D), dtype=torch.float32, device=dev)
         self.m_part = torch.empty((C, B, H, S), dtype=torch.float32, device=dev)
         self.l_part = torch.empty((C, B, H, S), dtype=torch.float32, device=dev)
@@ -224,6 +237,16 @@ class WorkloadRun:
 
     def flop(self, total_live):
         return 4.0 * self.w.block * self.w.block * self.D * total_live
+
+    def kernel_name(self):
+        """The attention kernel the forward call launches for this workload."""
+        if self.w.dtype != "bf16":
+            return "attn_f32_kernel"
+        if self.q_pairs:
+            return "attn_bf16_pair_kernel"
+        if self.w.block == 128 and (self.layout == "striped" or self.S % 128 == 0):
+            return "attn_bf16_pipe_kernel"
+        return "attn_bf16_kernel"
 
     def timed(self, fn, reps):
         """Mean time of fn() over reps launches (HIP events on the current stream, one untimed launch first)."""
@@ -307,13 +330,16 @@ def workload_summary(bd, W, torch, dev, cfg, layout="contiguous", steps=10, reps
     merge) and its forward in device-planned LPT, host LPT and round-robin order."""
     w = W.make(cfg, layout=layout)
     run = WorkloadRun(bd, torch, dev, w)
+    items = "Q-block pairs" if run.q_pairs else "Q-blocks"
     p = run.plan("lpt_device")
     info = bd.sparse_attn_plan_info(p)
     p.close()
     flop = run.flop(info["total_live"])
     step_ms, fwd_ms = run.steps("lpt_device", steps)
     merge_ms = run.timed(run.merge, reps)
-    out = {"workload": f"{w.name} B{run.B} H{run.H} S{run.S} d{run.D} block {w.block}, {run.C} {layout} chunks",
+    out = {"workload": f"{w.name} B{run.B} H{run.H} S{run.S} d{run.D} block {w.block}, {run.C} {layout} chunks, "
+                       f"work items: {items}",
+           "kernel": run.kernel_name(), "pair_overhead": run.pair_overhead,
            "live_tiles": info["total_live"], "flop": flop,
            "ms_per_step": round(step_ms, 4), "step_tflops": round(flop / step_ms / 1e9, 2),
            "step_pct_bf16_peak": round(100 * flop / step_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
@@ -341,6 +367,9 @@ def main() -> int:
                     help="work order: two-level LPT (heads to XCDs, then Q-blocks), one-level LPT, round-robin, "
                          "round-based LPT made on the GPU")
     ap.add_argument("--bins", type=int, default=0, help="persistent workgroups (0: one per resident slot)")
+    ap.add_argument("--q-pairs", choices=["auto", "on", "off"], default="auto",
+                    help="work items of two adjacent Q-blocks (auto: where their union tiles exceed the live "
+                         f"tiles by at most {round(100 * (PAIR_OVERHEAD_MAX - 1))}%%)")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the untimed breakdown runs")
@@ -376,7 +405,7 @@ def main() -> int:
         return 0
 
     w = W.make(WORKLOADS[args.workload], layout=args.layout)
-    run = WorkloadRun(bd, torch, dev, w)
+    run = WorkloadRun(bd, torch, dev, w, q_pairs=args.q_pairs)
     q, k, v, mask, out = run.q, run.k, run.v, run.mask, run.out
     B, H, S, D, C = run.B, run.H, run.S, run.D, run.C
     prob = run.prob
@@ -445,15 +474,17 @@ def main() -> int:
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name} block-sparse MHA B{B} H{H} S{S} d{D} block {w.block}, "
                                f"{C} {args.layout} KV chunks {'merged by chunk_merge' if args.mode == 'merged' else 'folded in-kernel'}, "
+                               f"work items: {'Q-block pairs' if run.q_pairs else 'Q-blocks'}, "
                                f"{ {'lpt_xcd': 'two-level LPT (heads to XCDs, then Q-blocks)', 'lpt': 'LPT', 'naive': 'round-robin', 'lpt_device': 'round-based LPT made on the GPU'}[args.order]} over {info['num_bins']} bins",
                    "B": B, "H": H, "S": S, "D": D, "block": w.block, "n_chunks": C, "layout": args.layout,
                    "mask": {"tiny": "Bernoulli(0.5)+diag", "video": "frame band / Bernoulli",
                             "causal": "block lower-triangular", "skewed": "Zipf(1.2) rows"}[args.workload],
-                   "live_tiles": info["total_live"], "mode": args.mode, "order": args.order},
+                   "live_tiles": info["total_live"], "mode": args.mode, "order": args.order,
+                   "q_pairs": run.q_pairs},
         "pct_bf16_peak_step": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": read_counter_traffic(traffic_key),
-                     "kernel": KERNEL_NAME, "kernel_ms": round(kernel_ms, 4),
+                     "kernel": run.kernel_name(), "kernel_ms": round(kernel_ms, 4),
                      "kernel_source_hash": kernel_source_hash()},
         "per_cu_work": {"planned_bin_max_over_mean": round(float(bin_load.max() / bin_load.mean()), 4),
                         "planned_makespan_tiles": info["makespan"], "lower_bound_tiles": info["lower_bound"]},
@@ -505,7 +536,8 @@ def main() -> int:
             alt_ms[alt] = (run.timed(lambda: run.fwd_fused(p_alt), reps), bd.sparse_attn_plan_info(p_alt))
             p_alt.close()
         # the same mask with token-level causality inside the live tiles
-        p_tc = run.plan(args.order, prob=bd.make_problem(q, w.block, C, args.layout, token_causal=True))
+        p_tc = run.plan(args.order, prob=bd.make_problem(q, w.block, C, args.layout, token_causal=True,
+                                                         q_pairs=run.q_pairs))
         tc_ms = run.timed(lambda: run.fwd_fused(p_tc), reps)
         p_tc.close()
         # the partial-mode forward with cold caches: a 512 MiB write first evicts the L2s and
@@ -528,6 +560,13 @@ def main() -> int:
         torch.cuda.synchronize()
         naive_balance = per_cu_balance(tr_naive.cpu().numpy())
         p_naive.close()
+        # the same step's forward with single Q-block items (when the step uses pairs)
+        single = {}
+        if run.q_pairs:
+            p_s = run.plan(args.order, prob=run.prob_single)
+            single = {"fwd_partial_single_items_ms": round(run.timed(lambda: run.fwd_partial(p_s), reps), 4),
+                      "fwd_fused_single_items_ms": round(run.timed(lambda: run.fwd_fused(p_s), reps), 4)}
+            p_s.close()
         props = torch.cuda.get_device_properties(dev)
         result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                             "compute_units": props.multi_processor_count, "peak_clock_mhz": peak_clock_mhz(dev.index or 0)}
@@ -545,6 +584,7 @@ def main() -> int:
             "fwd_fused_token_causal_ms": round(tc_ms, 4),
             "plan_device_call_ms": round(plan_device_call_ms, 4), "plan_device_gpu_ms": round(plan_device_gpu_ms, 4),
             "ms_per_step_by_planner": {args.order: round(ms_per_step, 4), other_order: round(step_other_ms, 4)},
+            "pair_overhead": run.pair_overhead, **single,
         }
     plan.close()
 

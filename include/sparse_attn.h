@@ -63,7 +63,8 @@ typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  *                    post notes that they add planning overhead): items in LPT
  *                    order are handed out num_bins per round, the round's j-th
  *                    item to the j-th least-loaded bin (lower index on ties).
- *                    Block plans only; at most 16384 (b, h, Q-block) items and
+ *                    Block plans only; at most 16384 work items (b, h, Q-block
+ *                    or, with q_pairs, Q-block pair) and
  *                    1024 bins (else SA_ERR_UNSUPPORTED).  The plan call then
  *                    never waits for the device: popcount and every list
  *                    (full range and each chunk) are made on `stream`, and
@@ -83,6 +84,14 @@ typedef enum { SA_KIND_BLOCK = 0, SA_KIND_TOPK = 1, SA_KIND_INDEX = 2 } sa_kind;
  *            j with j % C == c; requires S % (block*C) == 0 and block/C a
  *            multiple of 32.
  *  scale     softmax scale; <= 0 selects 1/sqrt(D).
+ *  q_pairs   non-zero: a work item is the Q-block pair (2p, 2p+1) of one
+ *            (batch, head) instead of one Q-block, so every K/V tile the kernel
+ *            stages feeds 256 query rows; the pair visits the union of its two
+ *            mask rows' live tiles (a tile live for one row only is computed
+ *            with zero probabilities for the other), and the LPT loads are
+ *            those union counts.  Block plans, bf16, block 128, contiguous
+ *            layout, S % 128 == 0 (else SA_ERR_UNSUPPORTED).  Worth it where
+ *            adjacent mask rows share most tiles (causal, banded masks).
  *  sb,sh,ss  element strides of the b, h and s axes of Q, K, V and O. */
 typedef struct {
   int32_t B, H, S, D;
@@ -94,6 +103,7 @@ typedef struct {
   int32_t token_causal; /* non-zero: inside live tiles, key j is also dropped for query i when
                            j > i (token positions; striped chunks use each key's original
                            position), i.e. causal attention at token granularity */
+  int32_t q_pairs;      /* non-zero: work items are Q-block pairs (see above) */
   int64_t sb, sh, ss;
 } sa_problem;
 
@@ -130,7 +140,8 @@ typedef struct {
   int32_t kind, num_bins, order, n_chunks;
   int32_t nQ, nK, n_items, top_k;
   int64_t total_live;   /* BLOCK: live (Q-block, KV-block) tiles; TOPK/INDEX: selected pairs */
-  int64_t load_sum;     /* sum of the full-range item loads (= total_live for BLOCK) */
+  int64_t load_sum;     /* sum of the full-range item loads (= total_live for BLOCK without
+                           q_pairs; with q_pairs the sum of the pairs' union counts) */
   int64_t makespan;     /* max bin load of the full-range list */
   int64_t lower_bound;  /* max(max item load, ceil(load_sum / num_bins)) */
                         /* (SA_ORDER_LPT_DEVICE: the call waits for the plan to read these) */
@@ -143,11 +154,14 @@ typedef enum {
   SA_PLAN_ROW = 0,      /* int32 [B][H][nQ]   live tiles per Q-block (mask row sums)      */
   SA_PLAN_COL = 1,      /* int32 [B][H][nK]   live tiles per KV-block (mask column sums)  */
   SA_PLAN_CROW = 2,     /* int32 [B][H][C][nQ] per-chunk row counts (striped: = row)      */
-  SA_PLAN_ITEMS = 3,    /* int32 [n_items]    item ids (b*H + h)*nQ + q, bins concatenated */
+  SA_PLAN_ITEMS = 3,    /* int32 [n_items]    item ids (b*H + h)*nQ + q, bins concatenated;
+                                             q_pairs: (b*H + h)*nP + p, nP = ceil(nQ/2) */
   SA_PLAN_BIN_PTR = 4,  /* int32 [num_bins+1] offsets of each bin's list in ITEMS          */
   SA_PLAN_BIN_LOAD = 5, /* int64 [num_bins]   sum of item loads per bin                    */
   SA_PLAN_TOPK_IDX = 6, /* int32 [B][H][S][top_k] selected keys (TOPK/INDEX)              */
-  SA_PLAN_TOPK_COUNT = 7 /* int32 [B][H][S]   number of selected keys                     */
+  SA_PLAN_TOPK_COUNT = 7, /* int32 [B][H][S]  number of selected keys                     */
+  SA_PLAN_PAIR_ROW = 8,   /* int32 [B][H][nP]  q_pairs: live tiles of the union of rows 2p, 2p+1 */
+  SA_PLAN_PAIR_CROW = 9   /* int32 [B][H][C][nP] q_pairs: the same per chunk                  */
 } sa_plan_array;
 
 /* Build a plan.
@@ -200,9 +214,10 @@ sa_status sparse_attn_fwd(const sa_plan* plan, const void* q, const void* k, con
  *  `stream`; the call never waits for the device.
  *  mask: uint8 [B][H][nQ][nK] as for a block plan, 16-byte aligned, read on
  *  the stream (keep it alive until the work is done); it is not copied.
- *  Limits: B*H*nQ <= 16384 and num_bins <= 1024 (as for SA_ORDER_LPT_DEVICE),
- *  and the counts and list must fit the array (about B*H*nQ*(n_chunks + 3)*4
- *  bytes); beyond them SA_ERR_UNSUPPORTED.  Other arguments as for
+ *  Limits: at most 16384 work items (B*H*nQ, or B*H*ceil(nQ/2) with q_pairs)
+ *  and num_bins <= 1024 (as for SA_ORDER_LPT_DEVICE), and the counts and list
+ *  must fit the array (about B*H*nQ*(n_chunks + 3)*4 bytes, half as much
+ *  again with q_pairs); beyond them SA_ERR_UNSUPPORTED.  Other arguments as for
  *  sparse_attn_plan and sparse_attn_fwd. */
 sa_status sparse_attn_fwd_noalloc(const sa_problem* prob, const uint8_t* mask, int32_t num_bins, const void* q,
                                   const void* k, const void* v, int32_t chunk_begin, int32_t chunk_end, void* o,

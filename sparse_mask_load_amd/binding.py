@@ -22,7 +22,7 @@ SA_ORDER_LPT, SA_ORDER_NAIVE, SA_ORDER_LPT_XCD, SA_ORDER_LPT_DEVICE = 0, 1, 2, 3
 SA_LAYOUT_CONTIGUOUS, SA_LAYOUT_STRIPED = 0, 1
 SA_KIND_BLOCK, SA_KIND_TOPK, SA_KIND_INDEX = 0, 1, 2
 (SA_PLAN_ROW, SA_PLAN_COL, SA_PLAN_CROW, SA_PLAN_ITEMS, SA_PLAN_BIN_PTR, SA_PLAN_BIN_LOAD,
- SA_PLAN_TOPK_IDX, SA_PLAN_TOPK_COUNT) = range(8)
+ SA_PLAN_TOPK_IDX, SA_PLAN_TOPK_COUNT, SA_PLAN_PAIR_ROW, SA_PLAN_PAIR_CROW) = range(10)
 
 _DTYPES = {"f32": SA_F32, "bf16": SA_BF16}
 _ORDERS = {"lpt": SA_ORDER_LPT, "naive": SA_ORDER_NAIVE, "lpt_xcd": SA_ORDER_LPT_XCD,
@@ -40,7 +40,8 @@ class sa_problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("S", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("n_chunks", ctypes.c_int32), ("layout", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("token_causal", ctypes.c_int32),
-                ("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("ss", ctypes.c_int64)]
+                ("q_pairs", ctypes.c_int32), ("sb", ctypes.c_int64), ("sh", ctypes.c_int64),
+                ("ss", ctypes.c_int64)]
 
 
 class sa_sparsity(ctypes.Structure):
@@ -121,7 +122,7 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_problem(q, block: int = 0, n_chunks: int = 1, layout: str = "contiguous",
-                 scale: float = 0.0, token_causal: bool = False) -> sa_problem:
+                 scale: float = 0.0, token_causal: bool = False, q_pairs: bool = False) -> sa_problem:
     """Describe a [B, H, S, D] tensor (last dim contiguous) as an sa_problem."""
     import torch
     if q.dim() != 4 or q.stride(-1) != 1:
@@ -129,7 +130,7 @@ def make_problem(q, block: int = 0, n_chunks: int = 1, layout: str = "contiguous
     dtype = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}[q.dtype]
     B, H, S, D = q.shape
     return sa_problem(B, H, S, D, block, n_chunks, _LAYOUTS[layout], dtype, float(scale), 1 if token_causal else 0,
-                      q.stride(0), q.stride(1), q.stride(2))
+                      1 if q_pairs else 0, q.stride(0), q.stride(1), q.stride(2))
 
 
 class Plan:

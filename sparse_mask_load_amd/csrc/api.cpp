@@ -23,6 +23,8 @@ struct sa_plan {
   int32_t order = SA_ORDER_LPT;
   int32_t groups = 1;  // bin groups of SA_ORDER_LPT_XCD (one per XCD), else 1
   int32_t nQ = 0, nK = 0, n_items = 0, top_k = 0, rank = 0, causal = 0;
+  int32_t nI = 0;        // items per (batch, head): nQ, or the pair count ceil(nQ/2) with q_pairs
+  bool q_pairs = false;  // items are Q-block pairs
   int device = 0;
   int32_t n_xcd = 1;  // L2 domains (XCDs) of the device
   // BLOCK
@@ -30,6 +32,8 @@ struct sa_plan {
   int32_t* d_row = nullptr;          // [B*H*nQ]
   int32_t* d_col = nullptr;          // [B*H*nK]
   int32_t* d_crow = nullptr;         // [B*H*C*nQ]
+  int32_t* d_prow = nullptr;         // q_pairs: [B*H*nI] union counts of each pair
+  int32_t* d_pcrow = nullptr;        // q_pairs: [B*H*C*nI] the same per chunk
   int32_t* d_items = nullptr;        // [(C+1)][n_items]: list 0 = full range, list 1+c = chunk c
   int32_t* d_bin_ptr = nullptr;      // [(C+1)][num_bins+1]
   // SA_ORDER_LPT_DEVICE: every list is made on the device; loads and statistics stay there
@@ -40,7 +44,7 @@ struct sa_plan {
   std::vector<int64_t> h_bin_load;   // [(C+1)][num_bins]
   // The full-range list is built by the plan call; the list of chunk c (used by forward calls
   // over that chunk alone, as in one ring step) is built on first use from the host counts.
-  std::vector<int32_t> h_crow;       // [B*H*C*nQ] per-chunk row counts
+  std::vector<int32_t> h_crow;       // [B*H*C*nI] per-chunk item loads (row or pair counts)
   std::unique_ptr<std::once_flag[]> list_once;
   std::unique_ptr<bool[]> list_uploaded;
   std::mutex upload_mutex;
@@ -101,6 +105,7 @@ sa_status validate_problem(const sa_problem* p, bool block_kind) {
     if (p->token_causal)
       return fail(SA_ERR_INVALID, "token_causal applies to block plans (top-k and index plans take causality "
                                   "from their key selection)");
+    if (p->q_pairs) return fail(SA_ERR_INVALID, "q_pairs applies to block plans");
     return SA_OK;
   }
   if (p->dtype == SA_BF16 && p->block != 64 && p->block != 128)
@@ -121,6 +126,8 @@ sa_status validate_problem(const sa_problem* p, bool block_kind) {
   } else if (p->layout != SA_LAYOUT_CONTIGUOUS) {
     return fail(SA_ERR_INVALID, "unknown layout %d", p->layout);
   }
+  if (p->q_pairs && (p->dtype != SA_BF16 || p->block != 128 || p->layout != SA_LAYOUT_CONTIGUOUS || p->S % 128))
+    return fail(SA_ERR_UNSUPPORTED, "q_pairs needs bf16, block 128, the contiguous layout and S %% 128 == 0");
   return SA_OK;
 }
 
@@ -243,7 +250,7 @@ int default_bins(const sa_problem& p, int device) {
 void assign_list(const sa_plan* P, const int64_t* loads, int32_t* items, int32_t* bin_ptr, int64_t* bin_load) {
   const int m = P->num_bins, n = P->n_items;
   if (P->order == SA_ORDER_LPT_XCD)
-    sa::assign_grouped(loads, n / P->nQ, P->nQ, m, P->groups, items, bin_ptr, bin_load);
+    sa::assign_grouped(loads, n / P->nI, P->nI, m, P->groups, items, bin_ptr, bin_load);
   else
     sa::assign(loads, n, m, P->order, items, bin_ptr, bin_load);
 }
@@ -261,7 +268,10 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   const int BH = pr.B * pr.H, C = pr.n_chunks;
   P->nQ = P->nK = (pr.S + pr.block - 1) / pr.block;
   const int nQ = P->nQ, nK = P->nK;
-  P->n_items = BH * nQ;
+  P->q_pairs = pr.q_pairs != 0;
+  P->nI = P->q_pairs ? (nQ + 1) / 2 : nQ;
+  const int nI = P->nI;
+  P->n_items = BH * nI;
   if (!sp->mask) return fail(SA_ERR_INVALID, "mask is NULL");
   const size_t mask_bytes = (size_t)BH * nQ * nK;
   sa_status st;
@@ -270,21 +280,32 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
       (st = dalloc(P, &P->d_items, (size_t)(C + 1) * P->n_items, stream)) ||
       (st = dalloc(P, &P->d_bin_ptr, (size_t)(C + 1) * (P->num_bins + 1), stream)))
     return st;
+  if (P->q_pairs && ((st = dalloc(P, &P->d_prow, (size_t)BH * nI, stream)) ||
+                     (st = dalloc(P, &P->d_pcrow, (size_t)BH * C * nI, stream))))
+    return st;
   SA_HIP(hipMemcpyAsync(P->d_mask, sp->mask, mask_bytes, hipMemcpyDeviceToDevice, stream));
-  SA_HIP(sa::launch_popcount(P->d_mask, BH, nQ, nK, C, pr.layout, P->d_row, P->d_col, P->d_crow, stream));
+  SA_HIP(sa::launch_popcount(P->d_mask, BH, nQ, nK, C, pr.layout, P->d_row, P->d_col, P->d_crow, stream, P->d_prow,
+                             P->d_pcrow));
+  // item loads: mask row counts, or the union counts of Q-block pairs
+  const int32_t* d_load = P->q_pairs ? P->d_prow : P->d_row;
+  const int32_t* d_cload = P->q_pairs ? P->d_pcrow : P->d_crow;
   if (P->order == SA_ORDER_LPT_DEVICE) {
     // every list on the device, right behind the popcount: nothing waits for the host
     if ((st = dalloc(P, &P->d_bin_load, (size_t)(C + 1) * P->num_bins, stream)) ||
         (st = dalloc(P, &P->d_stats, (size_t)(C + 1) * 4, stream)))
       return st;
-    SA_HIP(sa::launch_plan_rounds(P->d_row, P->d_crow, BH, nQ, C, P->num_bins, P->d_items, P->d_bin_ptr,
+    SA_HIP(sa::launch_plan_rounds(d_load, d_cload, BH, nI, C, P->num_bins, P->d_items, P->d_bin_ptr,
                                   P->d_bin_load, P->d_stats, stream));
     P->device_lists = true;
     return SA_OK;
   }
-  std::vector<int32_t> row((size_t)BH * nQ), crow((size_t)BH * C * nQ);
-  SA_HIP(hipMemcpyAsync(row.data(), P->d_row, row.size() * 4, hipMemcpyDeviceToHost, stream));
-  SA_HIP(hipMemcpyAsync(crow.data(), P->d_crow, crow.size() * 4, hipMemcpyDeviceToHost, stream));
+  std::vector<int32_t> row((size_t)BH * nI), crow((size_t)BH * C * nI), qrow;
+  SA_HIP(hipMemcpyAsync(row.data(), d_load, row.size() * 4, hipMemcpyDeviceToHost, stream));
+  SA_HIP(hipMemcpyAsync(crow.data(), d_cload, crow.size() * 4, hipMemcpyDeviceToHost, stream));
+  if (P->q_pairs) {
+    qrow.resize((size_t)BH * nQ);
+    SA_HIP(hipMemcpyAsync(qrow.data(), P->d_row, qrow.size() * 4, hipMemcpyDeviceToHost, stream));
+  }
   SA_HIP(hipStreamSynchronize(stream));
 
   const int m = P->num_bins, n = P->n_items;
@@ -306,6 +327,10 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   }
   P->load_sum = sum;
   P->total_live = sum;  // every live tile belongs to exactly one Q-block row
+  if (P->q_pairs) {
+    P->total_live = 0;
+    for (int32_t x : qrow) P->total_live += x;
+  }
   P->makespan = *std::max_element(P->h_bin_load.begin(), P->h_bin_load.begin() + m);
   P->lower_bound = std::max<int64_t>(pmax, (sum + m - 1) / m);
   SA_HIP(hipMemcpyAsync(P->d_items, P->h_items.data(), (size_t)n * 4, hipMemcpyHostToDevice, stream));
@@ -317,9 +342,9 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
 // Host lists of chunk `list - 1` (LPT or round-robin over the chunk's row counts), once.
 void build_chunk_list(sa_plan* P, int list) {
   std::call_once(P->list_once[list], [P, list] {
-    const int C = P->prob.n_chunks, nQ = P->nQ, n = P->n_items, m = P->num_bins, c = list - 1;
+    const int C = P->prob.n_chunks, nI = P->nI, n = P->n_items, m = P->num_bins, c = list - 1;
     std::vector<int64_t> loads(n);
-    for (int i = 0; i < n; ++i) loads[i] = P->h_crow[((size_t)(i / nQ) * C + c) * nQ + i % nQ];
+    for (int i = 0; i < n; ++i) loads[i] = P->h_crow[((size_t)(i / nI) * C + c) * nI + i % nI];
     assign_list(P, loads.data(), P->h_items.data() + (size_t)list * n, P->h_bin_ptr.data() + (size_t)list * (m + 1),
                 P->h_bin_load.data() + (size_t)list * m);
   });
@@ -445,7 +470,7 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
   if (num_bins < 0) return fail(SA_ERR_INVALID, "num_bins %d < 0", num_bins);
   if (order == SA_ORDER_LPT_DEVICE && sp->kind == SA_KIND_BLOCK) {
     const int64_t nQ = (prob->S + prob->block - 1) / prob->block;
-    const int64_t n_items = (int64_t)prob->B * prob->H * nQ;
+    const int64_t n_items = (int64_t)prob->B * prob->H * (prob->q_pairs ? (nQ + 1) / 2 : nQ);
     if (n_items > sa::kDevicePlanMaxItems || num_bins > sa::kDevicePlanMaxBins)
       return fail(SA_ERR_UNSUPPORTED, "device planning takes at most %d items and %d bins (got %lld, %d)",
                   sa::kDevicePlanMaxItems, sa::kDevicePlanMaxBins, (long long)n_items, num_bins);
@@ -525,6 +550,8 @@ sa_status sparse_attn_fwd(const sa_plan* P, const void* q, const void* k, const 
   a.B = pr.B; a.H = pr.H; a.S = pr.S; a.nQ = P->nQ; a.nK = P->nK; a.n_chunks = pr.n_chunks;
   a.layout = pr.layout; a.c0 = chunk_begin; a.c1 = chunk_end; a.num_bins = P->num_bins;
   a.token_causal = pr.token_causal ? 1 : 0;
+  a.q_pairs = P->q_pairs ? 1 : 0;
+  a.nI = P->nI;
   a.sb = pr.sb; a.sh = pr.sh; a.ss = pr.ss;
   a.scale = effective_scale(pr);
   a.scale_log2 = a.scale * 1.4426950408889634f;
@@ -579,6 +606,12 @@ sa_status sparse_attn_plan_info(const sa_plan* P, sa_plan_info* out) {
     SA_HIP(hipEventSynchronize(P->ready));
     SA_HIP(hipMemcpy(s, P->d_stats, sizeof(s), hipMemcpyDeviceToHost));
     out->total_live = out->load_sum = s[0];
+    if (P->q_pairs) {  // the list loads are union counts; the live tiles are the row sums
+      std::vector<int32_t> row((size_t)P->prob.B * P->prob.H * P->nQ);
+      SA_HIP(hipMemcpy(row.data(), P->d_row, row.size() * 4, hipMemcpyDeviceToHost));
+      out->total_live = 0;
+      for (int32_t x : row) out->total_live += x;
+    }
     out->makespan = s[2];
     out->lower_bound = s[3];
   }
@@ -608,6 +641,8 @@ sa_status sparse_attn_plan_copy(const sa_plan* P, int32_t what, int32_t chunk, v
     case SA_PLAN_ROW: src = P->d_row; count = block ? BH * P->nQ : 0; break;
     case SA_PLAN_COL: src = P->d_col; count = block ? BH * P->nK : 0; break;
     case SA_PLAN_CROW: src = P->d_crow; count = block ? BH * C * P->nQ : 0; break;
+    case SA_PLAN_PAIR_ROW: src = P->d_prow; count = P->q_pairs ? BH * P->nI : 0; break;
+    case SA_PLAN_PAIR_CROW: src = P->d_pcrow; count = P->q_pairs ? BH * C * P->nI : 0; break;
     case SA_PLAN_ITEMS:
       device = P->device_lists;
       src = device ? (const void*)(P->d_items + (size_t)list * P->n_items)

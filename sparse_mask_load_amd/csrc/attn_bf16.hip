@@ -1120,11 +1120,332 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
   }
 }
 
+// Q-block pairs (contiguous layout, S a multiple of 128): an item is the two
+// Q-blocks 2p and 2p+1 of one (batch, head), 256 query rows, so each K/V tile
+// staged in LDS feeds twice the queries of a single-block item.  Wave w owns
+// the 32 rows 32*(w%4) of Q-block 2p + w/4 and all four 32-key blocks of every
+// tile, so no key halves are merged.  The tile list is the union of both mask
+// rows; a tile that is live for one Q-block only is dead for the other's waves
+// (a dead block's probabilities are 0; its MFMAs still run).
+//
+// Each wave's block stream has four blocks per tile, pipelined as in the
+// single-block kernel: the S MFMAs of block b+2 and the P V MFMAs of block b
+// issue while the vector units take block b+1's softmax.  A tile is worked in
+// two halves with a workgroup barrier before each.  The first half (P V of
+// blocks 0-1) takes the S of blocks 2-3 from this tile's K and loads the next
+// tile's V into the V buffer the previous tile used; the second half (P V of
+// blocks 2-3) takes the S of the next tile's blocks 0-1 from the next K and
+// loads K of the tile after next into this tile's K buffer, which the first
+// half was the last to read.  TCAUSAL: token-level causality as in the
+// single-block kernel.
+template <int D, bool TCAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_pair_kernel(FwdArgs a) {
+  constexpr int BLK = 128;
+  using SH = Shape<D, BLK>;
+  constexpr int ND = SH::ND, NKS = SH::NKS;
+  static_assert(SH::NW * 64 == 512, "launch bounds");
+  constexpr int NOPS = NKS + 2 * ND;  // MFMAs of one section: S of one block, then P V of one block
+  constexpr int AHEAD = 4;            // operands read this many MFMAs ahead
+  constexpr int LPS = SH::IPW;        // load instructions of one K or V tile per wave
+  static_assert(LPS % 2 == 0 && LPS / 2 <= NOPS, "a half-tile's loads spread over its two sections");
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[SH::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[SH::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[SH::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[SH::TILE];
+  __shared__ int sList[kMaxTilesPerRow];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave >> 2, rg = wave & 3;  // Q-block of the pair, row group within it
+  const bool full = a.o != nullptr;
+  TileLoader<D, BLK> loader;
+  loader.init(wave, lane);
+  loader.set_stride((int)a.ss);
+  OperandLanes<D, true> ol;
+  ol.init(lane, 0);
+  const bf16* __restrict__ gQ = (const bf16*)a.q;
+  const bf16* __restrict__ gK = (const bf16*)a.k;
+  const bf16* __restrict__ gV = (const bf16*)a.v;
+  const int bin = blockIdx.x;
+  const int p_begin = a.bin_ptr[bin], p_end = a.bin_ptr[bin + 1];
+  const float sl2 = a.scale_log2;
+
+  for (int pos = p_begin; pos < p_end; ++pos) {
+    const int64_t t_start = realtime_now();
+    const int item = a.items[pos];
+    const int pr = item % a.nI;
+    const int bh = item / a.nI;
+    const int b = bh / a.H, h = bh % a.H;
+    const int64_t bh_base = (int64_t)b * a.sb + (int64_t)h * a.sh;
+    const int qa = 2 * pr;              // first Q-block of the pair
+    const int qb = qa + half;           // this wave's Q-block
+    const bool absent = qb >= a.nQ;     // second half of the last pair of an odd nQ: computes, never stores
+    const int qrow = qb * BLK + rg * 32 + (lane & 31);
+
+    bf16x8 qf[NKS];
+    {
+      const bf16* qp = gQ + bh_base + (int64_t)(absent ? qrow - BLK : qrow) * a.ss + 8 * (lane >> 5);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
+    }
+
+    __syncthreads();  // every wave is done with the previous item's list and tiles
+    const int n_tiles = build_pair_tile_list(a.mask + ((int64_t)bh * a.nQ + qa) * a.nK, qa + 1 < a.nQ, a.nK,
+                                             a.n_chunks, a.c0, a.c1, sList, wave == 0);
+    __syncthreads();
+
+    RowState<ND> st;  // acc and l relative to st.m_ref (the reference of the last consumed block)
+    reset(st);
+    int cur_chunk = a.c0;
+
+    // Writes chunk `chunk`'s partial of this wave's rows (O unnormalised, m, l in
+    // the true-max basis) straight from the registers and resets the state.
+    auto flush_partial = [&](int chunk) {
+      const int ln = opaque(lane), l32 = ln & 31, h2 = ln >> 5;
+      const bool any = st.m_true != kNegInf;
+      const float corr = any ? __builtin_amdgcn_exp2f(st.m_ref - st.m_true) : 0.f;
+      const float l_row = (st.l + other_half(st.l)) * corr;
+      if (!absent) {
+        const int64_t prow =
+            ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK + rg * 32 + l32;
+        float* const op = a.o_part + prow * D + 4 * h2;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v4 = {st.acc[d][4 * g] * corr, st.acc[d][4 * g + 1] * corr, st.acc[d][4 * g + 2] * corr,
+                              st.acc[d][4 * g + 3] * corr};
+            *(f32x4*)(op + d * 32 + 8 * g) = v4;
+          }
+        if (h2 == 0) {
+          a.m_part[prow] = any ? st.m_true * kLn2 : kNegInf;
+          a.l_part[prow] = l_row;
+        }
+      }
+      reset(st);
+    };
+    auto src_of = [&](int desc) {
+      return tile_source(desc, bh_base, a.ss, a.S, SA_LAYOUT_CONTIGUOUS, a.n_chunks, BLK);
+    };
+    auto chunk_of = [&](int desc) { return (desc >> kDescChunkShift) & 63; };
+    // the tile of `desc` has no live key for this wave's Q-block
+    auto dead_of = [&](int desc) { return !((desc >> (kDescCodeShift + half)) & 1); };
+    auto kpos_of = [&](int desc, int j) { return (desc & 0xFFFFF) * BLK + j * 32; };
+    // key block j of the tile of `desc` has a key after the wave's first query
+    auto diag_of = [&](int desc, int j) { return TCAUSAL && kpos_of(desc, j) + 31 > qb * BLK + rg * 32; };
+
+    f32x16 sc[2];        // scores of the next two blocks of the stream (by block parity)
+    PBlock pb[2];        // probabilities waiting for their P V product (by block parity)
+    uint64_t moved[2];   // rows whose reference moved with that block
+    float ref_cur = kNegInf;  // reference of the latest block exponentiated
+    float m_next = kNegInf;   // running max of a chunk that starts with the next tile (partial mode)
+    if (n_tiles > 0) {
+      const int d0 = __builtin_amdgcn_readfirstlane(sList[0]);
+      loader.template issue<false>(gK, src_of(d0), sK0, wave);
+      loader.template issue<false>(gV, src_of(d0), sV0, wave);
+      if (n_tiles > 1) loader.template issue<false>(gK, src_of(__builtin_amdgcn_readfirstlane(sList[1])), sK1, wave);
+      wait_vm();
+      __syncthreads();
+      tile_scores<D, BLK, false>(sK0, qf, ol, 0, sc);  // blocks 0 and 1 of tile 0
+      if (diag_of(d0, 0)) drop_future(sc[0], qrow, kpos_of(d0, 0), 1, lane >> 5);
+      moved[0] = block_softmax(sc[0], sl2, ref_cur, m_next, pb[0], dead_of(d0));
+    }
+
+    auto consume = [&](const PBlock& p, uint64_t mv) {
+      if (mv) {
+        const float alpha = (TCAUSAL && st.m_ref == p.ref) ? 1.f : __builtin_amdgcn_exp2f(st.m_ref - p.ref);
+        st.l *= alpha;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) st.acc[d] *= alpha;
+      }
+      st.m_ref = p.ref;
+      st.l += p.lsum;
+    };
+
+    // Half H of tile t (parity P = t % 2): sections j = 2H, 2H+1 of the tile.
+    auto halftile = [&](int t, auto parity, auto hc) {
+      constexpr int P = decltype(parity)::value;
+      constexpr int H = decltype(hc)::value;
+      const bf16* const Kt = P ? sK1 : sK0;  // K of tile t
+      const bf16* const Kn = P ? sK0 : sK1;  // K of tile t+1
+      const bf16* const Vt = P ? sV1 : sV0;  // V of tile t
+      bf16* const lfree = H == 0 ? (P ? sV0 : sV1) : (P ? sK1 : sK0);  // V of t+1, or K of t+2
+      const bf16* const Ks = H == 0 ? Kt : Kn;  // K of this half's S MFMAs
+      const int desc = __builtin_amdgcn_readfirstlane(sList[t]);
+      const bool has_next = t + 1 < n_tiles;
+      const int desc1 = has_next ? __builtin_amdgcn_readfirstlane(sList[t + 1]) : desc;
+      // the next tile starts a new accumulation (a chunk of its own in partial mode)
+      const bool next_new = !full && has_next && chunk_of(desc1) != chunk_of(desc);
+
+      wait_vm();
+      __syncthreads();
+      if constexpr (H == 0) {
+        bool fresh = t == 0;  // block 0 of this tile opens an accumulation
+        if (!full && cur_chunk < chunk_of(desc)) {
+          while (cur_chunk < chunk_of(desc)) flush_partial(cur_chunk++);
+          fresh = true;
+        }
+        if (fresh) st.m_true = m_next;
+      }
+      const TileSrc src = H == 0 ? src_of(desc1) : src_of(__builtin_amdgcn_readfirstlane(sList[min(t + 2, n_tiles - 1)]));
+      const bf16* const gsrc = H == 0 ? gV : gK;
+
+      bf16x8 fr[2 * NOPS];
+      auto rd = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int jj = i / NOPS, k = i % NOPS;
+        if constexpr (k < NKS)
+          fr[i] = ol.k_frag(Ks, H == 0 ? jj + 2 : jj, k);
+        else
+          fr[i] = ol.v_frag(Vt, 2 * H + jj, (k - NKS) / ND, (k - NKS) % ND);
+      };
+      auto mm = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int jj = i / NOPS, k = i % NOPS;
+        if constexpr (k < NKS) {
+          sc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], qf[k], k == 0 ? f32x16{} : sc[jj], 0, 0, 0);
+        } else {
+          constexpr int hf = (k - NKS) / ND, d = (k - NKS) % ND;
+          st.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pb[jj].p[hf], st.acc[d], 0, 0, 0);
+        }
+      };
+      static_for<AHEAD>([&](auto ic) { rd(ic); });
+
+      static_for<2>([&](auto jc) {
+        constexpr int jj = decltype(jc)::value;
+        constexpr int j = 2 * H + jj;          // section of the tile: P V of block j
+        constexpr bool NEXT = j == 3;          // its softmax is block 0 of the next tile
+        consume(pb[jj], moved[jj]);
+        constexpr int SRC = 1 - jj;            // parity of block j + 1
+        const f32x16& s = sc[SRC];
+        PBlock& out = pb[SRC];
+        const int sdesc = NEXT ? desc1 : desc;
+        constexpr int sblk = NEXT ? 0 : j + 1;
+        const bool dead = dead_of(sdesc);
+        float mx_a, mx_b, mx, run, ref_exp, l0, l1;
+        auto stage = [&](auto sc_) {
+          constexpr int g = decltype(sc_)::value;
+          if constexpr (g == 0) {
+            if constexpr (TCAUSAL)
+              if (diag_of(sdesc, sblk)) drop_future(sc[SRC], qrow, kpos_of(sdesc, sblk), 1, lane >> 5);
+            mx_a = fmaxf(fmaxf(s[0], s[1]), s[2]);
+            mx_a = fmaxf(fmaxf(mx_a, s[3]), s[4]);
+            mx_a = fmaxf(fmaxf(mx_a, s[5]), s[6]);
+          } else if constexpr (g == 1) {
+            mx_b = fmaxf(fmaxf(s[8], s[9]), s[10]);
+            mx_b = fmaxf(fmaxf(mx_b, s[11]), s[12]);
+            mx_b = fmaxf(fmaxf(mx_b, s[13]), s[14]);
+            mx = fmaxf(fmaxf(mx_a, s[7]), fmaxf(mx_b, s[15]));
+          } else if constexpr (g == 2) {
+            mx = fmaxf(mx, other_half(mx)) * sl2;
+            mx = dead ? kNegInf : mx;
+          } else if constexpr (g == 3) {
+            if constexpr (!NEXT) {
+              run = st.m_true;
+            } else {
+              ref_cur = next_new ? kNegInf : ref_cur;
+              run = next_new ? kNegInf : st.m_true;
+            }
+            run = fmaxf(run, mx);
+            const bool up = mx > ref_cur + kRescaleSlack;
+            ref_cur = up ? run : ref_cur;
+            out.ref = ref_cur;
+            // reference of the exponent: +inf makes a dead block's probabilities 0
+            ref_exp = dead ? __builtin_huge_valf() : (TCAUSAL && ref_cur == kNegInf) ? 0.f : ref_cur;
+            moved[SRC] = __builtin_amdgcn_ballot_w64(up);
+            if constexpr (!NEXT) {
+              st.m_true = run;
+            } else {
+              m_next = run;
+              st.m_true = (has_next && !next_new) ? run : st.m_true;
+            }
+            l0 = 0.f;
+            l1 = 0.f;
+          } else if constexpr (g < 12) {
+            constexpr int r = 2 * (g - 4);
+            out.p[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[r], sl2, -ref_exp));
+            out.p[r >> 3][(r & 7) + 1] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[r + 1], sl2, -ref_exp));
+          } else {
+            constexpr int hh = g - 12;
+            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+            float& acc_l = hh ? l1 : l0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc_l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{out.p[hh][2 * e], out.p[hh][2 * e + 1]}, ones, acc_l, false);
+            if constexpr (hh == 1) out.lsum = l0 + l1;
+          }
+        };
+        constexpr int NSTAGE = 14;
+        constexpr int SPS = (NSTAGE + NOPS - 1) / NOPS;  // stages per MFMA slot
+        static_for<NOPS>([&](auto kc) {
+          constexpr int k = decltype(kc)::value, i = jj * NOPS + k;
+          if constexpr (i + AHEAD < 2 * NOPS) rd(std::integral_constant<int, i + AHEAD>{});
+          mm(std::integral_constant<int, i>{});
+          static_for<SPS>([&](auto uc) {
+            constexpr int g = k * SPS + decltype(uc)::value;
+            if constexpr (g < NSTAGE) stage(std::integral_constant<int, g>{});
+          });
+          if constexpr (k < LPS / 2)
+            loader.template issue<false, jj * LPS / 2 + k, jj * LPS / 2 + k + 1>(gsrc, src, lfree, wave);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        // keep the section's vector results in this section (they are consumed one
+        // section later)
+        asm volatile("" : "+v"(out.p[0]), "+v"(out.p[1]), "+v"(out.lsum), "+v"(out.ref), "+v"(ref_cur));
+      });
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+      halftile(t, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+      halftile(t, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+      if (t + 1 < n_tiles) {
+        halftile(t + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+        halftile(t + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+      }
+    }
+
+    wait_vm();  // the last half's loads land before the next item loads into the same buffers
+    if (!full) {
+      while (cur_chunk < a.c1) flush_partial(cur_chunk++);
+    } else {
+      const int ln = opaque(lane), h2 = ln >> 5;
+      const float l_row = st.l + other_half(st.l);
+      const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+      if (!absent) {
+        bf16* op = (bf16*)a.o + bh_base + (int64_t)(qb * BLK + rg * 32 + (ln & 31)) * a.ss + 4 * h2;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const bf16x4 v4 = {(bf16)(st.acc[d][4 * g] * inv), (bf16)(st.acc[d][4 * g + 1] * inv),
+                               (bf16)(st.acc[d][4 * g + 2] * inv), (bf16)(st.acc[d][4 * g + 3] * inv)};
+            *(bf16x4*)(op + d * 32 + 8 * g) = v4;
+          }
+      }
+    }
+    if (a.trace && tid == 0) {
+      int64_t* tr = a.trace + (int64_t)pos * 4;
+      tr[0] = t_start;
+      tr[1] = realtime_now();
+      tr[2] = hw_location();
+      tr[3] = ((int64_t)bin << 32) | (int64_t)(uint32_t)item;
+    }
+  }
+}
+
 template <int D, int BLK>
 hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
   const bool general = a.layout == SA_LAYOUT_STRIPED || a.S % BLK != 0;
   const dim3 grid(a.num_bins), block(Shape<D, BLK>::NW * 64);
   if constexpr (BLK == 128) {
+    // Q-block pairs (contiguous layout, S a multiple of the block; checked by the plan)
+    if (a.q_pairs) {
+      if (a.token_causal)
+        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, false>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
     // striped chunks (S is then a multiple of block * n_chunks) without token-level causality
     if (a.layout == SA_LAYOUT_STRIPED) {
       if (a.token_causal)

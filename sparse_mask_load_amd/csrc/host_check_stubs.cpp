@@ -6,7 +6,8 @@
 
 namespace sa {
 
-hipError_t launch_popcount(const uint8_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*, hipStream_t) {
+hipError_t launch_popcount(const uint8_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*, hipStream_t, int32_t*,
+                           int32_t*) {
   return hipErrorNotSupported;
 }
 hipError_t launch_plan_rounds(const int32_t*, const int32_t*, int, int, int, int, int32_t*, int32_t*, int64_t*,

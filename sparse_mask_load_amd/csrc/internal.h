@@ -40,6 +40,8 @@ struct FwdArgs {
   int32_t B, H, S, nQ, nK, n_chunks, layout, c0, c1;
   int32_t num_bins;
   int32_t token_causal;  // also drop keys after the query inside live tiles
+  int32_t q_pairs;       // items are Q-block pairs (2p, 2p+1): item = (b*H + h)*nI + p
+  int32_t nI;            // items per (batch, head): nQ, or ceil(nQ / 2) with q_pairs
   int64_t sb, sh, ss;
   float scale;        // natural-log softmax scale
   float scale_log2;   // scale * log2(e)
@@ -85,8 +87,11 @@ struct MergeArgs {
 };
 
 // Kernel launchers (defined in the .hip files).  Return hipSuccess or the launch error.
+// Row, column and per-chunk row counts of the block mask; with prow/pcrow (contiguous layout)
+// also the union counts of Q-block pairs (2p, 2p+1): prow [BH*nP], pcrow [BH][C][nP], nP = ceil(nQ/2).
 hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_chunks, int layout,
-                           int32_t* row, int32_t* col, int32_t* crow, hipStream_t stream);
+                           int32_t* row, int32_t* col, int32_t* crow, hipStream_t stream,
+                           int32_t* prow = nullptr, int32_t* pcrow = nullptr);
 // Round-based LPT of the lists of a block plan on the device: list 0 from row, list 1 + c
 // from chunk c of crow.  Lists [list0, list0 + n_lists) are made (n_lists < 0: through list
 // C), list list0 + s written to slot s of items [.][BH*nQ], bin_ptr [.][m+1], bin_load [.][m]

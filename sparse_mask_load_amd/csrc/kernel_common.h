@@ -52,6 +52,31 @@ __device__ inline int build_tile_list(const uint8_t* __restrict__ mrow, int nK, 
   return count;
 }
 
+// Tile list of a Q-block pair (contiguous layout): the union of the live KV
+// tiles of mask rows qa (mrow_a) and qa + 1 (the next row, when has_b), for
+// chunks [c0, c1), in chunk then tile order.  A descriptor's group code holds
+// the tile's liveness for each half: bit 0 for row qa, bit 1 for row qa + 1.
+__device__ inline int build_pair_tile_list(const uint8_t* __restrict__ mrow_a, bool has_b, int nK, int n_chunks,
+                                           int c0, int c1, int* list, bool write = true) {
+  const int lane = threadIdx.x & 63;
+  const int per_chunk = nK / n_chunks;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint8_t* __restrict__ mrow_b = mrow_a + nK;
+  int count = 0;
+  for (int c = c0; c < c1; ++c) {
+    const int j0 = c * per_chunk, j1 = j0 + per_chunk;
+    for (int base = j0; base < j1; base += 64) {
+      const int j = base + lane;
+      const int code = j < j1 ? ((mrow_a[j] != 0 ? 1 : 0) | (has_b && mrow_b[j] != 0 ? 2 : 0)) : 0;
+      const uint64_t bits = __ballot(code != 0);
+      if (write && code != 0)
+        list[count + __popcll(bits & below)] = j | (code << kDescCodeShift) | (c << kDescChunkShift);
+      count += __popcll(bits);
+    }
+  }
+  return count;
+}
+
 // Workgroup index remapped so that each XCD works through one contiguous range
 // of [0, n) in order.  Workgroups b = 0, 1, ... of a launch are dealt to the
 // n_xcd XCDs round-robin (b mod n_xcd); XCD x then runs logical indices

@@ -49,16 +49,19 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Byte offsets of the arrays in the scratch array.
 struct Layout {
-  size_t row, col, crow, items, bin_ptr, bin_load, stats, end;
+  size_t row, col, crow, prow, pcrow, items, bin_ptr, bin_load, stats, end;
 };
 
-Layout layout_for(int64_t BH, int64_t nQ, int64_t nK, int64_t C, int64_t m) {
+// nI: items per (batch, head) (nQ, or the pair count with Q-block pairs; then nP = nI)
+Layout layout_for(int64_t BH, int64_t nQ, int64_t nK, int64_t C, int64_t m, int64_t nI, bool pairs) {
   Layout L;
   L.row = 0;
   L.col = align256(L.row + (size_t)(BH * nQ) * 4);
   L.crow = align256(L.col + (size_t)(BH * nK) * 4);
-  L.items = align256(L.crow + (size_t)(BH * C * nQ) * 4);
-  L.bin_ptr = align256(L.items + (size_t)(BH * nQ) * 4);
+  L.prow = align256(L.crow + (size_t)(BH * C * nQ) * 4);
+  L.pcrow = align256(L.prow + (pairs ? (size_t)(BH * nI) * 4 : 0));
+  L.items = align256(L.pcrow + (pairs ? (size_t)(BH * C * nI) * 4 : 0));
+  L.bin_ptr = align256(L.items + (size_t)(BH * nI) * 4);
   L.bin_load = align256(L.bin_ptr + (size_t)(m + 1) * 4);
   L.stats = align256(L.bin_load + (size_t)m * 8);
   L.end = L.stats + 4 * 8;
@@ -83,14 +86,16 @@ extern "C" sa_status sparse_attn_fwd_noalloc(const sa_problem* prob, const uint8
     return sa::set_error(SA_ERR_INVALID, "partial mode needs o_part, m_part and l_part");
   if (num_bins < 0) return sa::set_error(SA_ERR_INVALID, "num_bins %d < 0", num_bins);
   const int64_t nQ = (pr.S + pr.block - 1) / pr.block, nK = nQ, BH = (int64_t)pr.B * pr.H, C = pr.n_chunks;
+  const bool pairs = pr.q_pairs != 0;
+  const int64_t nI = pairs ? (nQ + 1) / 2 : nQ;  // items per (batch, head)
   // size limits first (before any HIP call), with the most bins the planner takes when the
   // default count is asked for
   auto limits = [&](int m) -> sa_status {
-    if (BH * nQ > sa::kDevicePlanMaxItems || m > sa::kDevicePlanMaxBins)
-      return sa::set_error(SA_ERR_UNSUPPORTED, "the allocation-free path plans at most %d (b, h, Q-block) items on "
+    if (BH * nI > sa::kDevicePlanMaxItems || m > sa::kDevicePlanMaxBins)
+      return sa::set_error(SA_ERR_UNSUPPORTED, "the allocation-free path plans at most %d work items on "
                                                "at most %d bins (got %lld, %d)",
-                           sa::kDevicePlanMaxItems, sa::kDevicePlanMaxBins, (long long)(BH * nQ), m);
-    const Layout L = layout_for(BH, nQ, nK, C, m);
+                           sa::kDevicePlanMaxItems, sa::kDevicePlanMaxBins, (long long)(BH * nI), m);
+    const Layout L = layout_for(BH, nQ, nK, C, m, nI, pairs);
     if (L.end > kScratchBytes)
       return sa::set_error(SA_ERR_UNSUPPORTED, "the allocation-free path's counts and list need %zu bytes, above its "
                                                "%zu-byte work array (B*H*n_chunks*nQ too large)",
@@ -103,21 +108,25 @@ extern "C" sa_status sparse_attn_fwd_noalloc(const sa_problem* prob, const uint8
   if (de != hipSuccess) return sa::set_error(SA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(de));
   const int m = num_bins ? num_bins : sa::default_num_bins(pr, device);
   if ((st = limits(m))) return st;
-  const Layout L = layout_for(BH, nQ, nK, C, m);
+  const Layout L = layout_for(BH, nQ, nK, C, m, nI, pairs);
   unsigned char* base = nullptr;
   if ((st = scratch_of(device, &base))) return st;
   int32_t* row = (int32_t*)(base + L.row);
   int32_t* col = (int32_t*)(base + L.col);
   int32_t* crow = (int32_t*)(base + L.crow);
+  int32_t* prow = pairs ? (int32_t*)(base + L.prow) : nullptr;
+  int32_t* pcrow = pairs ? (int32_t*)(base + L.pcrow) : nullptr;
   int32_t* items = (int32_t*)(base + L.items);
   int32_t* bin_ptr = (int32_t*)(base + L.bin_ptr);
   int64_t* bin_load = (int64_t*)(base + L.bin_load);
   int64_t* stats = (int64_t*)(base + L.stats);
-  hipError_t e = sa::launch_popcount(mask, (int)BH, (int)nQ, (int)nK, (int)C, pr.layout, row, col, crow, stream);
+  hipError_t e =
+      sa::launch_popcount(mask, (int)BH, (int)nQ, (int)nK, (int)C, pr.layout, row, col, crow, stream, prow, pcrow);
   if (e != hipSuccess) return sa::set_error(SA_ERR_HIP, "popcount launch: %s", hipGetErrorString(e));
   // the list the forward call of a plan would use: one chunk's own list, else the full-range one
   const int list = (chunk_end - chunk_begin == 1) ? 1 + chunk_begin : 0;
-  e = sa::launch_plan_rounds(row, crow, (int)BH, (int)nQ, (int)C, m, items, bin_ptr, bin_load, stats, stream, list, 1);
+  e = sa::launch_plan_rounds(pairs ? prow : row, pairs ? pcrow : crow, (int)BH, (int)nI, (int)C, m, items, bin_ptr,
+                             bin_load, stats, stream, list, 1);
   if (e != hipSuccess) return sa::set_error(SA_ERR_HIP, "planning launch: %s", hipGetErrorString(e));
   sa::FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o;
@@ -131,6 +140,8 @@ extern "C" sa_status sparse_attn_fwd_noalloc(const sa_problem* prob, const uint8
   a.B = pr.B; a.H = pr.H; a.S = pr.S; a.nQ = (int)nQ; a.nK = (int)nK; a.n_chunks = pr.n_chunks;
   a.layout = pr.layout; a.c0 = chunk_begin; a.c1 = chunk_end; a.num_bins = m;
   a.token_causal = pr.token_causal ? 1 : 0;
+  a.q_pairs = pairs ? 1 : 0;
+  a.nI = (int)nI;
   a.sb = pr.sb; a.sh = pr.sh; a.ss = pr.ss;
   a.scale = sa::softmax_scale(pr);
   a.scale_log2 = a.scale * 1.4426950408889634f;

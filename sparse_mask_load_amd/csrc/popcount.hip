@@ -8,7 +8,9 @@
 // 32-bit word; a byte is non-zero iff its low 7 bits are or its top bit is).
 // Column counts: a thread per column walks the rows with coalesced byte loads.
 // Counts are integers accumulated exactly.  The grand total is the sum of the
-// row counts, taken on the host.
+// row counts, taken on the host.  With Q-block pairs (prow non-null) a thread
+// per pair p also counts the union of rows 2p and 2p+1 (the OR of their bytes),
+// in total and per chunk: the tiles the pair's work item visits.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -23,7 +25,8 @@ __device__ __forceinline__ int nonzero_bytes(uint32_t v) {
 
 __global__ __launch_bounds__(256) void popcount_kernel(const uint8_t* __restrict__ mask, int nQ, int nK,
                                                        int n_chunks, int layout, int32_t* __restrict__ row,
-                                                       int32_t* __restrict__ col, int32_t* __restrict__ crow) {
+                                                       int32_t* __restrict__ col, int32_t* __restrict__ crow,
+                                                       int32_t* __restrict__ prow, int32_t* __restrict__ pcrow) {
   const int bh = blockIdx.x;
   const uint8_t* m = mask + (int64_t)bh * nQ * nK;
   const int per_chunk = nK / n_chunks;
@@ -49,6 +52,30 @@ __global__ __launch_bounds__(256) void popcount_kernel(const uint8_t* __restrict
     if (layout == SA_LAYOUT_STRIPED)
       for (int c = 0; c < n_chunks; ++c) crow[((int64_t)bh * n_chunks + c) * nQ + i] = tot;
   }
+  if (prow) {  // contiguous layout only
+    const int nP = (nQ + 1) / 2;
+    for (int p = threadIdx.x; p < nP; p += blockDim.x) {
+      const uint8_t* ma = m + (int64_t)(2 * p) * nK;
+      const bool has_b = 2 * p + 1 < nQ;
+      const uint8_t* mb = has_b ? ma + nK : ma;  // a lone last row is its own union
+      int tot = 0;
+      for (int c = 0; c < n_chunks; ++c) {
+        int cnt = 0;
+        if (vec) {
+          for (int j = c * per_chunk; j < (c + 1) * per_chunk; j += 16) {
+            const uint4 va = *(const uint4*)(ma + j), vb = *(const uint4*)(mb + j);
+            cnt += nonzero_bytes(va.x | vb.x) + nonzero_bytes(va.y | vb.y) + nonzero_bytes(va.z | vb.z) +
+                   nonzero_bytes(va.w | vb.w);
+          }
+        } else {
+          for (int j = c * per_chunk; j < (c + 1) * per_chunk; ++j) cnt += (ma[j] | mb[j]) != 0;
+        }
+        tot += cnt;
+        pcrow[((int64_t)bh * n_chunks + c) * nP + p] = cnt;
+      }
+      prow[(int64_t)bh * nP + p] = tot;
+    }
+  }
   for (int j = threadIdx.x; j < nK; j += blockDim.x) {
     int cnt = 0;
     int i = 0;
@@ -63,10 +90,10 @@ __global__ __launch_bounds__(256) void popcount_kernel(const uint8_t* __restrict
 }  // namespace
 
 hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_chunks, int layout, int32_t* row,
-                           int32_t* col, int32_t* crow, hipStream_t stream) {
+                           int32_t* col, int32_t* crow, hipStream_t stream, int32_t* prow, int32_t* pcrow) {
   if (BH == 0) return hipSuccess;
   hipLaunchKernelGGL(popcount_kernel, dim3(BH), dim3(256), 0, stream, mask, nQ, nK, n_chunks, layout, row, col,
-                     crow);
+                     crow, prow, pcrow);
   return hipGetLastError();
 }
 

@@ -47,8 +47,9 @@ def empty_like_qkv(q):
     return torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
 
 
-def plan_block(w, q, order="lpt", num_bins=0, layout=None, token_causal=False):
-    prob = bd.make_problem(q, w.block, w.n_chunks, layout or w.layout, token_causal=token_causal)
+def plan_block(w, q, order="lpt", num_bins=0, layout=None, token_causal=False, q_pairs=False, scale=0.0):
+    prob = bd.make_problem(q, w.block, w.n_chunks, layout or w.layout, scale=scale, token_causal=token_causal,
+                           q_pairs=q_pairs)
     mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
     plan = bd.sparse_attn_plan(prob, "block", mask=mask, num_bins=num_bins, order=order)
     del mask  # the plan keeps its own copy

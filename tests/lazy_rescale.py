@@ -46,10 +46,12 @@ def _tile_sequence(mask_row, S, block, C, layout, c0, c1):
     return out
 
 
-def count_rescales(w, scale=None, c0=0, c1=None, full=True, token_causal=False, heads=None):
+def count_rescales(w, scale=None, c0=0, c1=None, full=True, token_causal=False, heads=None, pairs=False):
     """Number of (row, tile) events where the kernel rescales a row that already holds a finite
     reference, over every item of heads ``heads`` (all by default), in full mode (one state over
-    the chunk range) or partial mode (the state restarts at every chunk)."""
+    the chunk range) or partial mode (the state restarts at every chunk).  ``pairs``: the
+    Q-block-pair mapping, where a wave holds all keys of every tile and checks its rows after
+    each 32-key block (a tile that is live only for the other Q-block of the pair adds nothing)."""
     c1 = w.n_chunks if c1 is None else c1
     blk, S = w.block, w.S
     nb = blk // 64  # 32-key blocks per wave
@@ -64,16 +66,17 @@ def count_rescales(w, scale=None, c0=0, c1=None, full=True, token_causal=False, 
                     rows = np.arange(qb * blk + rg * 32, min(S, qb * blk + rg * 32 + 32))
                     if rows.size == 0:
                         continue
-                    for kh in range(2):
+                    for kh in range(1 if pairs else 2):
                         m_ref = np.full(rows.size, -np.inf)
                         m_true = np.full(rows.size, -np.inf)
                         cur = c0
-                        for c, toks in tiles:
+                        steps = [(c, toks[i:i + 32]) for c, toks in tiles for i in range(0, blk, 32)] if pairs \
+                            else [(c, toks[kh * nb * 32:(kh + 1) * nb * 32]) for c, toks in tiles]
+                        for c, kt in steps:
                             if not full and c != cur:
                                 m_ref[:] = -np.inf
                                 m_true[:] = -np.inf
                                 cur = c
-                            kt = toks[kh * nb * 32:(kh + 1) * nb * 32]
                             sub = s[np.ix_(rows, np.maximum(kt, 0))]
                             dead = np.broadcast_to(kt < 0, sub.shape)
                             if token_causal:
@@ -104,6 +107,7 @@ RESCALE_CASES = [
     (1, 2, 2048, 128, 128, 4, "causal", 0.0, "striped", 1.0, 1, False),       # striped
     (1, 2, 1024, 128, 128, 2, "ones", 0.0, "contiguous", None, 8, True),      # token-causal, full tiles
     (1, 2, 1024, 64, 64, 2, "ones", 0.0, "striped", 1.0, 1, True),            # token-causal, striped
+    (1, 2, 1152, 128, 128, 3, "bernoulli", 0.6, "contiguous", 1.0, 1, False),  # odd nQ (a lone last pair row)
 ]
 
 

@@ -117,6 +117,12 @@ BAD_PROBLEMS = [
     (dict(layout=1, n_chunks=4), bd.SA_ERR_UNSUPPORTED),  # block/C = 16 keys < 32
     (dict(layout=7), bd.SA_ERR_INVALID),
     (dict(dtype=bd.SA_F32, block=128), bd.SA_ERR_UNSUPPORTED),
+    # Q-block pairs: bf16, block 128, contiguous layout, S a multiple of 128
+    (dict(q_pairs=1), bd.SA_ERR_UNSUPPORTED),  # block 64
+    (dict(q_pairs=1, block=128, S=320, n_chunks=1, sb=2 * 320 * 64, sh=320 * 64), bd.SA_ERR_UNSUPPORTED),
+    (dict(q_pairs=1, block=128, S=512, layout=1, n_chunks=2, sb=2 * 512 * 64, sh=512 * 64),
+     bd.SA_ERR_UNSUPPORTED),
+    (dict(q_pairs=1, block=64, dtype=bd.SA_F32), bd.SA_ERR_UNSUPPORTED),
 ]
 
 
@@ -144,12 +150,19 @@ def test_problem_fields_are_the_declared_ones():
     # a misspelt keyword would become a plain Python attribute and leave the field at 0
     names = [n for n, _ in bd.sa_problem._fields_]
     assert names == ["B", "H", "S", "D", "block", "n_chunks", "layout", "dtype", "scale", "token_causal",
-                     "sb", "sh", "ss"]
+                     "q_pairs", "sb", "sh", "ss"]
+    # q_pairs takes the padding after token_causal: the C struct keeps its size and offsets
+    assert ctypes.sizeof(bd.sa_problem) == 72 and bd.sa_problem.sb.offset == 48
 
 
 def test_token_causal_only_for_block_plans():
     assert _plan_status(_problem(token_causal=1), kind=bd.SA_KIND_TOPK) == bd.SA_ERR_INVALID
     assert "token_causal" in bd.sa_last_error()
+
+
+def test_q_pairs_only_for_block_plans():
+    assert _plan_status(_problem(q_pairs=1), kind=bd.SA_KIND_TOPK) == bd.SA_ERR_INVALID
+    assert "q_pairs" in bd.sa_last_error()
 
 
 def test_device_order_limits_checked_before_the_gpu():
@@ -158,6 +171,10 @@ def test_device_order_limits_checked_before_the_gpu():
     assert _plan_status(big, order=bd.SA_ORDER_LPT_DEVICE) == bd.SA_ERR_UNSUPPORTED
     assert "16384" in bd.sa_last_error()
     assert _plan_status(_problem(), order=bd.SA_ORDER_LPT_DEVICE, num_bins=1025) == bd.SA_ERR_UNSUPPORTED
+    # with Q-block pairs the limit counts pairs: 129 heads of 128 pairs = 16512 items
+    pairs = _problem(H=129, S=32768, block=128, q_pairs=1, sb=129 * 32768 * 64, sh=32768 * 64, n_chunks=1)
+    assert _plan_status(pairs, order=bd.SA_ORDER_LPT_DEVICE) == bd.SA_ERR_UNSUPPORTED
+    assert "16384" in bd.sa_last_error()
     assert _plan_status(_problem(), order=4) == bd.SA_ERR_INVALID
 
 

@@ -249,3 +249,52 @@ def test_rounds_lpt_plan_items_and_workload_makespans():
     r = P.plan_items(row, 256, "lpt_device")
     assert r["makespan"] == P.plan_items(row, 256, "lpt")["makespan"] == 516
     assert np.array_equal(np.sort(r["items"]), np.arange(row.size))
+
+
+def test_pair_counts_against_set_unions():
+    """Q-block pair loads: the size of the set of KV blocks live in row 2p or row 2p+1, counted
+    with Python sets, in total and per contiguous chunk; odd nQ leaves a pair of one row."""
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        nQ = int(rng.integers(1, 12))
+        C = int(rng.choice([1, 2, 3, 4]))
+        nK = C * int(rng.integers(1, 5))
+        mask = (rng.random((B, H, nQ, nK)) < rng.random()).astype(np.uint8)
+        got = P.pair_counts(mask, C)
+        nP = (nQ + 1) // 2
+        assert got["row"].shape == (B, H, nP) and got["crow"].shape == (B, H, C, nP)
+        for b in range(B):
+            for h in range(H):
+                for p in range(nP):
+                    rows = [2 * p] + ([2 * p + 1] if 2 * p + 1 < nQ else [])
+                    cols = {j for r in rows for j in range(nK) if mask[b, h, r, j]}
+                    assert got["row"][b, h, p] == len(cols)
+                    for c in range(C):
+                        per = nK // C
+                        assert got["crow"][b, h, c, p] == len({j for j in cols if j // per == c})
+
+
+def test_pair_counts_causal_closed_form_and_bounds():
+    """Block-causal mask: pair p covers KV blocks 0 .. 2p+1, so its load is 2p+2 and chunk c of
+    width w holds min(w, max(0, 2p+2 - c*w)) of them; in general a pair's load lies between
+    the larger and the sum of its two row counts."""
+    nQ, C = 64, 4
+    mask = np.tril(np.ones((nQ, nQ), np.uint8))[None, None]
+    got = P.pair_counts(mask, C)
+    p = np.arange(nQ // 2)
+    assert np.array_equal(got["row"][0, 0], 2 * p + 2)
+    wd = nQ // C
+    for c in range(C):
+        assert np.array_equal(got["crow"][0, 0, c], np.clip(2 * p + 2 - c * wd, 0, wd))
+    w = W.make(4, with_data=False)
+    row = P.popcount(w.mask, w.n_chunks)["row"]
+    pr = P.pair_counts(w.mask, w.n_chunks)["row"]
+    a, b = row[:, :, 0::2], row[:, :, 1::2]
+    assert (pr >= np.maximum(a, b)).all() and (pr <= a + b).all()
+    # causal workload: LPT over the 1024 pair loads reaches the lower bound of 66560 / 256
+    w3 = W.make(3, with_data=False)
+    pr3 = P.pair_counts(w3.mask, 4)["row"]
+    assert pr3.sum() == 66560
+    for order in ("lpt", "lpt_device"):
+        assert P.plan_items(pr3, 256, order)["makespan"] == 260

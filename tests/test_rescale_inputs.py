@@ -20,6 +20,18 @@ def test_case_crosses_the_rescale_threshold(n):
         assert events >= 100, f"case {n} full={full}: only {events} rescales of a non-empty row"
 
 
+# the cases that Q-block pairs also run (bf16, block 128, contiguous, S a multiple of 128)
+PAIR_CASES = [n for n, c in enumerate(LR.RESCALE_CASES) if c[4] == 128 and c[8] == "contiguous" and c[2] % 128 == 0]
+
+
+@pytest.mark.parametrize("n", PAIR_CASES)
+def test_case_crosses_the_rescale_threshold_with_q_block_pairs(n):
+    w, scale, tc = LR.make_rescale_case(n)
+    for full in (True, False):
+        events = LR.count_rescales(w, scale, full=full, token_causal=tc, pairs=True)
+        assert events >= 100, f"case {n} full={full}: only {events} rescales of a non-empty row"
+
+
 def test_default_scale_inputs_do_not_rescale():
     w = W.make_custom(1, 2, 2048, 128, block=128, n_chunks=4, pattern="causal", seed=105, layout="striped")
     assert LR.count_rescales(w, None, full=True) == 0

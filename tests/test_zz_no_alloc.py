@@ -22,11 +22,12 @@ def _need_gpu():
     bd.lib()  # fails loudly if the library is missing
 
 
-def _check(w, seed):
-    print(f"noalloc case: B{w.B} H{w.H} S{w.S} d{w.D} block {w.block} C{w.n_chunks} {w.layout}", flush=True)
+def _check(w, seed, q_pairs=False):
+    print(f"noalloc case: B{w.B} H{w.H} S{w.S} d{w.D} block {w.block} C{w.n_chunks} {w.layout} pairs {q_pairs}",
+          flush=True)
     q, k, v = G.upload(w)
     C = w.n_chunks
-    prob = bd.make_problem(q, w.block, C, w.layout)
+    prob = bd.make_problem(q, w.block, C, w.layout, q_pairs=q_pairs)
     mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
     plan = bd.sparse_attn_plan(prob, "block", mask=mask, order="lpt_device")
     # full mode over every chunk
@@ -59,6 +60,13 @@ def test_noalloc_matches_plan_and_forward_on_two_calls():
     _check(W.make(3), seed=1)
     _check(W.make_custom(1, 3, 1000, 64, block=128, n_chunks=2, dtype="bf16", pattern="bernoulli", density=0.5,
                          seed=41), seed=2)
+
+
+def test_noalloc_with_q_block_pairs_on_two_calls():
+    # pair items: the causal workload, then an odd number of Q-blocks (a lone last pair row)
+    _check(W.make(3), seed=3, q_pairs=True)
+    _check(W.make_custom(1, 3, 1152, 128, block=128, n_chunks=3, dtype="bf16", pattern="bernoulli", density=0.5,
+                         seed=42), seed=4, q_pairs=True)
 
 
 def test_noalloc_rejects_oversized_problems_on_the_gpu():
