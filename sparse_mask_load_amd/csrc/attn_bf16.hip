@@ -1199,32 +1199,59 @@ void attn_bf16_pair_kernel(FwdArgs a) {
     reset(st);
     int cur_chunk = a.c0;
 
-    // Writes chunk `chunk`'s partial of this wave's rows (O unnormalised, m, l in
-    // the true-max basis) straight from the registers and resets the state.
-    auto flush_partial = [&](int chunk) {
+    // Writes chunk `chunk`'s partial of this wave's rows (O unnormalised, m, l in the
+    // true-max basis) and resets the state.  D = 128: the O rows go through `stage`, a
+    // 4 KiB LDS region of this wave alone (its own slice of a tile buffer that no wave
+    // reads meanwhile), one head-dim block at a time, so that every store instruction
+    // writes eight whole 128-byte row segments; otherwise straight from the registers.
+    auto flush_partial = [&](int chunk, float* stage) {
       const int ln = opaque(lane), l32 = ln & 31, h2 = ln >> 5;
       const bool any = st.m_true != kNegInf;
       const float corr = any ? __builtin_amdgcn_exp2f(st.m_ref - st.m_true) : 0.f;
       const float l_row = (st.l + other_half(st.l)) * corr;
       if (!absent) {
-        const int64_t prow =
-            ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK + rg * 32 + l32;
-        float* const op = a.o_part + prow * D + 4 * h2;
+        const int64_t prow0 = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK + rg * 32;
+        if constexpr (D == 128) {
+          // stage layout: row r (32 floats) at 32 r, its 16-byte chunk c at physical chunk
+          // c ^ ((r >> 1) & 7), so that both the column-wise writes and the row-wise reads
+          // touch 16 different chunks of 16 bytes per 256 bytes
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
+          for (int d = 0; d < ND; ++d) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 v4 = {st.acc[d][4 * g] * corr, st.acc[d][4 * g + 1] * corr, st.acc[d][4 * g + 2] * corr,
-                              st.acc[d][4 * g + 3] * corr};
-            *(f32x4*)(op + d * 32 + 8 * g) = v4;
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 v4 = {st.acc[d][4 * g] * corr, st.acc[d][4 * g + 1] * corr,
+                                st.acc[d][4 * g + 2] * corr, st.acc[d][4 * g + 3] * corr};
+              *(f32x4*)(stage + l32 * 32 + 4 * ((2 * g + h2) ^ ((l32 >> 1) & 7))) = v4;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 8 * i + (ln >> 3), c = ln & 7;
+              const f32x4 v4 = *(const f32x4*)(stage + r * 32 + 4 * (c ^ ((r >> 1) & 7)));
+              *(f32x4*)(a.o_part + (prow0 + r) * D + d * 32 + 4 * c) = v4;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
           }
+        } else {
+          float* const op = a.o_part + (prow0 + l32) * D + 4 * h2;
+#pragma unroll
+          for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 v4 = {st.acc[d][4 * g] * corr, st.acc[d][4 * g + 1] * corr,
+                                st.acc[d][4 * g + 2] * corr, st.acc[d][4 * g + 3] * corr};
+              *(f32x4*)(op + d * 32 + 8 * g) = v4;
+            }
+        }
         if (h2 == 0) {
-          a.m_part[prow] = any ? st.m_true * kLn2 : kNegInf;
-          a.l_part[prow] = l_row;
+          a.m_part[prow0 + l32] = any ? st.m_true * kLn2 : kNegInf;
+          a.l_part[prow0 + l32] = l_row;
         }
       }
       reset(st);
     };
+    // this wave's slice of a tile buffer (the slots its own tile loads write), as staging
+    auto stage_of = [&](bf16* buf) { return (float*)(buf + wave * SH::IPW * 64 * 8); };
     auto src_of = [&](int desc) {
       return tile_source(desc, bh_base, a.ss, a.S, SA_LAYOUT_CONTIGUOUS, a.n_chunks, BLK);
     };
@@ -1278,12 +1305,18 @@ void attn_bf16_pair_kernel(FwdArgs a) {
       // the next tile starts a new accumulation (a chunk of its own in partial mode)
       const bool next_new = !full && has_next && chunk_of(desc1) != chunk_of(desc);
 
-      wait_vm();
+      // The first half reads V of this tile, loaded during the previous tile's first half:
+      // wait for this wave's loads, then the barrier makes every wave's visible (and frees the
+      // V buffer of the previous tile).  The second half reads only data that the first
+      // half's wait covered (K of the next tile, V of this one); its barrier just frees this
+      // tile's K buffer, so the loads and stores issued meanwhile keep draining.
+      if constexpr (H == 0) wait_vm();
       __syncthreads();
       if constexpr (H == 0) {
         bool fresh = t == 0;  // block 0 of this tile opens an accumulation
         if (!full && cur_chunk < chunk_of(desc)) {
-          while (cur_chunk < chunk_of(desc)) flush_partial(cur_chunk++);
+          // the V buffer of the previous tile is free until this half's loads go out
+          while (cur_chunk < chunk_of(desc)) flush_partial(cur_chunk++, stage_of(lfree));
           fresh = true;
         }
         if (fresh) st.m_true = m_next;
@@ -1323,7 +1356,8 @@ void attn_bf16_pair_kernel(FwdArgs a) {
         const int sdesc = NEXT ? desc1 : desc;
         constexpr int sblk = NEXT ? 0 : j + 1;
         const bool dead = dead_of(sdesc);
-        float mx_a, mx_b, mx, run, ref_exp, l0, l1;
+        const float dead_add = dead ? kNegInf : 0.f;  // uniform: a dead block's max is -inf
+        float mx_a, mx_b, mx, run, ref_exp, lsum;
         auto stage = [&](auto sc_) {
           constexpr int g = decltype(sc_)::value;
           if constexpr (g == 0) {
@@ -1338,8 +1372,7 @@ void attn_bf16_pair_kernel(FwdArgs a) {
             mx_b = fmaxf(fmaxf(mx_b, s[13]), s[14]);
             mx = fmaxf(fmaxf(mx_a, s[7]), fmaxf(mx_b, s[15]));
           } else if constexpr (g == 2) {
-            mx = fmaxf(mx, other_half(mx)) * sl2;
-            mx = dead ? kNegInf : mx;
+            mx = fmaf(fmaxf(mx, other_half(mx)), sl2, dead_add);
           } else if constexpr (g == 3) {
             if constexpr (!NEXT) {
               run = st.m_true;
@@ -1360,8 +1393,7 @@ void attn_bf16_pair_kernel(FwdArgs a) {
               m_next = run;
               st.m_true = (has_next && !next_new) ? run : st.m_true;
             }
-            l0 = 0.f;
-            l1 = 0.f;
+            lsum = 0.f;
           } else if constexpr (g < 12) {
             constexpr int r = 2 * (g - 4);
             out.p[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[r], sl2, -ref_exp));
@@ -1369,11 +1401,10 @@ void attn_bf16_pair_kernel(FwdArgs a) {
           } else {
             constexpr int hh = g - 12;
             const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-            float& acc_l = hh ? l1 : l0;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              acc_l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{out.p[hh][2 * e], out.p[hh][2 * e + 1]}, ones, acc_l, false);
-            if constexpr (hh == 1) out.lsum = l0 + l1;
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{out.p[hh][2 * e], out.p[hh][2 * e + 1]}, ones, lsum, false);
+            if constexpr (hh == 1) out.lsum = lsum;
           }
         };
         constexpr int NSTAGE = 14;
@@ -1406,7 +1437,10 @@ void attn_bf16_pair_kernel(FwdArgs a) {
 
     wait_vm();  // the last half's loads land before the next item loads into the same buffers
     if (!full) {
-      while (cur_chunk < a.c1) flush_partial(cur_chunk++);
+      // the buffer the last tile's first half loaded into (the next tile's V, of which there
+      // is none) is read by no wave; with no tile, no wave reads any buffer in this item
+      bf16* const spare = n_tiles > 0 ? (((n_tiles - 1) & 1) ? sV0 : sV1) : sV0;
+      while (cur_chunk < a.c1) flush_partial(cur_chunk++, stage_of(spare));
     } else {
       const int ln = opaque(lane), h2 = ln >> 5;
       const float l_row = st.l + other_half(st.l);
