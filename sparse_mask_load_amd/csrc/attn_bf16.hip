@@ -804,7 +804,8 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
   static_assert(SH::NW * 64 == 512, "launch bounds");
   static_assert(SH::TILE * 2 >= NRG * SH::RB * 4096, "merge round must fit in a K buffer");
   static_assert(SH::TILE * 2 >= NRG * 96 * 4, "merge statistics must fit in a V buffer");
-  constexpr int NOPS = NKS + 2 * ND;  // MFMAs of one section: S of one block, then P V of one block
+  constexpr int NOPS = NKS + 2 * ND;  // MFMAs of one section: S of one block and P V of one block
+  static_assert(NKS == 2 * ND, "a section alternates S and P V MFMAs one for one");
   constexpr int AHEAD = 4;            // operands read this many MFMAs ahead
   constexpr int LPS = SH::IPW;        // tile-load instructions per section (K and V slices)
   __shared__ __attribute__((aligned(1024))) bf16 sK0[SH::TILE];
@@ -999,7 +1000,10 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
           st.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pb[j].p[half], st.acc[d], 0, 0, 0);
         }
       };
-      static_for<AHEAD>([&](auto ic) { rd(ic); });
+      // slot q of a section runs op ord(q): all S MFMAs, then all P V MFMAs (alternating
+      // them, as the pair kernel does, measured 1% slower here)
+      auto ord = [](int q) constexpr { return q; };
+      static_for<AHEAD>([&](auto ic) { rd(std::integral_constant<int, ord(decltype(ic)::value)>{}); });
 
       static_for<NB>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
@@ -1066,9 +1070,9 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
         constexpr int NSTAGE = 14;
         constexpr int SPS = (NSTAGE + NOPS - 1) / NOPS;  // stages per MFMA slot
         static_for<NOPS>([&](auto kc) {
-          constexpr int k = decltype(kc)::value, i = j * NOPS + k;
-          if constexpr (i + AHEAD < 2 * NOPS) rd(std::integral_constant<int, i + AHEAD>{});
-          mm(std::integral_constant<int, i>{});
+          constexpr int k = decltype(kc)::value, q = j * NOPS + k;
+          if constexpr (q + AHEAD < 2 * NOPS) rd(std::integral_constant<int, ord(q + AHEAD)>{});
+          mm(std::integral_constant<int, ord(q)>{});
           static_for<SPS>([&](auto uc) {
             constexpr int g = k * SPS + decltype(uc)::value;
             if constexpr (g < NSTAGE) stage(std::integral_constant<int, g>{});
@@ -1145,7 +1149,8 @@ void attn_bf16_pair_kernel(FwdArgs a) {
   using SH = Shape<D, BLK>;
   constexpr int ND = SH::ND, NKS = SH::NKS;
   static_assert(SH::NW * 64 == 512, "launch bounds");
-  constexpr int NOPS = NKS + 2 * ND;  // MFMAs of one section: S of one block, then P V of one block
+  constexpr int NOPS = NKS + 2 * ND;  // MFMAs of one section: S of one block and P V of one block
+  static_assert(NKS == 2 * ND, "a section alternates S and P V MFMAs one for one");
   constexpr int AHEAD = 6;            // operands read this many MFMAs ahead (4 measured 1% slower)
   constexpr int LPS = SH::IPW;        // load instructions of one K or V tile per wave
   static_assert(LPS % 2 == 0 && LPS / 2 <= NOPS, "a half-tile's loads spread over its two sections");
@@ -1211,7 +1216,15 @@ void attn_bf16_pair_kernel(FwdArgs a) {
       const float l_row = (st.l + other_half(st.l)) * corr;
       if (!absent) {
         const int64_t prow0 = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK + rg * 32;
-        if constexpr (D == 128) {
+        if (D == 128 && !__builtin_amdgcn_ballot_w64(any)) {
+          // no row of the wave has a key in this chunk: zeros, row segments written whole
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              *(f32x4*)(a.o_part + (prow0 + 8 * i + (ln >> 3)) * D + d * 32 + 4 * (ln & 7)) = z;
+        } else if constexpr (D == 128) {
           // stage layout: row r (32 floats) at 32 r, its 16-byte chunk c at physical chunk
           // c ^ ((r >> 1) & 7), so that both the column-wise writes and the row-wise reads
           // touch 16 different chunks of 16 bytes per 256 bytes
@@ -1343,7 +1356,12 @@ void attn_bf16_pair_kernel(FwdArgs a) {
           st.acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pb[jj].p[hf], st.acc[d], 0, 0, 0);
         }
       };
-      static_for<AHEAD>([&](auto ic) { rd(ic); });
+      // slot q of a section runs op ord(q): its S and P V MFMAs alternate, so that the
+      // S chain (eight MFMAs into one accumulator) never has two links back to back
+      auto ord = [](int q) constexpr {
+        return (q / NOPS) * NOPS + ((q % NOPS) % 2 == 0 ? (q % NOPS) / 2 : NKS + (q % NOPS) / 2);
+      };
+      static_for<AHEAD>([&](auto ic) { rd(std::integral_constant<int, ord(decltype(ic)::value)>{}); });
 
       static_for<2>([&](auto jc) {
         constexpr int jj = decltype(jc)::value;
@@ -1410,9 +1428,9 @@ void attn_bf16_pair_kernel(FwdArgs a) {
         constexpr int NSTAGE = 14;
         constexpr int SPS = (NSTAGE + NOPS - 1) / NOPS;  // stages per MFMA slot
         static_for<NOPS>([&](auto kc) {
-          constexpr int k = decltype(kc)::value, i = jj * NOPS + k;
-          if constexpr (i + AHEAD < 2 * NOPS) rd(std::integral_constant<int, i + AHEAD>{});
-          mm(std::integral_constant<int, i>{});
+          constexpr int k = decltype(kc)::value, q = jj * NOPS + k;
+          if constexpr (q + AHEAD < 2 * NOPS) rd(std::integral_constant<int, ord(q + AHEAD)>{});
+          mm(std::integral_constant<int, ord(q)>{});
           static_for<SPS>([&](auto uc) {
             constexpr int g = k * SPS + decltype(uc)::value;
             if constexpr (g < NSTAGE) stage(std::integral_constant<int, g>{});
