@@ -36,6 +36,8 @@ for kw, status in T.BAD_PROBLEMS:
     T.test_plan_rejects_bad_problems_before_touching_the_gpu(kw, status)
 T.test_problem_fields_are_the_declared_ones()
 T.test_token_causal_only_for_block_plans()
+T.test_q_pairs_only_for_block_plans()
+T.test_hip_errors_surface_as_sa_err_hip()
 T.test_device_order_limits_checked_before_the_gpu()
 T.test_fwd_and_merge_argument_errors()
 print("SANITIZED HOST CHECKS OK", flush=True)

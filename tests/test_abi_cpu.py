@@ -160,6 +160,24 @@ def test_token_causal_only_for_block_plans():
     assert "token_causal" in bd.sa_last_error()
 
 
+def test_hip_errors_surface_as_sa_err_hip():
+    """A HIP runtime failure comes back as SA_ERR_HIP with the runtime's text (here: no device
+    on this machine), from the plan call and from a launch."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a device is visible; this failure path needs a machine without one")
+    mask = np.ones((1, 2, 4, 4), np.uint8)
+    sp = bd.sa_sparsity(bd.SA_KIND_BLOCK, 0, 0, 0, mask.ctypes.data, None, None, None, None, None, None)
+    out = ctypes.c_void_p()
+    st = bd.lib().sparse_attn_plan(ctypes.byref(_problem()), ctypes.byref(sp), 0, 0, ctypes.byref(out), None)
+    assert st == bd.SA_ERR_HIP and out.value is None
+    assert "hip" in bd.sa_last_error().lower()
+    arr = (bd._P * 1)(1)
+    assert bd.lib().chunk_merge(1, arr, arr, arr, 10, 64, None, 1, None, None) == bd.SA_ERR_INVALID  # NULL output
+    assert bd.lib().chunk_merge(1, arr, arr, arr, 10, 64, 1, 1, None, None) == bd.SA_ERR_HIP
+    assert "launch_merge" in bd.sa_last_error()  # the failing call, then the runtime's text
+
+
 def test_q_pairs_only_for_block_plans():
     assert _plan_status(_problem(q_pairs=1), kind=bd.SA_KIND_TOPK) == bd.SA_ERR_INVALID
     assert "q_pairs" in bd.sa_last_error()
