@@ -1304,6 +1304,9 @@ void attn_bf16_pair_kernel(FwdArgs a) {
     };
 
     // Half H of tile t (parity P = t % 2): sections j = 2H, 2H+1 of the tile.
+    // MFMA operands in flight; the first half of a tile also reads the second half's first
+    // operands (K of the next tile and V of this one, both complete since the first half's wait)
+    bf16x8 fr[2 * NOPS];
     auto halftile = [&](int t, auto parity, auto hc) {
       constexpr int P = decltype(parity)::value;
       constexpr int H = decltype(hc)::value;
@@ -1311,7 +1314,6 @@ void attn_bf16_pair_kernel(FwdArgs a) {
       const bf16* const Kn = P ? sK0 : sK1;  // K of tile t+1
       const bf16* const Vt = P ? sV1 : sV0;  // V of tile t
       bf16* const lfree = H == 0 ? (P ? sV0 : sV1) : (P ? sK1 : sK0);  // V of t+1, or K of t+2
-      const bf16* const Ks = H == 0 ? Kt : Kn;  // K of this half's S MFMAs
       const int desc = __builtin_amdgcn_readfirstlane(sList[t]);
       const bool has_next = t + 1 < n_tiles;
       const int desc1 = has_next ? __builtin_amdgcn_readfirstlane(sList[t + 1]) : desc;
@@ -1337,14 +1339,15 @@ void attn_bf16_pair_kernel(FwdArgs a) {
       const TileSrc src = H == 0 ? src_of(desc1) : src_of(__builtin_amdgcn_readfirstlane(sList[min(t + 2, n_tiles - 1)]));
       const bf16* const gsrc = H == 0 ? gV : gK;
 
-      bf16x8 fr[2 * NOPS];
-      auto rd = [&](auto ic) {
+      // operand of op i of half HH of this tile
+      auto rd = [&](auto hh, auto ic) {
+        constexpr int HH = decltype(hh)::value;
         constexpr int i = decltype(ic)::value;
         constexpr int jj = i / NOPS, k = i % NOPS;
         if constexpr (k < NKS)
-          fr[i] = ol.k_frag(Ks, H == 0 ? jj + 2 : jj, k);
+          fr[i] = ol.k_frag(HH == 0 ? Kt : Kn, HH == 0 ? jj + 2 : jj, k);
         else
-          fr[i] = ol.v_frag(Vt, 2 * H + jj, (k - NKS) / ND, (k - NKS) % ND);
+          fr[i] = ol.v_frag(Vt, 2 * HH + jj, (k - NKS) / ND, (k - NKS) % ND);
       };
       auto mm = [&](auto ic) {
         constexpr int i = decltype(ic)::value;
@@ -1361,7 +1364,10 @@ void attn_bf16_pair_kernel(FwdArgs a) {
       auto ord = [](int q) constexpr {
         return (q / NOPS) * NOPS + ((q % NOPS) % 2 == 0 ? (q % NOPS) / 2 : NKS + (q % NOPS) / 2);
       };
-      static_for<AHEAD>([&](auto ic) { rd(std::integral_constant<int, ord(decltype(ic)::value)>{}); });
+      if constexpr (H == 0)
+        static_for<AHEAD>([&](auto ic) {
+          rd(std::integral_constant<int, 0>{}, std::integral_constant<int, ord(decltype(ic)::value)>{});
+        });
 
       static_for<2>([&](auto jc) {
         constexpr int jj = decltype(jc)::value;
@@ -1429,7 +1435,10 @@ void attn_bf16_pair_kernel(FwdArgs a) {
         constexpr int SPS = (NSTAGE + NOPS - 1) / NOPS;  // stages per MFMA slot
         static_for<NOPS>([&](auto kc) {
           constexpr int k = decltype(kc)::value, q = jj * NOPS + k;
-          if constexpr (q + AHEAD < 2 * NOPS) rd(std::integral_constant<int, ord(q + AHEAD)>{});
+          if constexpr (q + AHEAD < 2 * NOPS)
+            rd(std::integral_constant<int, H>{}, std::integral_constant<int, ord(q + AHEAD)>{});
+          else if constexpr (H == 0)
+            rd(std::integral_constant<int, 1>{}, std::integral_constant<int, ord(q + AHEAD - 2 * NOPS)>{});
           mm(std::integral_constant<int, ord(q)>{});
           static_for<SPS>([&](auto uc) {
             constexpr int g = k * SPS + decltype(uc)::value;
