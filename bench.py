@@ -196,7 +196,7 @@ class WorkloadRun:
         # Q-block pair items where the kernel has them and adjacent mask rows share their tiles:
         # the pairs' union tiles (what the pair kernel computes) against the live tiles
         self.q_pairs, self.pair_overhead = False, None
-        if q_pairs != "off" and w.dtype == "bf16" and w.block == 128 and self.layout == "contiguous" and S % 128 == 0:
+        if q_pairs != "off" and w.dtype == "bf16" and w.block == 128 and S % 128 == 0:
             prob_p = bd.make_problem(self.q, w.block, C, self.layout, q_pairs=True)
             p = bd.sparse_attn_plan(prob_p, "block", mask=self.mask, order="lpt")
             info = bd.sparse_attn_plan_info(p)
@@ -204,7 +204,7 @@ class WorkloadRun:
             self.pair_overhead = 2.0 * info["load_sum"] / max(1, info["total_live"])
             self.q_pairs = q_pairs == "on" or self.pair_overhead <= PAIR_OVERHEAD_MAX
         elif q_pairs == "on":
-            raise SystemExit("--q-pairs on needs a bf16 workload with block 128, contiguous chunks, S % 128 == 0")
+            raise SystemExit("--q-pairs on needs a bf16 workload with block 128 and S % 128 == 0")
         self.prob = bd.make_problem(self.q, w.block, C, self.layout, q_pairs=self.q_pairs)
         self.o_part = torch.empty((C, B, H, S, D), dtype=torch.float32, device=dev)
         self.m_part = torch.empty((C, B, H, S), dtype=torch.float32, device=dev)

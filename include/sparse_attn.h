@@ -89,9 +89,9 @@ typedef enum { SA_KIND_BLOCK = 0, SA_KIND_TOPK = 1, SA_KIND_INDEX = 2 } sa_kind;
  *            stages feeds 256 query rows; the pair visits the union of its two
  *            mask rows' live tiles (a tile live for one row only is computed
  *            with zero probabilities for the other), and the LPT loads are
- *            those union counts.  Block plans, bf16, block 128, contiguous
- *            layout, S % 128 == 0 (else SA_ERR_UNSUPPORTED).  Worth it where
- *            adjacent mask rows share most tiles (causal, banded masks).
+ *            those union counts.  Block plans, bf16, block 128, S % 128 == 0
+ *            (else SA_ERR_UNSUPPORTED); both layouts.  Worth it where adjacent
+ *            mask rows share most tiles (causal, banded masks).
  *  sb,sh,ss  element strides of the b, h and s axes of Q, K, V and O. */
 typedef struct {
   int32_t B, H, S, D;
@@ -161,7 +161,7 @@ typedef enum {
   SA_PLAN_TOPK_IDX = 6, /* int32 [B][H][S][top_k] selected keys (TOPK/INDEX)              */
   SA_PLAN_TOPK_COUNT = 7, /* int32 [B][H][S]  number of selected keys                     */
   SA_PLAN_PAIR_ROW = 8,   /* int32 [B][H][nP]  q_pairs: live tiles of the union of rows 2p, 2p+1 */
-  SA_PLAN_PAIR_CROW = 9   /* int32 [B][H][C][nP] q_pairs: the same per chunk                  */
+  SA_PLAN_PAIR_CROW = 9   /* int32 [B][H][C][nP] q_pairs: the same per chunk (striped: = PAIR_ROW) */
 } sa_plan_array;
 
 /* Build a plan.

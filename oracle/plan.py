@@ -53,14 +53,16 @@ def popcount(mask: np.ndarray, n_chunks: int, layout: str = "contiguous") -> Dic
     return {"row": row, "col": col, "crow": crow, "total": int(live.sum())}
 
 
-def pair_counts(mask: np.ndarray, n_chunks: int) -> Dict[str, np.ndarray]:
-    """Loads of Q-block pair items on a contiguous-layout [B, H, nQ, nK] block mask.
+def pair_counts(mask: np.ndarray, n_chunks: int, layout: str = "contiguous") -> Dict[str, np.ndarray]:
+    """Loads of Q-block pair items on a [B, H, nQ, nK] block mask.
 
     A pair item p covers Q-blocks 2p and 2p+1 and visits every KV block that is
     live for either of them, so its work is the size of the union of the two
     mask rows (the single-row work of scenario 2 taken over both rows); a lone
     last row of an odd nQ is a pair of one.  Returns the union sizes "row"
-    [B, H, nP] and their split over the contiguous chunks "crow" [B, H, C, nP].
+    [B, H, nP] and their split over the chunks "crow" [B, H, C, nP]: contiguous
+    chunks take their KV-block ranges; every striped chunk holds a slice of each
+    live block, so its load is the whole union (as for single rows).
     """
     live = np.asarray(mask) != 0
     B, H, nQ, nK = live.shape
@@ -70,11 +72,18 @@ def pair_counts(mask: np.ndarray, n_chunks: int) -> Dict[str, np.ndarray]:
         union[:, :, p, :] = live[:, :, 2 * p, :]
         if 2 * p + 1 < nQ:
             union[:, :, p, :] |= live[:, :, 2 * p + 1, :]
-    per = nK // n_chunks
+    row = union.sum(axis=3).astype(np.int64)
     crow = np.zeros((B, H, n_chunks, nP), dtype=np.int64)
-    for c in range(n_chunks):
-        crow[:, :, c, :] = union[:, :, :, c * per:(c + 1) * per].sum(axis=3)
-    return {"row": union.sum(axis=3).astype(np.int64), "crow": crow}
+    if layout == "contiguous":
+        per = nK // n_chunks
+        for c in range(n_chunks):
+            crow[:, :, c, :] = union[:, :, :, c * per:(c + 1) * per].sum(axis=3)
+    elif layout == "striped":
+        for c in range(n_chunks):
+            crow[:, :, c, :] = row
+    else:
+        raise ValueError(layout)
+    return {"row": row, "crow": crow}
 
 
 def lpt(loads: Sequence[int], m: int) -> Tuple[List[List[int]], List[int]]:

@@ -126,8 +126,8 @@ sa_status validate_problem(const sa_problem* p, bool block_kind) {
   } else if (p->layout != SA_LAYOUT_CONTIGUOUS) {
     return fail(SA_ERR_INVALID, "unknown layout %d", p->layout);
   }
-  if (p->q_pairs && (p->dtype != SA_BF16 || p->block != 128 || p->layout != SA_LAYOUT_CONTIGUOUS || p->S % 128))
-    return fail(SA_ERR_UNSUPPORTED, "q_pairs needs bf16, block 128, the contiguous layout and S %% 128 == 0");
+  if (p->q_pairs && (p->dtype != SA_BF16 || p->block != 128 || p->S % 128))
+    return fail(SA_ERR_UNSUPPORTED, "q_pairs needs bf16, block 128 and S %% 128 == 0");
   return SA_OK;
 }
 

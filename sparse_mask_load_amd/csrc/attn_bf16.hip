@@ -1124,13 +1124,14 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
   }
 }
 
-// Q-block pairs (contiguous layout, S a multiple of 128): an item is the two
-// Q-blocks 2p and 2p+1 of one (batch, head), 256 query rows, so each K/V tile
-// staged in LDS feeds twice the queries of a single-block item.  Wave w owns
-// the 32 rows 32*(w%4) of Q-block 2p + w/4 and all four 32-key blocks of every
-// tile, so no key halves are merged.  The tile list is the union of both mask
-// rows; a tile that is live for one Q-block only is dead for the other's waves
-// (a dead block's probabilities are 0; its MFMAs still run).
+// Q-block pairs (S a multiple of 128): an item is the two Q-blocks 2p and 2p+1
+// of one (batch, head), 256 query rows, so each K/V tile staged in LDS feeds
+// twice the queries of a single-block item.  Wave w owns the 32 rows 32*(w%4)
+// of Q-block 2p + w/4 and all four 32-key blocks of every tile, so no key
+// halves are merged.  The tile list is the union of both mask rows; a 32-key
+// block that has no live key for a Q-block (a tile live for the other row only,
+// or, STRIPED, a dead group of a striped chunk's tile) is a dead block for that
+// Q-block's waves (its probabilities are 0; its MFMAs still run).
 //
 // Each wave's block stream has four blocks per tile, pipelined as in the
 // single-block kernel: the S MFMAs of block b+2 and the P V MFMAs of block b
@@ -1142,7 +1143,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
 // loads K of the tile after next into this tile's K buffer, which the first
 // half was the last to read.  TCAUSAL: token-level causality as in the
 // single-block kernel.
-template <int D, bool TCAUSAL>
+template <int D, bool STRIPED, bool TCAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_pair_kernel(FwdArgs a) {
   constexpr int BLK = 128;
@@ -1164,9 +1165,14 @@ void attn_bf16_pair_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = wave >> 2, rg = wave & 3;  // Q-block of the pair, row group within it
   const bool full = a.o != nullptr;
+  constexpr int LAYOUT = STRIPED ? SA_LAYOUT_STRIPED : SA_LAYOUT_CONTIGUOUS;
+  // 32-key blocks per liveness group: one group per striped chunk's slice of a KV block, one
+  // per tile for contiguous chunks (whose code bits are all set together)
+  const int kb_div = STRIPED ? SH::NKB / a.n_chunks : SH::NKB;
+  const int kstep = STRIPED ? a.n_chunks : 1;  // token distance of consecutive keys of a tile
   TileLoader<D, BLK> loader;
   loader.init(wave, lane);
-  loader.set_stride((int)a.ss);
+  loader.set_stride(STRIPED ? (int)(a.ss * a.n_chunks) : (int)a.ss);
   OperandLanes<D, true> ol;
   ol.init(lane, 0);
   const bf16* __restrict__ gQ = (const bf16*)a.q;
@@ -1197,7 +1203,7 @@ void attn_bf16_pair_kernel(FwdArgs a) {
 
     __syncthreads();  // every wave is done with the previous item's list and tiles
     const int n_tiles = build_pair_tile_list(a.mask + ((int64_t)bh * a.nQ + qa) * a.nK, qa + 1 < a.nQ, a.nK,
-                                             a.n_chunks, a.c0, a.c1, sList, wave == 0);
+                                             a.n_chunks, LAYOUT, a.c0, a.c1, sList, wave == 0);
     __syncthreads();
 
     RowState<ND> st;  // acc and l relative to st.m_ref (the reference of the last consumed block)
@@ -1265,15 +1271,22 @@ void attn_bf16_pair_kernel(FwdArgs a) {
     };
     // this wave's slice of a tile buffer (the slots its own tile loads write), as staging
     auto stage_of = [&](bf16* buf) { return (float*)(buf + wave * SH::IPW * 64 * 8); };
-    auto src_of = [&](int desc) {
-      return tile_source(desc, bh_base, a.ss, a.S, SA_LAYOUT_CONTIGUOUS, a.n_chunks, BLK);
+    auto src_of = [&](int desc) {  // (the group codes cleared, the tile index and chunk kept)
+      return tile_source(desc & ~(0xFF << kPairCodeShift), bh_base, a.ss, a.S, LAYOUT, a.n_chunks, BLK);
     };
     auto chunk_of = [&](int desc) { return (desc >> kDescChunkShift) & 63; };
-    // the tile of `desc` has no live key for this wave's Q-block
-    auto dead_of = [&](int desc) { return !((desc >> (kDescCodeShift + half)) & 1); };
-    auto kpos_of = [&](int desc, int j) { return (desc & 0xFFFFF) * BLK + j * 32; };
+    // 32-key block j of the tile of `desc` has no live key for this wave's Q-block
+    auto dead_of = [&](int desc, int j) { return !((desc >> (kPairCodeShift + 4 * half + j / kb_div)) & 1); };
+    // token position of the first key of block j of the tile of `desc` (striped chunk c's
+    // compacted position p is token c + C p)
+    auto kpos_of = [&](int desc, int j) {
+      const int key = (desc & kPairTileMask) * BLK + j * 32;
+      return STRIPED ? chunk_of(desc) + a.n_chunks * key : key;
+    };
     // key block j of the tile of `desc` has a key after the wave's first query
-    auto diag_of = [&](int desc, int j) { return TCAUSAL && kpos_of(desc, j) + 31 > qb * BLK + rg * 32; };
+    auto diag_of = [&](int desc, int j) {
+      return TCAUSAL && kpos_of(desc, j) + kstep * 31 > qb * BLK + rg * 32;
+    };
 
     f32x16 sc[2];        // scores of the next two blocks of the stream (by block parity)
     PBlock pb[2];        // probabilities waiting for their P V product (by block parity)
@@ -1288,8 +1301,8 @@ void attn_bf16_pair_kernel(FwdArgs a) {
       wait_vm();
       __syncthreads();
       tile_scores<D, BLK, false>(sK0, qf, ol, 0, sc);  // blocks 0 and 1 of tile 0
-      if (diag_of(d0, 0)) drop_future(sc[0], qrow, kpos_of(d0, 0), 1, lane >> 5);
-      moved[0] = block_softmax(sc[0], sl2, ref_cur, m_next, pb[0], dead_of(d0));
+      if (diag_of(d0, 0)) drop_future(sc[0], qrow, kpos_of(d0, 0), kstep, lane >> 5);
+      moved[0] = block_softmax(sc[0], sl2, ref_cur, m_next, pb[0], dead_of(d0, 0));
     }
 
     auto consume = [&](const PBlock& p, uint64_t mv) {
@@ -1379,14 +1392,14 @@ void attn_bf16_pair_kernel(FwdArgs a) {
         PBlock& out = pb[SRC];
         const int sdesc = NEXT ? desc1 : desc;
         constexpr int sblk = NEXT ? 0 : j + 1;
-        const bool dead = dead_of(sdesc);
+        const bool dead = dead_of(sdesc, sblk);
         const float dead_add = dead ? kNegInf : 0.f;  // uniform: a dead block's max is -inf
         float mx_a, mx_b, mx, run, ref_exp, lsum;
         auto stage = [&](auto sc_) {
           constexpr int g = decltype(sc_)::value;
           if constexpr (g == 0) {
             if constexpr (TCAUSAL)
-              if (diag_of(sdesc, sblk)) drop_future(sc[SRC], qrow, kpos_of(sdesc, sblk), 1, lane >> 5);
+              if (diag_of(sdesc, sblk)) drop_future(sc[SRC], qrow, kpos_of(sdesc, sblk), kstep, lane >> 5);
             mx_a = fmaxf(fmaxf(s[0], s[1]), s[2]);
             mx_a = fmaxf(fmaxf(mx_a, s[3]), s[4]);
             mx_a = fmaxf(fmaxf(mx_a, s[5]), s[6]);
@@ -1499,12 +1512,18 @@ hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
   const bool general = a.layout == SA_LAYOUT_STRIPED || a.S % BLK != 0;
   const dim3 grid(a.num_bins), block(Shape<D, BLK>::NW * 64);
   if constexpr (BLK == 128) {
-    // Q-block pairs (contiguous layout, S a multiple of the block; checked by the plan)
+    // Q-block pairs (S a multiple of the block; checked by the plan)
     if (a.q_pairs) {
-      if (a.token_causal)
-        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, true>), grid, block, 0, stream, a);
-      else
-        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, false>), grid, block, 0, stream, a);
+      if (a.layout == SA_LAYOUT_STRIPED) {
+        if (a.token_causal)
+          hipLaunchKernelGGL((attn_bf16_pair_kernel<D, true, true>), grid, block, 0, stream, a);
+        else
+          hipLaunchKernelGGL((attn_bf16_pair_kernel<D, true, false>), grid, block, 0, stream, a);
+      } else if (a.token_causal) {
+        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, false, true>), grid, block, 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, false, false>), grid, block, 0, stream, a);
+      }
       return hipGetLastError();
     }
     // striped chunks (S is then a multiple of block * n_chunks) without token-level causality

@@ -87,8 +87,8 @@ struct MergeArgs {
 };
 
 // Kernel launchers (defined in the .hip files).  Return hipSuccess or the launch error.
-// Row, column and per-chunk row counts of the block mask; with prow/pcrow (contiguous layout)
-// also the union counts of Q-block pairs (2p, 2p+1): prow [BH*nP], pcrow [BH][C][nP], nP = ceil(nQ/2).
+// Row, column and per-chunk row counts of the block mask; with prow/pcrow also the union counts
+// of Q-block pairs (2p, 2p+1): prow [BH*nP], pcrow [BH][C][nP], nP = ceil(nQ/2).
 hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_chunks, int layout,
                            int32_t* row, int32_t* col, int32_t* crow, hipStream_t stream,
                            int32_t* prow = nullptr, int32_t* pcrow = nullptr);

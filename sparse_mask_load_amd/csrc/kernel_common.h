@@ -52,25 +52,44 @@ __device__ inline int build_tile_list(const uint8_t* __restrict__ mrow, int nK, 
   return count;
 }
 
-// Tile list of a Q-block pair (contiguous layout): the union of the live KV
-// tiles of mask rows qa (mrow_a) and qa + 1 (the next row, when has_b), for
-// chunks [c0, c1), in chunk then tile order.  A descriptor's group code holds
-// the tile's liveness for each half: bit 0 for row qa, bit 1 for row qa + 1.
+// Tile list of a Q-block pair: the union of the live KV tiles of mask rows qa
+// (mrow_a) and qa + 1 (the next row, when has_b), for chunks [c0, c1), in chunk
+// then tile order, tiles as in build_tile_list (contiguous KV blocks, or the
+// compacted tiles of the striped layout).  A pair descriptor holds the tile
+// index in bits 0..11, the group code of row qa in bits 12..15 and that of row
+// qa + 1 in bits 16..19 (contiguous: all four bits set when the row has the
+// tile), and the chunk in the usual chunk field.
+constexpr int kPairTileMask = 0xFFF;
+constexpr int kPairCodeShift = 12;
 __device__ inline int build_pair_tile_list(const uint8_t* __restrict__ mrow_a, bool has_b, int nK, int n_chunks,
-                                           int c0, int c1, int* list, bool write = true) {
+                                           int layout, int c0, int c1, int* list, bool write = true) {
   const int lane = threadIdx.x & 63;
   const int per_chunk = nK / n_chunks;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const uint8_t* __restrict__ mrow_b = mrow_a + nK;
   int count = 0;
   for (int c = c0; c < c1; ++c) {
-    const int j0 = c * per_chunk, j1 = j0 + per_chunk;
-    for (int base = j0; base < j1; base += 64) {
-      const int j = base + lane;
-      const int code = j < j1 ? ((mrow_a[j] != 0 ? 1 : 0) | (has_b && mrow_b[j] != 0 ? 2 : 0)) : 0;
-      const uint64_t bits = __ballot(code != 0);
-      if (write && code != 0)
-        list[count + __popcll(bits & below)] = j | (code << kDescCodeShift) | (c << kDescChunkShift);
+    for (int base = 0; base < per_chunk; base += 64) {
+      const int t = base + lane;
+      int ca = 0, cb = 0;
+      if (t < per_chunk) {
+        if (layout == SA_LAYOUT_CONTIGUOUS) {
+          const int j = c * per_chunk + t;
+          ca = mrow_a[j] != 0 ? 15 : 0;
+          cb = has_b && mrow_b[j] != 0 ? 15 : 0;
+        } else {
+          for (int g = 0; g < n_chunks; ++g) {
+            ca |= (mrow_a[n_chunks * t + g] != 0 ? 1 : 0) << g;
+            cb |= (has_b && mrow_b[n_chunks * t + g] != 0 ? 1 : 0) << g;
+          }
+        }
+      }
+      const bool live = (ca | cb) != 0;
+      const uint64_t bits = __ballot(live);
+      const int tile = layout == SA_LAYOUT_CONTIGUOUS ? c * per_chunk + t : t;
+      if (write && live)
+        list[count + __popcll(bits & below)] =
+            tile | (ca << kPairCodeShift) | (cb << (kPairCodeShift + 4)) | (c << kDescChunkShift);
       count += __popcll(bits);
     }
   }

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void popcount_kernel(const uint8_t* __restrict
     if (layout == SA_LAYOUT_STRIPED)
       for (int c = 0; c < n_chunks; ++c) crow[((int64_t)bh * n_chunks + c) * nQ + i] = tot;
   }
-  if (prow) {  // contiguous layout only
+  if (prow) {
     const int nP = (nQ + 1) / 2;
     for (int p = threadIdx.x; p < nP; p += blockDim.x) {
       const uint8_t* ma = m + (int64_t)(2 * p) * nK;
@@ -71,9 +71,12 @@ __global__ __launch_bounds__(256) void popcount_kernel(const uint8_t* __restrict
           for (int j = c * per_chunk; j < (c + 1) * per_chunk; ++j) cnt += (ma[j] | mb[j]) != 0;
         }
         tot += cnt;
-        pcrow[((int64_t)bh * n_chunks + c) * nP + p] = cnt;
+        if (layout == SA_LAYOUT_CONTIGUOUS) pcrow[((int64_t)bh * n_chunks + c) * nP + p] = cnt;
       }
       prow[(int64_t)bh * nP + p] = tot;
+      // striped: every chunk holds a slice of each live block, so each chunk's load is the pair's
+      if (layout == SA_LAYOUT_STRIPED)
+        for (int c = 0; c < n_chunks; ++c) pcrow[((int64_t)bh * n_chunks + c) * nP + p] = tot;
     }
   }
   for (int j = threadIdx.x; j < nK; j += blockDim.x) {

@@ -120,8 +120,6 @@ BAD_PROBLEMS = [
     # Q-block pairs: bf16, block 128, contiguous layout, S a multiple of 128
     (dict(q_pairs=1), bd.SA_ERR_UNSUPPORTED),  # block 64
     (dict(q_pairs=1, block=128, S=320, n_chunks=1, sb=2 * 320 * 64, sh=320 * 64), bd.SA_ERR_UNSUPPORTED),
-    (dict(q_pairs=1, block=128, S=512, layout=1, n_chunks=2, sb=2 * 512 * 64, sh=512 * 64),
-     bd.SA_ERR_UNSUPPORTED),
     (dict(q_pairs=1, block=64, dtype=bd.SA_F32), bd.SA_ERR_UNSUPPORTED),
 ]
 

@@ -31,8 +31,8 @@ def _check_pair_plan(w, plan, order):
     info = bd.sparse_attn_plan_info(plan)
     B, H, nQ, C, m = w.B, w.H, w.nQ, w.n_chunks, info["num_bins"]
     nP = (nQ + 1) // 2
-    ref = P.pair_counts(w.mask, C)
-    cnt = P.popcount(w.mask, C)
+    ref = P.pair_counts(w.mask, C, w.layout)
+    cnt = P.popcount(w.mask, C, w.layout)
     assert np.array_equal(bd.sparse_attn_plan_copy(plan, bd.SA_PLAN_PAIR_ROW, B * H * nP), ref["row"].reshape(-1))
     assert np.array_equal(bd.sparse_attn_plan_copy(plan, bd.SA_PLAN_PAIR_CROW, B * H * C * nP),
                           ref["crow"].reshape(-1))
@@ -91,24 +91,28 @@ def _check_every_row(w, plan, q, k, v, scale=None, tc=False):
 
 
 PAIR_CASES = [
-    # (B, H, S, D, C, pattern, density, token_causal, [B,S,H,D] strides)
-    (1, 2, 1024, 128, 4, "causal", 0.0, False, False),
-    (1, 3, 1152, 128, 3, "bernoulli", 0.5, False, False),  # odd nQ = 9: the last pair has one row
-    (2, 2, 1024, 64, 2, "bernoulli", 0.4, False, True),   # D 64, [B,S,H,D] strides
-    (1, 2, 1024, 128, 4, "causal", 0.0, True, False),     # token-level causality
-    (1, 2, 640, 128, 1, "zipf", 0.5, True, False),        # token-causal, odd nQ = 5, one chunk
-    (1, 2, 768, 128, 3, "zipf", 0.5, False, False),
-    (1, 2, 512, 128, 2, "empty", 0.0, False, False),
+    # (B, H, S, D, C, pattern, density, token_causal, [B,S,H,D] strides, layout)
+    (1, 2, 1024, 128, 4, "causal", 0.0, False, False, "contiguous"),
+    (1, 3, 1152, 128, 3, "bernoulli", 0.5, False, False, "contiguous"),  # odd nQ = 9: a lone last row
+    (2, 2, 1024, 64, 2, "bernoulli", 0.4, False, True, "contiguous"),   # D 64, [B,S,H,D] strides
+    (1, 2, 1024, 128, 4, "causal", 0.0, True, False, "contiguous"),     # token-level causality
+    (1, 2, 640, 128, 1, "zipf", 0.5, True, False, "contiguous"),        # token-causal, odd nQ, one chunk
+    (1, 2, 768, 128, 3, "zipf", 0.5, False, False, "contiguous"),
+    (1, 2, 512, 128, 2, "empty", 0.0, False, False, "contiguous"),
+    (1, 2, 2048, 128, 4, "causal", 0.0, False, False, "striped"),      # striped: 32-key groups
+    (1, 2, 2048, 128, 2, "bernoulli", 0.5, False, True, "striped"),    # 64-key groups, strides
+    (1, 2, 1024, 128, 2, "ones", 0.0, True, False, "striped"),         # striped token-causal
+    (1, 3, 1152, 64, 1, "zipf", 0.5, False, False, "striped"),         # one chunk, odd nQ, D 64
 ]
 
 
 @pytest.mark.parametrize("n", range(len(PAIR_CASES)),
-                         ids=[f"{c[5]}-S{c[2]}-d{c[3]}-C{c[4]}{'-tc' if c[7] else ''}{'-bshd' if c[8] else ''}"
-                              for c in PAIR_CASES])
+                         ids=[f"{c[5]}-S{c[2]}-d{c[3]}-C{c[4]}-{c[9][:4]}{'-tc' if c[7] else ''}"
+                              f"{'-bshd' if c[8] else ''}" for c in PAIR_CASES])
 def test_pair_cases_every_row(n):
-    B, H, S, D, C, pattern, dens, tc, bshd = PAIR_CASES[n]
+    B, H, S, D, C, pattern, dens, tc, bshd, layout = PAIR_CASES[n]
     w = W.make_custom(B, H, S, D, block=128, n_chunks=C, dtype="bf16", pattern=pattern, density=dens,
-                      seed=500 + n)
+                      seed=500 + n, layout=layout)
     print(f"pair case {n}: {PAIR_CASES[n]}", flush=True)
     q, k, v = G.upload(w, layout_bshd=bshd)
     for order, bins in (("lpt", 0), ("lpt", 7), ("lpt_device", 0), ("naive", 5)):
@@ -122,8 +126,7 @@ def test_pair_cases_every_row(n):
         plan.close()
 
 
-@pytest.mark.parametrize("n", [i for i, c in enumerate(LR.RESCALE_CASES)
-                               if c[4] == 128 and c[8] == "contiguous" and c[2] % 128 == 0],
+@pytest.mark.parametrize("n", [i for i, c in enumerate(LR.RESCALE_CASES) if c[4] == 128 and c[2] % 128 == 0],
                          ids=lambda n: LR.rescale_case_id(LR.RESCALE_CASES[n]))
 def test_pair_rescale_every_row(n):
     """Inputs that move the lazy exponent reference inside a chunk (the CPU replay with the pair
@@ -170,6 +173,27 @@ def test_causal_pairs_bench_path(causal_w):
     G.assert_close(G.to64(o)[0, 11, 100 * 128:102 * 128], ref_b, G.BF16_TOL, "pair 50")
     o_single = G.run_full(G.plan_block(w, q, order="lpt_device"), q, k, v)
     G.assert_close(G.to64(o), G.to64(o_single), (2e-2, 1e-3), "pairs vs single Q-blocks")
+
+
+def test_causal_striped_pairs_against_oracle():
+    """The causal workload in the striped layout with pair items: the device-planned order, the
+    partial-mode forward and the merge against the oracle on sampled rows, every chunk's partial,
+    and full mode."""
+    w = W.make(3, layout="striped")
+    q, k, v = G.upload(w)
+    plan = G.plan_block(w, q, order="lpt_device", q_pairs=True)
+    info = _check_pair_plan(w, plan, "lpt_device")
+    assert info["makespan"] == info["lower_bound"]
+    rows = G.sample_rows(w, 96, seed=12)
+    idx = tuple(np.array(rows).T)
+    ref, ref_lse = A.masked_attention(w.q, w.k, w.v, w.mask, w.block, rows=rows)
+    op, mp, lp = G.run_partial(plan, q, k, v, 0, w.n_chunks)
+    _check_partials(w, op, mp, lp, 0, w.n_chunks, rows=rows)
+    om, lse = G.merge(op, mp, lp)
+    G.assert_close(G.to64(om)[idx], ref, G.BF16_TOL, "striped pairs merged")
+    G.assert_close(G.to64(lse)[idx], ref_lse, G.ROWSUM_TOL, "striped pairs lse")
+    del op, mp, lp
+    G.assert_close(G.to64(G.run_full(plan, q, k, v))[idx], ref, G.BF16_TOL, "striped pairs full")
 
 
 def test_causal_pairs_token_causal(causal_w):

@@ -262,6 +262,10 @@ def test_pair_counts_against_set_unions():
         nK = C * int(rng.integers(1, 5))
         mask = (rng.random((B, H, nQ, nK)) < rng.random()).astype(np.uint8)
         got = P.pair_counts(mask, C)
+        striped = P.pair_counts(mask, C, "striped")
+        assert np.array_equal(striped["row"], got["row"])
+        # a striped chunk holds a slice of every live block: its load is the whole union
+        assert all(np.array_equal(striped["crow"][:, :, c, :], got["row"]) for c in range(C))
         nP = (nQ + 1) // 2
         assert got["row"].shape == (B, H, nP) and got["crow"].shape == (B, H, C, nP)
         for b in range(B):
