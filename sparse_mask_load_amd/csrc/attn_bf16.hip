@@ -1180,7 +1180,8 @@ void attn_bf16_pair_kernel(FwdArgs a) {
   const bf16* __restrict__ gV = (const bf16*)a.v;
   const int bin = blockIdx.x;
   const int p_begin = a.bin_ptr[bin], p_end = a.bin_ptr[bin + 1];
-  const float sl2 = a.scale_log2;
+  const float sl2 = a.scale_log2;   // > 0
+  const float inv_sl2 = 1.f / sl2;
 
   for (int pos = p_begin; pos < p_end; ++pos) {
     const int64_t t_start = realtime_now();
@@ -1209,6 +1210,11 @@ void attn_bf16_pair_kernel(FwdArgs a) {
     RowState<ND> st;  // acc and l relative to st.m_ref (the reference of the last consumed block)
     reset(st);
     int cur_chunk = a.c0;
+    // Row maxima are kept per lane, over the lane's own keys and in raw score units (the
+    // scale is positive): lmax for the accumulation in progress, lmax_next for one that starts
+    // with the next tile (partial mode).  A row's true max (both half-waves) is formed only
+    // where it is needed: when a reference may move, and when a partial is written.
+    float lmax = kNegInf, lmax_next = kNegInf;
 
     // Writes chunk `chunk`'s partial of this wave's rows (O unnormalised, m, l in the
     // true-max basis) and resets the state.  D = 128: the O rows go through `stage`, a
@@ -1217,8 +1223,9 @@ void attn_bf16_pair_kernel(FwdArgs a) {
     // writes eight whole 128-byte row segments; otherwise straight from the registers.
     auto flush_partial = [&](int chunk, float* stage) {
       const int ln = opaque(lane), l32 = ln & 31, h2 = ln >> 5;
-      const bool any = st.m_true != kNegInf;
-      const float corr = any ? __builtin_amdgcn_exp2f(st.m_ref - st.m_true) : 0.f;
+      const float m_true = fmaxf(lmax, other_half(lmax)) * sl2;  // the row's true max, log2 units
+      const bool any = m_true != kNegInf;
+      const float corr = any ? __builtin_amdgcn_exp2f(st.m_ref - m_true) : 0.f;
       const float l_row = (st.l + other_half(st.l)) * corr;
       if (!absent) {
         const int64_t prow0 = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK + rg * 32;
@@ -1263,11 +1270,12 @@ void attn_bf16_pair_kernel(FwdArgs a) {
             }
         }
         if (h2 == 0) {
-          a.m_part[prow0 + l32] = any ? st.m_true * kLn2 : kNegInf;
+          a.m_part[prow0 + l32] = any ? m_true * kLn2 : kNegInf;
           a.l_part[prow0 + l32] = l_row;
         }
       }
       reset(st);
+      lmax = kNegInf;
     };
     // this wave's slice of a tile buffer (the slots its own tile loads write), as staging
     auto stage_of = [&](bf16* buf) { return (float*)(buf + wave * SH::IPW * 64 * 8); };
@@ -1291,8 +1299,24 @@ void attn_bf16_pair_kernel(FwdArgs a) {
     f32x16 sc[2];        // scores of the next two blocks of the stream (by block parity)
     PBlock pb[2];        // probabilities waiting for their P V product (by block parity)
     uint64_t moved[2];   // rows whose reference moved with that block
-    float ref_cur = kNegInf;  // reference of the latest block exponentiated
-    float m_next = kNegInf;   // running max of a chunk that starts with the next tile (partial mode)
+    float ref_cur = kNegInf;  // reference of the latest block exponentiated (log2 units)
+    float thr = kNegInf;      // raw score above which that reference moves: (ref_cur + slack) / scale
+    // A row's reference moves when its running max (both half-waves) exceeds thr: the lanes
+    // compare their own maxima, and only a ballot with a lane above thr forms the row maxima.
+    // A block's PBlock::ref is written only then (it is read only for a block whose ballot
+    // of moved rows is not empty).
+    auto move_ref = [&](float mx, float& ref, float& th, float& pref) {
+      uint64_t mv = 0;
+      if (__builtin_amdgcn_ballot_w64(mx > th)) {
+        const float rm = fmaxf(mx, other_half(mx));
+        const bool up = rm > th;
+        ref = up ? rm * sl2 : ref;
+        th = up ? (ref + kRescaleSlack) * inv_sl2 : th;
+        pref = ref;
+        mv = __builtin_amdgcn_ballot_w64(up);
+      }
+      return mv;
+    };
     if (n_tiles > 0) {
       const int d0 = __builtin_amdgcn_readfirstlane(sList[0]);
       loader.template issue<false>(gK, src_of(d0), sK0, wave);
@@ -1302,17 +1326,26 @@ void attn_bf16_pair_kernel(FwdArgs a) {
       __syncthreads();
       tile_scores<D, BLK, false>(sK0, qf, ol, 0, sc);  // blocks 0 and 1 of tile 0
       if (diag_of(d0, 0)) drop_future(sc[0], qrow, kpos_of(d0, 0), kstep, lane >> 5);
-      moved[0] = block_softmax(sc[0], sl2, ref_cur, m_next, pb[0], dead_of(d0, 0));
+      const bool dead = dead_of(d0, 0);
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+      lmax_next = dead ? kNegInf : mx;
+      moved[0] = move_ref(lmax_next, ref_cur, thr, pb[0].ref);
+      float l0 = 0.f, l1 = 0.f;
+      tile_probs(sc[0], sl2, dead ? __builtin_huge_valf() : (ref_cur == kNegInf ? 0.f : ref_cur), pb[0].p, l0, l1);
+      pb[0].lsum = l0 + l1;
     }
 
+    // Adds block p to the state; st.m_ref changes only with a moved reference.
     auto consume = [&](const PBlock& p, uint64_t mv) {
       if (mv) {
         const float alpha = (TCAUSAL && st.m_ref == p.ref) ? 1.f : __builtin_amdgcn_exp2f(st.m_ref - p.ref);
         st.l *= alpha;
 #pragma unroll
         for (int d = 0; d < ND; ++d) st.acc[d] *= alpha;
+        st.m_ref = p.ref;
       }
-      st.m_ref = p.ref;
       st.l += p.lsum;
     };
 
@@ -1347,7 +1380,7 @@ void attn_bf16_pair_kernel(FwdArgs a) {
           while (cur_chunk < chunk_of(desc)) flush_partial(cur_chunk++, stage_of(lfree));
           fresh = true;
         }
-        if (fresh) st.m_true = m_next;
+        if (fresh) lmax = lmax_next;
       }
       const TileSrc src = H == 0 ? src_of(desc1) : src_of(__builtin_amdgcn_readfirstlane(sList[min(t + 2, n_tiles - 1)]));
       const bf16* const gsrc = H == 0 ? gV : gK;
@@ -1392,43 +1425,41 @@ void attn_bf16_pair_kernel(FwdArgs a) {
         PBlock& out = pb[SRC];
         const int sdesc = NEXT ? desc1 : desc;
         constexpr int sblk = NEXT ? 0 : j + 1;
-        const bool dead = dead_of(sdesc, sblk);
-        const float dead_add = dead ? kNegInf : 0.f;  // uniform: a dead block's max is -inf
-        float mx_a, mx_b, mx, run, ref_exp, lsum;
+        const bool dead = dead_of(sdesc, sblk);  // uniform
+        float mx_a, mx_b, mx, seed, ref_exp, lsum;
+        uint64_t mv;
         auto stage = [&](auto sc_) {
           constexpr int g = decltype(sc_)::value;
           if constexpr (g == 0) {
             if constexpr (TCAUSAL)
               if (diag_of(sdesc, sblk)) drop_future(sc[SRC], qrow, kpos_of(sdesc, sblk), kstep, lane >> 5);
-            mx_a = fmaxf(fmaxf(s[0], s[1]), s[2]);
-            mx_a = fmaxf(fmaxf(mx_a, s[3]), s[4]);
-            mx_a = fmaxf(fmaxf(mx_a, s[5]), s[6]);
+            // the running max this block folds into (a new accumulation starts empty)
+            seed = (NEXT && next_new) ? kNegInf : lmax;
+            mx_a = fmaxf(fmaxf(seed, s[0]), s[1]);
+            mx_a = fmaxf(fmaxf(mx_a, s[2]), s[3]);
+            mx_a = fmaxf(fmaxf(mx_a, s[4]), s[5]);
           } else if constexpr (g == 1) {
-            mx_b = fmaxf(fmaxf(s[8], s[9]), s[10]);
+            mx_b = fmaxf(fmaxf(s[6], s[7]), s[8]);
+            mx_b = fmaxf(fmaxf(mx_b, s[9]), s[10]);
             mx_b = fmaxf(fmaxf(mx_b, s[11]), s[12]);
             mx_b = fmaxf(fmaxf(mx_b, s[13]), s[14]);
-            mx = fmaxf(fmaxf(mx_a, s[7]), fmaxf(mx_b, s[15]));
+            mx = fmaxf(fmaxf(mx_a, mx_b), s[15]);
           } else if constexpr (g == 2) {
-            mx = fmaf(fmaxf(mx, other_half(mx)), sl2, dead_add);
-          } else if constexpr (g == 3) {
-            if constexpr (!NEXT) {
-              run = st.m_true;
-            } else {
+            mx = dead ? seed : mx;  // a dead block has no live key
+            if constexpr (NEXT) {
               ref_cur = next_new ? kNegInf : ref_cur;
-              run = next_new ? kNegInf : st.m_true;
+              thr = next_new ? kNegInf : thr;
             }
-            run = fmaxf(run, mx);
-            const bool up = mx > ref_cur + kRescaleSlack;
-            ref_cur = up ? run : ref_cur;
-            out.ref = ref_cur;
+            mv = move_ref(mx, ref_cur, thr, out.ref);
+          } else if constexpr (g == 3) {
             // reference of the exponent: +inf makes a dead block's probabilities 0
             ref_exp = dead ? __builtin_huge_valf() : (TCAUSAL && ref_cur == kNegInf) ? 0.f : ref_cur;
-            moved[SRC] = __builtin_amdgcn_ballot_w64(up);
+            moved[SRC] = mv;
             if constexpr (!NEXT) {
-              st.m_true = run;
+              lmax = mx;
             } else {
-              m_next = run;
-              st.m_true = (has_next && !next_new) ? run : st.m_true;
+              lmax_next = mx;
+              lmax = (has_next && !next_new) ? mx : lmax;
             }
             lsum = 0.f;
           } else if constexpr (g < 12) {
