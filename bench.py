@@ -249,11 +249,14 @@ class WorkloadRun:
         return "attn_bf16_kernel"
 
     def timed(self, fn, reps):
-        """Mean time of fn() over reps launches (HIP events on the current stream, one untimed launch first)."""
+        """Mean time of fn() over reps launches (HIP events on the current stream), after three
+        untimed launches (the first launches after a different kernel mix run slower while the
+        caches turn over)."""
         torch = self.torch
         stream = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
+        for _ in range(3):
+            fn()
         e0.record(stream)
         for _ in range(reps):
             fn()
