@@ -249,13 +249,18 @@ class WorkloadRun:
         return "attn_bf16_kernel"
 
     def timed(self, fn, reps):
-        """Mean time of fn() over reps launches (HIP events on the current stream), after three
-        untimed launches (the first launches after a different kernel mix run slower while the
-        caches turn over)."""
+        """Mean time of fn() over reps launches (HIP events on the current stream), after about
+        30 ms of untimed launches (at least three): right after the timed partial-mode loop the
+        first dozen full-mode launches run about 10% slower than later ones."""
         torch = self.torch
         stream = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        once = time.perf_counter() - t0
+        for _ in range(min(50, max(3, int(0.03 / max(once, 1e-6))))):
             fn()
         e0.record(stream)
         for _ in range(reps):
@@ -308,6 +313,46 @@ class WorkloadRun:
         prev.close()
         return (t1 - t0) * 1e3 / n, float(np.mean([a.elapsed_time(b) for a, b in fwd]))
 
+    def ring_steps(self, order, reps):
+        """The ring emulation: one forward launch per KV chunk, each over that chunk's own LPT list
+        (the per-step greedy), then the merge.  Per chunk: its time, the planned bin max/mean of
+        its own list and of the full-range list carrying the same chunk's loads (one assignment
+        reused for every step), and the measured per-CU balance."""
+        bd, torch = self.bd, self.torch
+        p = self.plan(order)
+        info = bd.sparse_attn_plan_info(p)
+        m, n, C = info["num_bins"], info["n_items"], self.C
+        nI = (info["nQ"] + 1) // 2 if self.q_pairs else info["nQ"]
+        items0 = bd.sparse_attn_plan_copy(p, bd.SA_PLAN_ITEMS, n)
+        ptr0 = bd.sparse_attn_plan_copy(p, bd.SA_PLAN_BIN_PTR, m + 1)
+        crow = bd.sparse_attn_plan_copy(p, bd.SA_PLAN_PAIR_CROW if self.q_pairs else bd.SA_PLAN_CROW,
+                                        self.B * self.H * C * nI).reshape(self.B * self.H, C, nI)
+        bin_of = np.repeat(np.arange(m), np.diff(ptr0))
+        chunks = []
+        for c in range(C):
+            own = bd.sparse_attn_plan_copy(p, bd.SA_PLAN_BIN_LOAD, m, chunk=c)
+            full = np.bincount(bin_of, weights=crow[items0 // nI, c, items0 % nI], minlength=m)
+            trace = torch.zeros((n, 4), dtype=torch.int64, device=self.q.device)
+            args = dict(o_part=self.o_part[c], m_part=self.m_part[c], l_part=self.l_part[c])
+            bd.sparse_attn_fwd(p, self.q, self.k, self.v, c, c + 1, trace=trace, **args)
+            torch.cuda.synchronize()
+            bal = per_cu_balance(trace.cpu().numpy())
+            ms = self.timed(lambda: bd.sparse_attn_fwd(p, self.q, self.k, self.v, c, c + 1, **args), reps)
+            chunks.append({"chunk": c, "fwd_ms": round(ms, 4), "live_tiles": int(crow[:, c, :].sum()),
+                           "planned_bin_max_over_mean_own_list": round(float(own.max() / own.mean()), 4),
+                           "planned_bin_max_over_mean_full_list": round(float(full.max() / full.mean()), 4),
+                           "measured_cu_max_over_mean": round(bal["measured_cu_max_over_mean"], 4)})
+
+        def ring():
+            for c in range(C):
+                bd.sparse_attn_fwd(p, self.q, self.k, self.v, c, c + 1, o_part=self.o_part[c],
+                                   m_part=self.m_part[c], l_part=self.l_part[c])
+            self.merge()
+        step = self.timed(ring, reps)
+        p.close()
+        return {"per_chunk": chunks, "fwd_ms_sum": round(sum(x["fwd_ms"] for x in chunks), 4),
+                "ring_step_ms": round(step, 4)}
+
     def order_summary(self, order, reps):
         """Fused and partial forward time of one work order, its planned and measured per-CU balance."""
         bd, torch = self.bd, self.torch
@@ -328,9 +373,10 @@ class WorkloadRun:
                 "measured_cu_max_over_mean": round(bal["measured_cu_max_over_mean"], 4)}
 
 
-def workload_summary(bd, W, torch, dev, cfg, layout="contiguous", steps=10, reps=5):
+def workload_summary(bd, W, torch, dev, cfg, layout="contiguous", steps=10, reps=5, ring=False):
     """Untimed extra: another workload's whole step (device plan, partial forward over every chunk,
-    merge) and its forward in device-planned LPT, host LPT and round-robin order."""
+    merge) and its forward in device-planned LPT, host LPT and round-robin order; with `ring`,
+    also the one-launch-per-chunk ring emulation."""
     w = W.make(cfg, layout=layout)
     run = WorkloadRun(bd, torch, dev, w)
     items = "Q-block pairs" if run.q_pairs else "Q-blocks"
@@ -349,6 +395,8 @@ def workload_summary(bd, W, torch, dev, cfg, layout="contiguous", steps=10, reps
            "fwd_partial_ms": round(fwd_ms, 4), "fwd_partial_tflops": round(flop / fwd_ms / 1e9, 2),
            "merge_ms": round(merge_ms, 4), "merge_gbs": round(run.merge_bytes() / merge_ms / 1e6, 1),
            "by_order": {o: run.order_summary(o, reps) for o in ("lpt_device", "lpt", "naive")}}
+    if ring:
+        out["ring_steps"] = run.ring_steps("lpt_device", reps)
     del run
     torch.cuda.empty_cache()
     return out
@@ -563,6 +611,8 @@ def main() -> int:
         torch.cuda.synchronize()
         naive_balance = per_cu_balance(tr_naive.cpu().numpy())
         p_naive.close()
+        # the ring emulation: one launch per chunk over its own list (per-step LPT), then the merge
+        ring = run.ring_steps(args.order, reps)
         # the same step's forward with single Q-block items (when the step uses pairs)
         single = {}
         if run.q_pairs:
@@ -588,6 +638,7 @@ def main() -> int:
             "plan_device_call_ms": round(plan_device_call_ms, 4), "plan_device_gpu_ms": round(plan_device_gpu_ms, 4),
             "ms_per_step_by_planner": {args.order: round(ms_per_step, 4), other_order: round(step_other_ms, 4)},
             "pair_overhead": run.pair_overhead, **single,
+            "ring_steps": ring,
         }
     plan.close()
 
@@ -610,7 +661,7 @@ def main() -> int:
                 other_layout = "striped" if args.layout == "contiguous" else "contiguous"
                 others[f"causal_{other_layout}"] = workload_summary(bd, W, torch, dev, 3, other_layout)
             others["video"] = workload_summary(bd, W, torch, dev, 2)
-            others["skewed"] = workload_summary(bd, W, torch, dev, 4)
+            others["skewed"] = workload_summary(bd, W, torch, dev, 4, ring=True)
             result["workloads"] = others
         if not args.no_topk:
             result["topk_path"] = topk_path(bd, W, torch, dev)
