@@ -749,35 +749,6 @@ __device__ __forceinline__ void drop_future(f32x16& s, int qpos, int kpos, int k
     if (16 * (r >> 3) + (r & 7) > off_max) s[r] = kNegInf;
 }
 
-// One 32-key block's step of the online softmax for rows whose scores are all
-// finite: the block's row max (both half-waves), its fold into the running
-// true max, the lazy move of the reference (a row whose block max exceeds its
-// reference by more than the slack takes its running max) and the block's
-// rounded probabilities with their row sum.  Returns the ballot of the rows
-// whose reference moved.
-__device__ __forceinline__ uint64_t block_softmax(const f32x16& s, float sl2, float& ref, float& m_true,
-                                                  PBlock& pb, bool dead = false) {
-  float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
-  float b = fmaxf(fmaxf(s[8], s[9]), s[10]);
-  a = fmaxf(fmaxf(a, s[3]), s[4]);
-  b = fmaxf(fmaxf(b, s[11]), s[12]);
-  a = fmaxf(fmaxf(a, s[5]), s[6]);
-  b = fmaxf(fmaxf(b, s[13]), s[14]);
-  float mx = fmaxf(fmaxf(a, s[7]), fmaxf(b, s[15]));
-  mx = fmaxf(mx, other_half(mx)) * sl2;
-  mx = dead ? kNegInf : mx;  // a dead block (striped layout) has no live key
-  m_true = fmaxf(m_true, mx);
-  const bool up = mx > ref + kRescaleSlack;
-  ref = up ? m_true : ref;
-  pb.ref = ref;
-  float l0 = 0.f, l1 = 0.f;
-  // a dead block's P is 0; a row without a finite score yet (token-level causality) takes
-  // reference 0 so that its dropped scores give 0, not exp(-inf + inf)
-  tile_probs(s, sl2, dead ? __builtin_huge_valf() : (ref == kNegInf ? 0.f : ref), pb.p, l0, l1);
-  pb.lsum = l0 + l1;
-  return __builtin_amdgcn_ballot_w64(up);
-}
-
 // Full-tile kernel for 128-key blocks (S a multiple of the block, no
 // token-level causality), software-pipelined per 32-key block.  The
 // wave's work is a stream of blocks b (two per tile): the S MFMAs of block
@@ -831,7 +802,8 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
   const bf16* __restrict__ gV = (const bf16*)a.v;
   const int bin = blockIdx.x;
   const int p_begin = a.bin_ptr[bin], p_end = a.bin_ptr[bin + 1];
-  const float sl2 = a.scale_log2;
+  const float sl2 = a.scale_log2;   // > 0
+  const float inv_sl2 = 1.f / sl2;
 
   for (int pos = p_begin; pos < p_end; ++pos) {
     const int64_t t_start = realtime_now();
@@ -857,6 +829,12 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
     RowState<ND> st;  // acc and l relative to st.m_ref (the reference of the last consumed block)
     reset(st);
     int cur_chunk = a.c0;
+    // Row maxima are kept per lane, over the lane's own keys and in raw score units (the
+    // scale is positive): lmax for the accumulation in progress, lmax_next for one that starts
+    // with the next tile (partial mode).  The wave's row max (both half-waves) is formed when
+    // a reference may move and when the key halves are merged (st.m_true).
+    float lmax = kNegInf, lmax_next = kNegInf;
+    auto true_max = [&]() { st.m_true = fmaxf(lmax, other_half(lmax)) * sl2; };
 
     // Same flush as the general kernel: merge the key halves, write chunk
     // `chunk`'s partial through the staging buffers, reset the state.
@@ -870,6 +848,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       // lane-derived addresses are formed here, not kept live across the tile loop
       const int ln = opaque(lane), l32 = ln & 31, h2 = ln >> 5;
       float m, l_row;
+      true_max();
       merge_halves<D, BLK>(st, m, l_row, kscr, mscr, rg, kh, ln);
       const int64_t prow0 = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK;
       if (kh == 0) {
@@ -901,6 +880,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       }
       __syncthreads();
       reset(st);
+      lmax = kNegInf;
     };
     auto src_of = [&](int desc) { return tile_source(desc, bh_base, a.ss, a.S, LAYOUT, a.n_chunks, BLK); };
     auto chunk_of = [&](int desc) { return (desc >> kDescChunkShift) & 63; };
@@ -923,8 +903,24 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
     f32x16 sc[NB];       // scores of the two blocks of the next tile to be exponentiated
     PBlock pb[NB];       // probabilities waiting for their P V product
     uint64_t moved[NB];  // rows whose reference moved with that block
-    float ref_cur = kNegInf;  // reference of the latest block exponentiated
-    float m_next = kNegInf;   // running max of a chunk that starts with the next tile (partial mode)
+    float ref_cur = kNegInf;  // reference of the latest block exponentiated (log2 units)
+    float thr = kNegInf;      // raw score above which that reference moves: (ref_cur + slack) / scale
+    // A row's reference moves when its running max (both half-waves) exceeds thr: the lanes
+    // compare their own maxima, and only a ballot with a lane above thr forms the row maxima.
+    // A block's PBlock::ref is written only then (it is read only for a block whose ballot
+    // of moved rows is not empty).
+    auto move_ref = [&](float mx, float& ref, float& th, float& pref) {
+      uint64_t mv = 0;
+      if (__builtin_amdgcn_ballot_w64(mx > th)) {
+        const float rm = fmaxf(mx, other_half(mx));
+        const bool up = rm > th;
+        ref = up ? rm * sl2 : ref;
+        th = up ? (ref + kRescaleSlack) * inv_sl2 : th;
+        pref = ref;
+        mv = __builtin_amdgcn_ballot_w64(up);
+      }
+      return mv;
+    };
     if (n_tiles > 0) {
       const int d0 = __builtin_amdgcn_readfirstlane(sList[0]);
       loader.template issue<false>(gK, src_of(d0), sK0, wave);
@@ -933,10 +929,18 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       wait_vm();
       __syncthreads();
       tile_scores<D, BLK, false>(sK0, qf, ol, 0, sc);
-      // block 0 starts an accumulation: its running max goes to m_next, which
+      // block 0 starts an accumulation: its running max goes to lmax_next, which
       // the first tile takes over (after flushing any empty leading chunks)
       if (diag_of(d0, 0)) drop_future(sc[0], qrow, kpos_of(d0, 0), kstep, lane >> 5);
-      moved[0] = block_softmax(sc[0], sl2, ref_cur, m_next, pb[0], dead_of(d0, 0));
+      const bool dead = dead_of(d0, 0);
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+      lmax_next = dead ? kNegInf : mx;
+      moved[0] = move_ref(lmax_next, ref_cur, thr, pb[0].ref);
+      float l0 = 0.f, l1 = 0.f;
+      tile_probs(sc[0], sl2, dead ? __builtin_huge_valf() : (ref_cur == kNegInf ? 0.f : ref_cur), pb[0].p, l0, l1);
+      pb[0].lsum = l0 + l1;
     }
 
     // Brings the accumulators and row sum to the reference of block pb, then
@@ -948,8 +952,8 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
         st.l *= alpha;
 #pragma unroll
         for (int d = 0; d < ND; ++d) st.acc[d] *= alpha;
+        st.m_ref = p.ref;  // (changes only with a moved reference)
       }
-      st.m_ref = p.ref;
       st.l += p.lsum;
     };
 
@@ -975,7 +979,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
         while (cur_chunk < chunk_of(desc)) flush_partial(cur_chunk++, (float*)kfree, (float*)vfree);
         fresh = true;
       }
-      if (fresh) st.m_true = m_next;
+      if (fresh) lmax = lmax_next;
       const TileSrc srcK = src_of(__builtin_amdgcn_readfirstlane(sList[min(t + 2, n_tiles - 1)]));
       const TileSrc srcV = src_of(desc1);
 
@@ -1013,43 +1017,42 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
         constexpr int SRC = j == 0 ? 1 : 0;
         const f32x16& s = sc[SRC];
         PBlock& out = pb[SRC];
-        float mx_a, mx_b, mx, run, ref_exp, l0, l1;
+        float mx_a, mx_b, mx, seed, ref_exp, l0, l1;
+        uint64_t mv;
+        constexpr bool NEXT = j == 1;  // block 0 of the next tile
+        const bool dead = STRIPED && dead_sec[j];  // uniform
         auto stage = [&](auto sc_) {
           constexpr int g = decltype(sc_)::value;
           if constexpr (g == 0) {
             if constexpr (TCAUSAL)
               if (diag_sec[j]) drop_future(sc[SRC], qrow, kpos_sec[j], kstep, lane >> 5);
-            mx_a = fmaxf(fmaxf(s[0], s[1]), s[2]);
-            mx_a = fmaxf(fmaxf(mx_a, s[3]), s[4]);
-            mx_a = fmaxf(fmaxf(mx_a, s[5]), s[6]);
+            // the running max this block folds into (a new accumulation starts empty)
+            seed = (NEXT && next_new) ? kNegInf : lmax;
+            mx_a = fmaxf(fmaxf(seed, s[0]), s[1]);
+            mx_a = fmaxf(fmaxf(mx_a, s[2]), s[3]);
+            mx_a = fmaxf(fmaxf(mx_a, s[4]), s[5]);
           } else if constexpr (g == 1) {
-            mx_b = fmaxf(fmaxf(s[8], s[9]), s[10]);
+            mx_b = fmaxf(fmaxf(s[6], s[7]), s[8]);
+            mx_b = fmaxf(fmaxf(mx_b, s[9]), s[10]);
             mx_b = fmaxf(fmaxf(mx_b, s[11]), s[12]);
             mx_b = fmaxf(fmaxf(mx_b, s[13]), s[14]);
-            mx = fmaxf(fmaxf(mx_a, s[7]), fmaxf(mx_b, s[15]));
+            mx = fmaxf(fmaxf(mx_a, mx_b), s[15]);
           } else if constexpr (g == 2) {
-            mx = fmaxf(mx, other_half(mx)) * sl2;
-            if constexpr (STRIPED) mx = dead_sec[j] ? kNegInf : mx;
-          } else if constexpr (g == 3) {
-            if constexpr (j == 0) {
-              run = st.m_true;
-            } else {
+            mx = dead ? seed : mx;  // a dead block has no live key
+            if constexpr (NEXT) {
               ref_cur = next_new ? kNegInf : ref_cur;
-              run = next_new ? kNegInf : st.m_true;
+              thr = next_new ? kNegInf : thr;
             }
-            run = fmaxf(run, mx);
-            const bool up = mx > ref_cur + kRescaleSlack;
-            ref_cur = up ? run : ref_cur;
-            out.ref = ref_cur;
+            mv = move_ref(mx, ref_cur, thr, out.ref);
+          } else if constexpr (g == 3) {
             // reference of the exponent: +inf makes a dead block's probabilities 0
-            ref_exp = (STRIPED && dead_sec[j]) ? __builtin_huge_valf()
-                      : (TCAUSAL && ref_cur == kNegInf) ? 0.f : ref_cur;
-            moved[SRC] = __builtin_amdgcn_ballot_w64(up);
-            if constexpr (j == 0) {
-              st.m_true = run;
+            ref_exp = dead ? __builtin_huge_valf() : (TCAUSAL && ref_cur == kNegInf) ? 0.f : ref_cur;
+            moved[SRC] = mv;
+            if constexpr (!NEXT) {
+              lmax = mx;
             } else {
-              m_next = run;
-              st.m_true = (has_next && !next_new) ? run : st.m_true;
+              lmax_next = mx;
+              lmax = (has_next && !next_new) ? mx : lmax;
             }
             l0 = 0.f;
             l1 = 0.f;
@@ -1100,6 +1103,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
     } else {
       const int ln = opaque(lane), h2 = ln >> 5;
       float m, l_row;
+      true_max();
       merge_halves<D, BLK>(st, m, l_row, (float*)sK0, (float*)sV0, rg, kh, ln);
       const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
       if (kh == 0) {
