@@ -63,10 +63,13 @@ def test_noalloc_matches_plan_and_forward_on_two_calls():
 
 
 def test_noalloc_with_q_block_pairs_on_two_calls():
-    # pair items: the causal workload, then an odd number of Q-blocks (a lone last pair row)
+    # pair items: the causal workload, then an odd number of Q-blocks (a lone last pair row),
+    # then striped chunks
     _check(W.make(3), seed=3, q_pairs=True)
     _check(W.make_custom(1, 3, 1152, 128, block=128, n_chunks=3, dtype="bf16", pattern="bernoulli", density=0.5,
                          seed=42), seed=4, q_pairs=True)
+    _check(W.make_custom(1, 2, 2048, 128, block=128, n_chunks=4, dtype="bf16", pattern="causal", seed=43,
+                         layout="striped"), seed=5, q_pairs=True)
 
 
 def test_noalloc_rejects_oversized_problems_on_the_gpu():
