@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       op[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (mp[i] != kNegInf) op[i] = *(const f32x4*)(a.o[p0 + i] + row * D + dq);
+      // each O vector is read once: a streaming (nontemporal) load
+      if (mp[i] != kNegInf) op[i] = __builtin_nontemporal_load((const f32x4*)(a.o[p0 + i] + row * D + dq));
     }
 #pragma unroll
     for (int i = 0; i < G; ++i) {
