@@ -4,14 +4,14 @@
 // gives one.
 //
 // One wavefront per query.  A key row of D bf16 values is read by D/8 lanes
-// (16 bytes each), so a wave reads 64/(D/8) gathered rows per instruction.
-// Pass 1 forms the scores (in-group reduction over the D/8 lanes) into LDS;
-// pass 2 takes the max, the exp2 weights and the weighted V sum; the partial
-// sums of the row groups are combined at the end.  Bound by the gather: every
-// selected key costs one K row and one V row, and a row's address is known
-// only once its index is loaded, so each pass issues kUnroll independent row
-// loads per lane group before it uses any of them (a few: occupancy, which the
-// LDS score buffer sized to top_k keeps high, matters more than depth per wave).
+// (16 bytes each), so a wave holds 64/(D/8) lane groups, each taking its own
+// keys.  One pass: a group gathers the K and V rows of kUnroll keys together,
+// forms their scores (in-group reduction over the D/8 lanes) and folds them into
+// its online-softmax state (running max, row sum and weighted V sum, rescaled
+// when the max grows); the groups' states are merged at the end by the same
+// rule.  Bound by the gather: every selected key costs one K row and one V row,
+// and a row's address is known only once its index is loaded, so the indices of
+// the next kUnroll keys are loaded while the current rows are in flight.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -24,13 +24,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kWaves = 4;
 constexpr int kMaxTopK = 2048;
-constexpr int kUnroll = 4;  // gathered rows in flight per lane group
+constexpr int kUnroll = 4;  // keys per lane group and step (their K and V rows in flight together)
 
 template <int D>
 __global__ __launch_bounds__(64 * kWaves) void gather_attn_kernel(GatherArgs a) {
   constexpr int LPR = D / 8;     // lanes per key row
-  constexpr int KPI = 64 / LPR;  // key rows per wave instruction
-  extern __shared__ float sScore[];  // [kWaves][top_k]: sized by the launch, so short lists keep occupancy
+  constexpr int KPI = 64 / LPR;  // lane groups (keys per wave instruction)
+  constexpr int STEP = KPI * kUnroll;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t gq = (int64_t)blockIdx.x * kWaves + wave;
   if (gq >= (int64_t)a.B * a.H * a.S) return;
@@ -42,7 +42,6 @@ __global__ __launch_bounds__(64 * kWaves) void gather_attn_kernel(GatherArgs a) 
   const bf16* gV = (const bf16*)a.v + base + 8 * sub;
   const int32_t* sel = a.idx + gq * a.top_k;
   const int cnt = a.count[gq];
-  float* sc = sScore + wave * a.top_k;
 
   float q[8];
   {
@@ -50,70 +49,69 @@ __global__ __launch_bounds__(64 * kWaves) void gather_attn_kernel(GatherArgs a) 
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = (float)qv[e];
   }
-  float mx = kNegInf;
-  for (int t0 = 0; t0 < cnt; t0 += KPI * kUnroll) {
-    // indices first (a missing one reads key 0 and is discarded), then all rows, then the math
-    int kidx[kUnroll];
+  // key u of a step for this group: position t0 + u * KPI + grp of the list (a position
+  // past the count reads key 0 and is discarded)
+  int kid[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int t = u * KPI + grp;
+    kid[u] = t < cnt ? sel[t] : 0;
+  }
+  float m = kNegInf, l = 0.f;  // the group's running max (log2 units) and row sum
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int t0 = 0; t0 < cnt; t0 += STEP) {
+    bf16x8 kv[kUnroll], vv[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * KPI + grp;
-      kidx[u] = t < cnt ? sel[t] : 0;
+      kv[u] = *(const bf16x8*)(gK + (int64_t)kid[u] * a.ss);
+      vv[u] = *(const bf16x8*)(gV + (int64_t)kid[u] * a.ss);
     }
-    bf16x8 kv[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) kv[u] = *(const bf16x8*)(gK + (int64_t)kidx[u] * a.ss);
+    // the next step's indices, in flight with the rows
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * KPI + grp;
+      const int t = t0 + STEP + u * KPI + grp;
+      kid[u] = t < cnt ? sel[t] : 0;
+    }
+    float s[kUnroll];
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot = fmaf(q[e], (float)kv[u][e], dot);
 #pragma unroll
       for (int w = LPR / 2; w >= 1; w >>= 1) dot += __shfl_xor(dot, w);
-      const float s2 = dot * a.scale_log2;
-      if (t < cnt) {
-        if (sub == 0) sc[t] = s2;
-        mx = fmaxf(mx, s2);
-      }
+      s[u] = t0 + u * KPI + grp < cnt ? dot * a.scale_log2 : kNegInf;
+      mx = fmaxf(mx, s[u]);
     }
-  }
+    if (mx == kNegInf) continue;  // (the group has no key in this step, nor before)
+    const float alpha = __builtin_amdgcn_exp2f(m - mx);  // exp2(-inf) = 0 for an empty state
+    l *= alpha;
 #pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) mx = fmaxf(mx, __shfl_xor(mx, w));
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
-  for (int t0 = 0; t0 < cnt; t0 += KPI * kUnroll) {
-    int vidx[kUnroll];
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * KPI + grp;
-      vidx[u] = t < cnt ? sel[t] : 0;
-    }
-    bf16x8 vv[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) vv[u] = *(const bf16x8*)(gV + (int64_t)vidx[u] * a.ss);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * KPI + grp;
-      const float sv = sc[t < cnt ? t : 0];  // no read past the query's scores
-      const float p = t < cnt ? __builtin_amdgcn_exp2f(sv - mx) : 0.f;
-      if (sub == 0) lsum += p;
+      const float p = __builtin_amdgcn_exp2f(s[u] - mx);  // 0 for a discarded key
+      l += p;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = fmaf(p, (float)vv[u][e], acc[e]);
     }
+    m = mx;
   }
+  // merge the groups' states (lanes LPR apart hold the same head-dim slice)
 #pragma unroll
   for (int w = LPR; w < 64; w <<= 1) {
+    const float mo = __shfl_xor(m, w), lo = __shfl_xor(l, w);
+    const float mm = fmaxf(m, mo);
+    const float ref = mm == kNegInf ? 0.f : mm;
+    const float a0 = __builtin_amdgcn_exp2f(m - ref), a1 = __builtin_amdgcn_exp2f(mo - ref);
+    l = l * a0 + lo * a1;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], w);
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * a0 + __shfl_xor(acc[e], w) * a1;
+    m = mm;
   }
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) lsum += __shfl_xor(lsum, w);
   if (grp == 0) {
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
     bf16x8 ov;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ov[e] = (bf16)(acc[e] * inv);
@@ -127,11 +125,10 @@ hipError_t launch_gather_attn(const GatherArgs& a, hipStream_t stream) {
   if (a.top_k > kMaxTopK) return hipErrorInvalidValue;
   const int64_t rows = (int64_t)a.B * a.H * a.S;
   const unsigned grid = (unsigned)((rows + kWaves - 1) / kWaves);
-  const size_t lds = (size_t)kWaves * a.top_k * sizeof(float);
   if (a.D == 128)
-    hipLaunchKernelGGL((gather_attn_kernel<128>), dim3(grid), dim3(64 * kWaves), lds, stream, a);
+    hipLaunchKernelGGL((gather_attn_kernel<128>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
   else if (a.D == 64)
-    hipLaunchKernelGGL((gather_attn_kernel<64>), dim3(grid), dim3(64 * kWaves), lds, stream, a);
+    hipLaunchKernelGGL((gather_attn_kernel<64>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
