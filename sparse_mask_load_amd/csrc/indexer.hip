@@ -18,8 +18,10 @@
 //    above each row's threshold to the row's LDS buffer (kCap entries); the
 //    common case rejects a 16-score group with one max and one compare.  The
 //    threshold is first estimated from the mean and deviation of the row's
-//    first kFirstLook importances (a normal quantile, Abramowitz & Stegun
-//    26.2.23); a pass that collects fewer than top_k or more than kCap keys
+//    first importances, kFirstLook or a quarter of the block's largest
+//    candidate count if more (a normal quantile, Abramowitz & Stegun 26.2.23:
+//    the larger sample keeps the rows of long blocks inside the buffer's
+//    window, so that one counting pass suffices more often); a pass that collects fewer than top_k or more than kCap keys
 //    moves it (by the normal-model distance between the observed and the
 //    target count, then by bisection of the key space, which ends because one
 //    more unit of the threshold removes at most one key).  Finally
@@ -46,7 +48,7 @@ constexpr int kRank = 32;
 constexpr int kRows = 32;          // queries per workgroup
 constexpr int kWaves = 16;         // 4 per SIMD: the key stream is latency-bound
 constexpr int kCap = 768;          // candidate buffer entries per row
-constexpr int kFirstLook = 2048;   // keys of the threshold estimate
+constexpr int kFirstLook = 2048;   // keys of the threshold estimate (at least)
 constexpr int kPrefetch = 4;       // key blocks whose K' loads each wave keeps in flight
 constexpr int kModelSteps = 6;     // threshold corrections from the normal model before bisection
 constexpr int kMaxPasses = 80;     // kModelSteps + at most 64 bisections suffice
@@ -186,9 +188,9 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
   // Threshold estimate for rows with more candidates than the buffer holds.
   if (n_max > kCap) {
     float s1 = 0.f, s2 = 0.f, s0 = 0.f;
-    const int n_fl = min(n_max, kFirstLook);
+    const int n_fl = min(n_max, max(kFirstLook, n_max / 4));
     const int nfl_kb = (n_fl + 31) / 32;
-    const int my_n = i < a.S ? min(causal ? i + 1 : a.S, kFirstLook) : 0;
+    const int my_n = i < a.S ? min(causal ? i + 1 : a.S, n_fl) : 0;
     for (int kb = wave; kb < nfl_kb; kb += kWaves) {
       const f32x16 sc = tile_scores(load_kfrag(kp, kb, a.S, lane), qf, kb, a.S, i, causal, kb >= first_edge_kb, lane);
 #pragma unroll
