@@ -26,6 +26,25 @@ constexpr int kWaves = 4;
 constexpr int kMaxTopK = 2048;
 constexpr int kUnroll = 4;  // keys per lane group and step (their K and V rows in flight together)
 
+// x from another lane of the same 16-lane row (a DPP move; CTRL is the DPP control code)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum of x over each aligned group of N lanes (N = 8 or 16), in every lane of the group:
+// swaps within quads (lanes ^1, ^2), then the mirrored lane of the 8-lane half row (the
+// other quad), then, for 16, the mirrored lane of the row (the other half).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+  x += dpp_mov<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  if constexpr (N == 16) x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * kWaves) void gather_attn_kernel(GatherArgs a) {
   constexpr int LPR = D / 8;     // lanes per key row
@@ -79,8 +98,7 @@ __global__ __launch_bounds__(64 * kWaves) void gather_attn_kernel(GatherArgs a) 
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot = fmaf(q[e], (float)kv[u][e], dot);
-#pragma unroll
-      for (int w = LPR / 2; w >= 1; w >>= 1) dot += __shfl_xor(dot, w);
+      dot = group_sum<LPR>(dot);
       s[u] = t0 + u * KPI + grp < cnt ? dot * a.scale_log2 : kNegInf;
       mx = fmaxf(mx, s[u]);
     }
