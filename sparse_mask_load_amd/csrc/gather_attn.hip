@@ -21,6 +21,7 @@ namespace {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kWaves = 4;
 constexpr int kMaxTopK = 2048;
@@ -45,12 +46,15 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int D>
+// OFF32: a head's rows span less than 2^31 bytes and fewer than 2^23 rows of stride below
+// 2^22 elements, so a gathered row's byte offset from the head's base is one 24-bit multiply
+// and an add, and the load takes the head's base as its uniform (scalar) address.
+template <int D, bool OFF32>
 __global__ __launch_bounds__(64 * kWaves) void gather_attn_kernel(GatherArgs a) {
   constexpr int LPR = D / 8;     // lanes per key row
   constexpr int KPI = 64 / LPR;  // lane groups (keys per wave instruction)
   constexpr int STEP = KPI * kUnroll;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gq = (int64_t)blockIdx.x * kWaves + wave;
   if (gq >= (int64_t)a.B * a.H * a.S) return;
   const int bh = (int)(gq / a.S), i = (int)(gq % a.S);
@@ -59,22 +63,21 @@ __global__ __launch_bounds__(64 * kWaves) void gather_attn_kernel(GatherArgs a) 
   const int grp = lane / LPR, sub = lane % LPR;
   const bf16* gK = (const bf16*)a.k + base + 8 * sub;
   const bf16* gV = (const bf16*)a.v + base + 8 * sub;
+  const char* const kbase = (const char*)((const bf16*)a.k + base);  // uniform
+  const char* const vbase = (const char*)((const bf16*)a.v + base);
+  const int row_bytes = (int)a.ss * 2;
   const int32_t* sel = a.idx + gq * a.top_k;
   const int cnt = a.count[gq];
 
-  float q[8];
-  {
-    const bf16x8 qv = *(const bf16x8*)((const bf16*)a.q + base + (int64_t)i * a.ss + 8 * sub);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = (float)qv[e];
-  }
+  const bf16x8 qv = *(const bf16x8*)((const bf16*)a.q + base + (int64_t)i * a.ss + 8 * sub);
   // key u of a step for this group: position t0 + u * KPI + grp of the list (a position
   // past the count reads key 0 and is discarded)
   int kid[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int t = u * KPI + grp;
-    kid[u] = t < cnt ? sel[t] : 0;
+    const int ld = sel[min(t, a.top_k - 1)];  // always a valid slot of the list
+    kid[u] = t < cnt ? ld : 0;
   }
   float m = kNegInf, l = 0.f;  // the group's running max (log2 units) and row sum
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -82,22 +85,31 @@ __global__ __launch_bounds__(64 * kWaves) void gather_attn_kernel(GatherArgs a) 
     bf16x8 kv[kUnroll], vv[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      kv[u] = *(const bf16x8*)(gK + (int64_t)kid[u] * a.ss);
-      vv[u] = *(const bf16x8*)(gV + (int64_t)kid[u] * a.ss);
+      if constexpr (OFF32) {
+        const uint32_t off = (uint32_t)__mul24(kid[u], row_bytes) + 16u * sub;
+        kv[u] = *(const bf16x8*)(kbase + off);
+        vv[u] = *(const bf16x8*)(vbase + off);
+      } else {
+        kv[u] = *(const bf16x8*)(gK + (int64_t)kid[u] * a.ss);
+        vv[u] = *(const bf16x8*)(gV + (int64_t)kid[u] * a.ss);
+      }
     }
     // the next step's indices, in flight with the rows
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = t0 + STEP + u * KPI + grp;
-      kid[u] = t < cnt ? sel[t] : 0;
+      const int ld = sel[min(t, a.top_k - 1)];
+      kid[u] = t < cnt ? ld : 0;
     }
     float s[kUnroll];
     float mx = m;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+      // bf16 pair products summed in fp32 (exact products, as the fma form)
       float dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dot = fmaf(q[e], (float)kv[u][e], dot);
+      for (int e = 0; e < 8; e += 2)
+        dot = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{qv[e], qv[e + 1]}, bf16x2{kv[u][e], kv[u][e + 1]}, dot, false);
       dot = group_sum<LPR>(dot);
       s[u] = t0 + u * KPI + grp < cnt ? dot * a.scale_log2 : kNegInf;
       mx = fmaxf(mx, s[u]);
@@ -109,10 +121,17 @@ __global__ __launch_bounds__(64 * kWaves) void gather_attn_kernel(GatherArgs a) 
     for (int e = 0; e < 8; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const float p = __builtin_amdgcn_exp2f(s[u] - mx);  // 0 for a discarded key
-      l += p;
+      // the weight in bf16 (0 for a discarded key); the row sum adds the same rounded value,
+      // and each V element takes it with one bf16 dot product against (p, 0) or (0, p)
+      const bf16 pb = (bf16)__builtin_amdgcn_exp2f(s[u] - mx);
+      l += (float)pb;
+      const bf16x2 p_lo = {pb, (bf16)0.f}, p_hi = {(bf16)0.f, pb};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(p, (float)vv[u][e], acc[e]);
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 v2 = {vv[u][e], vv[u][e + 1]};
+        acc[e] = __builtin_amdgcn_fdot2_f32_bf16(v2, p_lo, acc[e], false);
+        acc[e + 1] = __builtin_amdgcn_fdot2_f32_bf16(v2, p_hi, acc[e + 1], false);
+      }
     }
     m = mx;
   }
@@ -143,10 +162,16 @@ hipError_t launch_gather_attn(const GatherArgs& a, hipStream_t stream) {
   if (a.top_k > kMaxTopK) return hipErrorInvalidValue;
   const int64_t rows = (int64_t)a.B * a.H * a.S;
   const unsigned grid = (unsigned)((rows + kWaves - 1) / kWaves);
-  if (a.D == 128)
-    hipLaunchKernelGGL((gather_attn_kernel<128>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  const int64_t extent = ((int64_t)(a.S - 1) * a.ss + a.D) * 2;
+  const bool off32 = extent < ((int64_t)1 << 31) && a.S < (1 << 23) && a.ss < (1 << 21);
+  if (a.D == 128 && off32)
+    hipLaunchKernelGGL((gather_attn_kernel<128, true>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  else if (a.D == 128)
+    hipLaunchKernelGGL((gather_attn_kernel<128, false>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  else if (a.D == 64 && off32)
+    hipLaunchKernelGGL((gather_attn_kernel<64, true>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
   else if (a.D == 64)
-    hipLaunchKernelGGL((gather_attn_kernel<64>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((gather_attn_kernel<64, false>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
