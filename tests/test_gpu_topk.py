@@ -113,6 +113,25 @@ def test_topk_d64_strided_layout():
     _attention_checks(w, q, k, v, plan, idx, cnt, G.sample_rows(w, 32, seed=7), w.top_k, True)
 
 
+def test_topk_wide_row_stride():
+    # rows 2^21 elements apart (a head spans more than 2 GiB of address range): the gather takes
+    # its 64-bit row addresses instead of 32-bit offsets from the head's base
+    w = W.make_custom(1, 1, 100, 128, pattern="topk", top_k=32, causal=True, seed=8)
+    ss = 1 << 21
+
+    def wide(x):
+        buf = torch.empty((w.S - 1) * ss + w.D, dtype=torch.bfloat16, device="cuda")
+        view = buf.as_strided((1, 1, w.S, w.D), (w.S * ss, w.S * ss, ss, 1))
+        view.copy_(torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.bfloat16))
+        return view
+    q, k, v = wide(w.q), wide(w.k), wide(w.v)
+    plan = _plan_topk(w, q, k)
+    idx, cnt = _copy_selection(plan, w, w.top_k)
+    rows = [(0, 0, i) for i in range(w.S)]
+    _check_rows(w, idx, cnt, rows, w.top_k, True)
+    _attention_checks(w, q, k, v, plan, idx, cnt, rows, w.top_k, True)
+
+
 def test_topk_all_tied_takes_lowest_indices():
     """Zero indexer weights: every importance is 0, so each row keeps its lowest indices."""
     w = W.make_custom(1, 2, 1100, 128, pattern="topk", top_k=100, causal=True, seed=8)
