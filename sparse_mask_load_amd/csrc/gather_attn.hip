@@ -9,9 +9,12 @@
 // forms their scores (in-group reduction over the D/8 lanes) and folds them into
 // its online-softmax state (running max, row sum and weighted V sum, rescaled
 // when the max grows); the groups' states are merged at the end by the same
-// rule.  Bound by the gather: every selected key costs one K row and one V row,
-// and a row's address is known only once its index is loaded, so the indices of
-// the next kUnroll keys are loaded while the current rows are in flight.
+// rule.  Scores and weighted V sums are bf16 dot products with fp32 sums (the
+// weights rounded to bf16, the value the row sum also adds), so the bf16 rows
+// need no conversion.  Bound by the gather: every selected key costs one K row
+// and one V row, and a row's address is known only once its index is loaded, so
+// the indices of the next kUnroll keys are loaded while the current rows are in
+// flight.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
