@@ -26,8 +26,9 @@
 //    target count, then by bisection of the key space, which ends because one
 //    more unit of the threshold removes at most one key).  Finally
 //    a wave per row picks the exact top_k from its buffer: a radix select of
-//    the top_k-th largest importance bits, 8 bits per round (a histogram of the
-//    next byte among the entries that match the bytes fixed so far), then, for
+//    the top_k-th largest importance bits, 8 bits per round from the highest bit
+//    in which the entries differ (a histogram of the next byte among the entries
+//    that match the bits fixed so far), then, for
 //    ties, bisection on the key index.  The order of the indices within a
 //    row's list is unspecified.
 #include <hip/hip_runtime.h>
@@ -360,15 +361,36 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
     uint32_t t_ord = 0;   // selected: ord > t_ord, plus ord == t_ord with index <= t_j
     int t_j = -1;
     if (n > need) {
-      // Radix select of the need-th largest ord, 8 bits at a time from the top: a histogram
+      // Radix select of the need-th largest ord, 8 bits at a time from the first bit in which
+      // the entries differ (the buffered keys are the row's largest, so their leading bits
+      // mostly agree, and a histogram of a shared digit would also put every lane's atomic
+      // add on one bin): a histogram
       // of the next digit among the entries that match the digits fixed so far, then the
       // digit where the count from the top reaches the keys still needed.  The histogram
       // lives in this row's score buffer, whose entries are now in registers (a wave's LDS
       // accesses complete in order, so the reads above precede these writes).
       uint32_t* hist = (uint32_t*)sh.score[row];
-      uint32_t prefix = 0, pmask = 0;
+      // the entries' common leading bits need no round: the first digit window ends at the
+      // highest bit in which they differ
+      uint32_t o_lo = 0xFFFFFFFFu, o_hi = 0u;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (e * 64 + lane < n) {
+          o_lo = min(o_lo, o[e]);
+          o_hi = max(o_hi, o[e]);
+        }
+#pragma unroll
+      for (int w = 32; w >= 1; w >>= 1) {
+        o_lo = min(o_lo, (uint32_t)__shfl_xor((int)o_lo, w));
+        o_hi = max(o_hi, (uint32_t)__shfl_xor((int)o_hi, w));
+      }
+      const uint32_t diff = o_lo ^ o_hi;  // n > need >= 1, so both are entries
+      const int top = diff ? 31 - __builtin_clz(diff) : 0;
+      const int shift0 = max(top - 7, 0);
+      uint32_t pmask = shift0 + 8 >= 32 ? 0u : ~0u << (shift0 + 8);
+      uint32_t prefix = o_hi & pmask;
       int remaining = need;  // keys still to take among the entries matching prefix
-      for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int shift = shift0; ; shift = max(shift - 8, 0)) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) hist[q * 64 + lane] = 0u;
 #pragma unroll
@@ -404,6 +426,7 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
         prefix |= (uint32_t)digit << shift;
         pmask |= 255u << shift;
         remaining -= (int)gt_d;
+        if (shift == 0) break;
       }
       const uint32_t hi = prefix;  // the need-th largest ord
       const int c_hi = need - remaining;  // entries strictly above it
