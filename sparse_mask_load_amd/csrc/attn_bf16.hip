@@ -128,6 +128,16 @@ __device__ __forceinline__ int opaque(int x) {
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier without the memory fence of __syncthreads, whose release part waits for
+// every load and store the wave has in flight: for a barrier that only orders LDS reads that
+// are complete (consumed by the instructions that needed them) before tile loads that
+// overwrite them.  The compiler moves no memory access across it.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Where the rows of one K/V tile live in global memory: row r of the tile is
 // element base + r * row_stride; rows at or beyond `rows` repeat the last
 // valid row (the partial last block of a ragged sequence).
@@ -1374,9 +1384,15 @@ void attn_bf16_pair_kernel(FwdArgs a) {
       // wait for this wave's loads, then the barrier makes every wave's visible (and frees the
       // V buffer of the previous tile).  The second half reads only data that the first
       // half's wait covered (K of the next tile, V of this one); its barrier just frees this
-      // tile's K buffer, so the loads and stores issued meanwhile keep draining.
-      if constexpr (H == 0) wait_vm();
-      __syncthreads();
+      // tile's K buffer, whose reads the first half's MFMAs have consumed, so it waits for no
+      // memory operation and the loads and partial stores issued meanwhile keep draining
+      // (waiting for the stores of a chunk flush here took 1.6% of the partial forward).
+      if constexpr (H == 0) {
+        wait_vm();
+        __syncthreads();
+      } else {
+        barrier_only();
+      }
       if constexpr (H == 0) {
         bool fresh = t == 0;  // block 0 of this tile opens an accumulation
         if (!full && cur_chunk < chunk_of(desc)) {
