@@ -192,15 +192,39 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
     const int n_fl = min(n_max, max(kFirstLook, n_max / 4));
     const int nfl_kb = (n_fl + 31) / 32;
     const int my_n = i < a.S ? min(causal ? i + 1 : a.S, n_fl) : 0;
-    for (int kb = wave; kb < nfl_kb; kb += kWaves) {
-      const f32x16 sc = tile_scores(load_kfrag(kp, kb, a.S, lane), qf, kb, a.S, i, causal, kb >= first_edge_kb, lane);
+    // key blocks below this bound lie inside every row's sample (no per-key test)
+    const int n_full = i0 + kRows > a.S ? 0 : min(causal ? i0 + 1 : a.S, n_fl);
+    // the same ring of K' loads as the counting pass below
+    KFrag ring[kPrefetch];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        if (j < my_n) {
-          s0 += 1.f;
-          s1 += sc[r];
-          s2 = fmaf(sc[r], sc[r], s2);
+    for (int p = 0; p < kPrefetch; ++p) {
+      ring[p] = load_kfrag(kp, min(wave + p * kWaves, nfl_kb - 1), a.S, lane);
+      __builtin_amdgcn_sched_barrier(0);  // issue order = use order
+    }
+    for (int kb0 = wave; kb0 < nfl_kb; kb0 += kPrefetch * kWaves) {
+#pragma unroll
+      for (int p = 0; p < kPrefetch; ++p) {
+        const int kb = kb0 + p * kWaves;
+        const f32x16 sc = tile_scores(ring[p], qf, kb, a.S, i, causal, kb >= first_edge_kb, lane);
+        ring[p] = load_kfrag(kp, min(kb + kPrefetch * kWaves, nfl_kb - 1), a.S, lane);
+        if (kb >= nfl_kb) continue;
+        if (kb * 32 + 32 <= n_full) {
+          s0 += 16.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s1 += sc[r];
+            s2 = fmaf(sc[r], sc[r], s2);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            if (j < my_n) {
+              s0 += 1.f;
+              s1 += sc[r];
+              s2 = fmaf(sc[r], sc[r], s2);
+            }
+          }
         }
       }
     }
@@ -244,8 +268,47 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
     const uint64_t K = live ? c.K : ~0ull;
     const uint32_t k_hi = (uint32_t)(K >> 32);
     const float t_filter = !live ? __builtin_huge_valf() : (k_hi == 0 ? kNegInf : float_of_ord(k_hi));
-    auto process = [&](const KFrag& cur, int kb) {
-      const f32x16 sc = tile_scores(cur, qf, kb, a.S, i, causal, kb >= first_edge_kb, lane);
+    // A threshold whose index part is all ones (every threshold but those of the bisection
+    // fallback) keeps exactly the importances strictly above t_filter: then one compare per
+    // key decides, with no tie test.  Wave-uniform.
+    const bool plain = __ballot(!(K == 0 || (uint32_t)K == 0xFFFFFFFFu)) == 0;
+    auto process_plain = [&](const f32x16& sc, int kb) {
+      bool sel[16];
+      int c = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sel[r] = sc[r] > t_filter;
+        c += sel[r] ? 1 : 0;
+      }
+      if (__ballot(c > 0) == 0) return;
+      int pos = 0;
+      if (c > 0) pos = atomicAdd(&sh.cnt[l32], c);  // one claim per lane
+      const int kbase = kb * 32 + 4 * h2;
+      if (__builtin_expect(__ballot(pos + c > kCap) == 0, 1)) {
+        // the common case: every claimed slot is inside the buffer; the stores are unrolled
+        // over the 16 scores, each under its compare's lane mask (no dynamic register index)
+        float* ps = &sh.score[l32][pos];
+        uint16_t* pk = &sh.key[l32][pos];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (sel[r]) {
+            *ps++ = sc[r];
+            *pk++ = (uint16_t)(kbase + 8 * (r >> 2) + (r & 3));
+          }
+      } else {
+        // the buffer overflows (the pass is repeated): keep the slots that fit
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (sel[r]) {
+            if (pos < kCap) {
+              sh.score[l32][pos] = sc[r];
+              sh.key[l32][pos] = (uint16_t)(kbase + 8 * (r >> 2) + (r & 3));
+            }
+            ++pos;
+          }
+      }
+    };
+    auto process = [&](const f32x16& sc, int kb) {
       float m = sc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) m = fmaxf(m, sc[r]);
@@ -286,19 +349,29 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
         }
       }
     };
-    // key blocks wave, wave + kWaves, ...: each wave keeps kPrefetch blocks' K' loads in flight
+    // key blocks wave, wave + kWaves, ...: each wave keeps kPrefetch blocks' K' loads in
+    // flight.  A slot is refilled once its MFMAs have read it, into the same registers, and
+    // every round issues the same loads (past the last block they repeat it, a cache hit), so
+    // that each block waits only for its own loads (conditional loads, or a refill while the
+    // old operand is still live, made the compiler wait for all of them at every round's end).
     KFrag ring[kPrefetch];
 #pragma unroll
-    for (int p = 0; p < kPrefetch; ++p)
-      if (wave + p * kWaves < nkb) ring[p] = load_kfrag(kp, wave + p * kWaves, a.S, lane);
+    for (int p = 0; p < kPrefetch; ++p) {
+      ring[p] = load_kfrag(kp, min(wave + p * kWaves, nkb - 1), a.S, lane);
+      // issue order = use order (the first slot's wait then counts only the later slots)
+      __builtin_amdgcn_sched_barrier(0);
+    }
     for (int kb0 = wave; kb0 < nkb; kb0 += kPrefetch * kWaves) {
 #pragma unroll
       for (int p = 0; p < kPrefetch; ++p) {
         const int kb = kb0 + p * kWaves;
+        const f32x16 sc = tile_scores(ring[p], qf, kb, a.S, i, causal, kb >= first_edge_kb, lane);
+        ring[p] = load_kfrag(kp, min(kb + kPrefetch * kWaves, nkb - 1), a.S, lane);
         if (kb < nkb) {
-          const KFrag cur = ring[p];
-          if (kb + kPrefetch * kWaves < nkb) ring[p] = load_kfrag(kp, kb + kPrefetch * kWaves, a.S, lane);
-          process(cur, kb);
+          if (plain)
+            process_plain(sc, kb);
+          else
+            process(sc, kb);
         }
       }
     }
