@@ -463,6 +463,7 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
       uint32_t pmask = shift0 + 8 >= 32 ? 0u : ~0u << (shift0 + 8);
       uint32_t prefix = o_hi & pmask;
       int remaining = need;  // keys still to take among the entries matching prefix
+      bool whole_bin = false;  // every entry matching prefix is taken: no lower digit decides
       for (int shift = shift0; ; shift = max(shift - 8, 0)) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) hist[q * 64 + lane] = 0u;
@@ -481,7 +482,7 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
         above -= mine;  // entries with a digit above this lane's four
         // find the digit d with count(> d) < remaining <= count(>= d); exactly one lane has it
         int found = -1;
-        uint32_t gt_found = 0;
+        uint32_t gt_found = 0, n_found = 0;
         uint32_t ge = above;
 #pragma unroll
         for (int k = 3; k >= 0; --k) {
@@ -490,22 +491,32 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
           if (found < 0 && gt < (uint32_t)remaining && ge >= (uint32_t)remaining) {
             found = 4 * lane + k;
             gt_found = gt;
+            n_found = cnt[k];
           }
         }
         const uint64_t who = __ballot(found >= 0);
         const int src = __builtin_ctzll(who);
         const int digit = __shfl(found, src);
         const uint32_t gt_d = (uint32_t)__shfl((int)gt_found, src);
+        const uint32_t n_d = (uint32_t)__shfl((int)n_found, src);
         prefix |= (uint32_t)digit << shift;
         pmask |= 255u << shift;
         remaining -= (int)gt_d;
+        // the digit's whole bin is taken (its smallest entry is the need-th largest): the
+        // selection is every entry at or above prefix, whatever the lower bits
+        if (n_d == (uint32_t)remaining) {
+          whole_bin = true;
+          break;
+        }
         if (shift == 0) break;
       }
-      const uint32_t hi = prefix;  // the need-th largest ord
+      const uint32_t hi = prefix;  // the need-th largest ord, or with whole_bin a lower bound of the taken bin
       const int c_hi = need - remaining;  // entries strictly above it
       t_ord = hi;
       const int ties_needed = need - c_hi;
-      if (count_if([&](uint32_t ov, int) { return ov == hi; }) == ties_needed) {
+      if (whole_bin) {
+        t_j = 0xFFFF;  // ord > hi, or ord == hi with any index
+      } else if (count_if([&](uint32_t ov, int) { return ov == hi; }) == ties_needed) {
         t_j = 0xFFFF;  // every tied key is taken (the usual case: the tie is the need-th key alone)
       } else {
         // smallest index bound taking ties_needed of the tied keys (lowest indices first)
