@@ -35,6 +35,8 @@
 
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "internal.h"
 #include "kernel_common.h"
 
@@ -76,24 +78,57 @@ __device__ float normal_upper_quantile(float p) {
 }
 
 // ---------------------------------------------------------------------------
-// Projections: Xp[row][r] = bf16(sum_d X[row][d] * W[d][r]); 8 rows per block,
-// 32 threads per row.
+// Projections: Xp[row][r] = bf16(sum_d X[row][d] * W[d][r]), the sum an fp32 fma chain in
+// index order.  Thread (g, r) of a 256-thread block keeps column r of W in registers (as
+// fp32) and takes rows g, g + 8, ... of each chunk of kProjRows rows, which the block first
+// stages in LDS as fp32 (one conversion per element; the 32 lanes of a group then read the
+// same row, a broadcast).  The block strides over the chunks, so W is read once per block.
+constexpr int kProjRows = 64;
+constexpr int kProjBlocks = 1024;
+template <int D>
 __global__ __launch_bounds__(256) void proj_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W,
-                                                   bf16* __restrict__ Xp, int B, int H, int S, int D, int64_t sb,
+                                                   bf16* __restrict__ Xp, int B, int H, int S, int64_t sb,
                                                    int64_t sh, int64_t ss) {
-  const int64_t row = (int64_t)blockIdx.x * 8 + threadIdx.x / 32;
-  const int r = threadIdx.x & 31;
-  if (row >= (int64_t)B * H * S) return;
-  const int i = (int)(row % S);
-  const int bh = (int)(row / S);
-  const bf16* x = X + (int64_t)(bh / H) * sb + (int64_t)(bh % H) * sh + (int64_t)i * ss;
-  float acc = 0.f;
-  for (int d = 0; d < D; d += 8) {
-    const bf16x8 xv = *(const bf16x8*)(x + d);
+  constexpr int LD = D + 4;  // row stride in floats: rows of one wave's two groups fall on other banks
+  __shared__ __attribute__((aligned(16))) float xs[kProjRows * LD];
+  const int r = threadIdx.x & 31, g = threadIdx.x >> 5;
+  float w[D];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)xv[e], (float)W[(d + e) * kRank + r], acc);
+  for (int d = 0; d < D; ++d) w[d] = (float)W[d * kRank + r];
+  const int64_t rows = (int64_t)B * H * S;
+  const int64_t n_chunks = (rows + kProjRows - 1) / kProjRows;
+  for (int64_t chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {
+    const int64_t row0 = chunk * kProjRows;
+    __syncthreads();  // the previous chunk's rows are consumed
+    for (int c = threadIdx.x; c < kProjRows * (D / 8); c += 256) {
+      const int rr = c / (D / 8), d8 = (c % (D / 8)) * 8;
+      const int64_t row = row0 + rr;
+      if (row < rows) {
+        const int i = (int)(row % S);
+        const int bh = (int)(row / S);
+        const bf16x8 v = *(const bf16x8*)(X + (int64_t)(bh / H) * sb + (int64_t)(bh % H) * sh + (int64_t)i * ss + d8);
+        float* dst = xs + rr * LD + d8;
+        *(float4*)dst = float4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+        *(float4*)(dst + 4) = float4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+      }
+    }
+    __syncthreads();
+    for (int rr = g; rr < kProjRows; rr += 8) {
+      const int64_t row = row0 + rr;
+      if (row >= rows) break;
+      const float* x = xs + rr * LD;
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; d += 4) {
+        const float4 xv = *(const float4*)(x + d);
+        acc = fmaf(xv.x, w[d], acc);
+        acc = fmaf(xv.y, w[d + 1], acc);
+        acc = fmaf(xv.z, w[d + 2], acc);
+        acc = fmaf(xv.w, w[d + 3], acc);
+      }
+      Xp[row * kRank + r] = (bf16)acc;
+    }
   }
-  Xp[row * kRank + r] = (bf16)acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -548,14 +583,20 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
-  if (a.rank != kRank || a.top_k < 1 || a.top_k > kIndexerMaxTopK || a.S > 65536 || a.D % 8 != 0)
+  if (a.rank != kRank || a.top_k < 1 || a.top_k > kIndexerMaxTopK || a.S > 65536 || (a.D != 64 && a.D != 128))
     return hipErrorInvalidValue;
   const int64_t rows = (int64_t)a.B * a.H * a.S;
-  const dim3 pg((unsigned)((rows + 7) / 8));
-  hipLaunchKernelGGL(proj_kernel, pg, dim3(256), 0, stream, (const bf16*)a.q, (const bf16*)a.wq, a.qp, a.B, a.H, a.S,
-                     a.D, a.sb, a.sh, a.ss);
-  hipLaunchKernelGGL(proj_kernel, pg, dim3(256), 0, stream, (const bf16*)a.k, (const bf16*)a.wk, a.kp, a.B, a.H, a.S,
-                     a.D, a.sb, a.sh, a.ss);
+  const dim3 pg((unsigned)std::min<int64_t>((rows + kProjRows - 1) / kProjRows, kProjBlocks));
+  auto proj = [&](const void* x, const void* w, bf16* xp) {
+    if (a.D == 128)
+      hipLaunchKernelGGL(proj_kernel<128>, pg, dim3(256), 0, stream, (const bf16*)x, (const bf16*)w, xp, a.B, a.H,
+                         a.S, a.sb, a.sh, a.ss);
+    else
+      hipLaunchKernelGGL(proj_kernel<64>, pg, dim3(256), 0, stream, (const bf16*)x, (const bf16*)w, xp, a.B, a.H,
+                         a.S, a.sb, a.sh, a.ss);
+  };
+  proj(a.q, a.wq, a.qp);
+  proj(a.k, a.wk, a.kp);
   const int blocks = a.B * a.H * ((a.S + kRows - 1) / kRows);
   hipLaunchKernelGGL(select_kernel, dim3(blocks), dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
