@@ -97,22 +97,40 @@ __global__ __launch_bounds__(256) void proj_kernel(const bf16* __restrict__ X, c
   for (int d = 0; d < D; ++d) w[d] = (float)W[d * kRank + r];
   const int64_t rows = (int64_t)B * H * S;
   const int64_t n_chunks = (rows + kProjRows - 1) / kProjRows;
-  for (int64_t chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {
-    const int64_t row0 = chunk * kProjRows;
-    __syncthreads();  // the previous chunk's rows are consumed
-    for (int c = threadIdx.x; c < kProjRows * (D / 8); c += 256) {
-      const int rr = c / (D / 8), d8 = (c % (D / 8)) * 8;
-      const int64_t row = row0 + rr;
+  constexpr int NL = kProjRows * (D / 8) / 256;  // 16-byte row pieces per thread and chunk
+  static_assert(NL * 256 == kProjRows * (D / 8), "a chunk's pieces cover the block evenly");
+  // piece c of a chunk: row c / (D/8), elements (c % (D/8)) * 8 .. +7; a piece past the last
+  // row is zero (and never stored)
+  auto load_chunk = [&](int64_t chunk, bf16x8 (&v)[NL]) {
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int c = threadIdx.x + 256 * k;
+      const int64_t row = chunk * kProjRows + c / (D / 8);
+      v[k] = bf16x8{};
       if (row < rows) {
         const int i = (int)(row % S);
         const int bh = (int)(row / S);
-        const bf16x8 v = *(const bf16x8*)(X + (int64_t)(bh / H) * sb + (int64_t)(bh % H) * sh + (int64_t)i * ss + d8);
-        float* dst = xs + rr * LD + d8;
-        *(float4*)dst = float4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-        *(float4*)(dst + 4) = float4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+        v[k] = *(const bf16x8*)(X + (int64_t)(bh / H) * sb + (int64_t)(bh % H) * sh + (int64_t)i * ss +
+                                (c % (D / 8)) * 8);
       }
     }
+  };
+  // the next chunk's rows are loaded into registers while the current one is computed
+  bf16x8 nxt[NL];
+  if (blockIdx.x < n_chunks) load_chunk(blockIdx.x, nxt);
+  for (int64_t chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {
+    const int64_t row0 = chunk * kProjRows;
+    __syncthreads();  // the previous chunk's rows are consumed
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int c = threadIdx.x + 256 * k;
+      float* dst = xs + (c / (D / 8)) * LD + (c % (D / 8)) * 8;
+      const bf16x8 v = nxt[k];
+      *(float4*)dst = float4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+      *(float4*)(dst + 4) = float4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+    }
     __syncthreads();
+    if (chunk + gridDim.x < n_chunks) load_chunk(chunk + gridDim.x, nxt);
     for (int rr = g; rr < kProjRows; rr += 8) {
       const int64_t row = row0 + rr;
       if (row >= rows) break;
