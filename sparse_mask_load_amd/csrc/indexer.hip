@@ -15,22 +15,23 @@
 //    map of fp32 onto uint32, so "larger key" means "higher importance, then
 //    lower index" and exactly top_k keys lie above the right threshold.  A
 //    counting pass streams all candidate keys of the 32 rows and appends those
-//    above each row's threshold to the row's LDS buffer (kCap entries); the
-//    common case rejects a 16-score group with one max and one compare.  The
-//    threshold is first estimated from the mean and deviation of the row's
-//    first importances, kFirstLook or a quarter of the block's largest
-//    candidate count if more (a normal quantile, Abramowitz & Stegun 26.2.23:
-//    the larger sample keeps the rows of long blocks inside the buffer's
-//    window, so that one counting pass suffices more often); a pass that collects fewer than top_k or more than kCap keys
-//    moves it (by the normal-model distance between the observed and the
-//    target count, then by bisection of the key space, which ends because one
-//    more unit of the threshold removes at most one key).  Finally
-//    a wave per row picks the exact top_k from its buffer: a radix select of
-//    the top_k-th largest importance bits, 8 bits per round from the highest bit
-//    in which the entries differ (a histogram of the next byte among the entries
-//    that match the bits fixed so far), then, for
-//    ties, bisection on the key index.  The order of the indices within a
-//    row's list is unspecified.
+//    above each row's threshold to the row's LDS buffer (kCap entries); while
+//    the threshold's index part is all ones, a plain compare of the importance
+//    with the threshold's float decides each key.  The threshold is first
+//    estimated from the mean and deviation of the row's first importances,
+//    kFirstLook or a quarter of the block's largest candidate count if more (a
+//    normal quantile, Abramowitz & Stegun 26.2.23: the larger sample keeps the
+//    rows of long blocks inside the buffer's window, so that one counting pass
+//    suffices more often); a pass that collects fewer than top_k or more than
+//    kCap keys moves it (by the normal-model distance between the observed and
+//    the target count, then by bisection of the key space, which ends because
+//    one more unit of the threshold removes at most one key).  Finally a wave
+//    per row picks the exact top_k from its buffer: a radix select of the
+//    top_k-th largest importance bits, 8 bits per round from the highest bit in
+//    which the entries differ (a histogram of the next byte among the entries
+//    that match the bits fixed so far), stopping once the boundary digit's whole
+//    bin is taken, then, for ties, bisection on the key index.  The order of
+//    the indices within a row's list is unspecified.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
