@@ -54,6 +54,7 @@ struct sa_plan {
   int32_t* d_count = nullptr;        // [B][H][S]
   __bf16* d_qp = nullptr;            // [B][H][S][rank]
   __bf16* d_kp = nullptr;
+  float* d_mom = nullptr;            // [B][H][S/128 + 1][rank + rank^2]
   // recorded on the plan's stream once its device arrays are complete; every forward call
   // makes its own stream wait for it, so a plan may be built on a side stream
   hipEvent_t ready = nullptr;
@@ -420,10 +421,13 @@ sa_status plan_topk(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
     return fail(SA_ERR_UNSUPPORTED, "indexer top_k %d above %d", P->top_k, sa::kIndexerMaxTopK);
   if (pr.S > 65536) return fail(SA_ERR_UNSUPPORTED, "indexer sequence length %d above 65536", pr.S);
   P->rank = sp->rank;
-  if ((st = dalloc(P, &P->d_qp, rows * P->rank, stream)) || (st = dalloc(P, &P->d_kp, rows * P->rank, stream))) return st;
+  const size_t mom = (size_t)pr.B * pr.H * ((size_t)(pr.S + sa::kMomGroup - 1) / sa::kMomGroup + 1) * sa::kMomEntry;
+  if ((st = dalloc(P, &P->d_qp, rows * P->rank, stream)) || (st = dalloc(P, &P->d_kp, rows * P->rank, stream)) ||
+      (st = dalloc(P, &P->d_mom, mom, stream)))
+    return st;
   sa::IndexerArgs a{};
   a.q = sp->q; a.k = sp->k; a.wq = sp->wq; a.wk = sp->wk;
-  a.qp = P->d_qp; a.kp = P->d_kp; a.idx = P->d_idx; a.count = P->d_count;
+  a.qp = P->d_qp; a.kp = P->d_kp; a.mom = P->d_mom; a.idx = P->d_idx; a.count = P->d_count;
   a.B = pr.B; a.H = pr.H; a.S = pr.S; a.D = pr.D; a.rank = P->rank; a.top_k = P->top_k; a.causal = P->causal;
   a.sb = pr.sb; a.sh = pr.sh; a.ss = pr.ss;
   a.n_xcd = P->n_xcd;

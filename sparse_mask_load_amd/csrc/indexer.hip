@@ -18,12 +18,11 @@
 //    above each row's threshold to the row's LDS buffer (kCap entries); while
 //    the threshold's index part is all ones, a plain compare of the importance
 //    with the threshold's float decides each key.  The threshold is first
-//    estimated from the mean and deviation of the row's first importances,
-//    kFirstLook or a quarter of the block's largest candidate count if more (a
-//    normal quantile, Abramowitz & Stegun 26.2.23: the larger sample keeps the
-//    rows of long blocks inside the buffer's window, so that one counting pass
-//    suffices more often); a pass that collects fewer than top_k or more than
-//    kCap keys moves it (by the normal-model distance between the observed and
+//    estimated as a normal quantile (Abramowitz & Stegun 26.2.23) from the mean
+//    and deviation of the row's importances over the block's key prefix, which
+//    come from prefix sums of K' and K' K'^T in groups of kMomGroup keys
+//    (moments_group_kernel, moments_scan_kernel), with no pass over the keys;
+//    a pass that collects fewer than top_k or more than kCap keys moves it (by the normal-model distance between the observed and
 //    the target count, then by bisection of the key space, which ends because
 //    one more unit of the threshold removes at most one key).  Finally a wave
 //    per row picks the exact top_k from its buffer: a radix select of the
@@ -52,7 +51,6 @@ constexpr int kRank = 32;
 constexpr int kRows = 32;          // queries per workgroup
 constexpr int kWaves = 16;         // 4 per SIMD: the key stream is latency-bound
 constexpr int kCap = 768;          // candidate buffer entries per row
-constexpr int kFirstLook = 2048;   // keys of the threshold estimate (at least)
 constexpr int kPrefetch = 4;       // key blocks whose K' loads each wave keeps in flight
 constexpr int kModelSteps = 6;     // threshold corrections from the normal model before bisection
 constexpr int kMaxPasses = 80;     // kModelSteps + at most 64 bisections suffice
@@ -162,7 +160,6 @@ struct SelShared {
   uint16_t key[kRows][kCap];
   int cnt[kRows];
   RowCtl ctl[kRows];
-  float red[kWaves][kRows][3];
   int active;
 };
 
@@ -192,6 +189,64 @@ __device__ __forceinline__ f32x16 tile_scores(const KFrag& kf, const bf16x8 (&qf
     }
   }
   return acc;
+}
+
+// Prefix moments of K' for the threshold estimate: entry g of a (batch, head) holds the sum
+// of K'_j (kRank floats) and of K'_j K'_j^T (kRank x kRank, row-major) over the keys
+// [0, min(kMomGroup g, S)).  moments_group_kernel writes group g's own sums into entry g + 1
+// (and zeroes entry 0); moments_scan_kernel turns entries 1.. into running sums.
+__global__ __launch_bounds__(256) void moments_group_kernel(const bf16* __restrict__ kp, float* __restrict__ mom,
+                                                            int S, int n_groups) {
+  __shared__ float ks[kMomGroup][kRank + 1];
+  const int bh = blockIdx.x / n_groups, g = blockIdx.x % n_groups;
+  const int nk = min(kMomGroup, S - g * kMomGroup);
+  const bf16* src = kp + ((int64_t)bh * S + (int64_t)g * kMomGroup) * kRank;
+  for (int c = threadIdx.x; c < kMomGroup * kRank / 8; c += 256) {
+    const int j = c / (kRank / 8), r8 = (c % (kRank / 8)) * 8;
+    bf16x8 v = {};
+    if (j < nk) v = *(const bf16x8*)(src + (int64_t)j * kRank + r8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ks[j][r8 + e] = (float)v[e];
+  }
+  __syncthreads();
+  float* dst = mom + ((int64_t)bh * (n_groups + 1) + g + 1) * kMomEntry;
+  // thread t: row t / 8 of K'K'^T, columns 4 (t % 8) .. +3
+  const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int j = 0; j < kMomGroup; ++j) {
+    const float x = ks[j][r];
+    a0 = fmaf(x, ks[j][c0], a0);
+    a1 = fmaf(x, ks[j][c0 + 1], a1);
+    a2 = fmaf(x, ks[j][c0 + 2], a2);
+    a3 = fmaf(x, ks[j][c0 + 3], a3);
+  }
+  *(float4*)(dst + kRank + r * kRank + c0) = float4{a0, a1, a2, a3};
+  if (threadIdx.x < kRank) {
+    float t = 0.f;
+    for (int j = 0; j < kMomGroup; ++j) t += ks[j][threadIdx.x];
+    dst[threadIdx.x] = t;
+  }
+  if (g == 0)
+    for (int e = threadIdx.x; e < kMomEntry; e += 256) mom[(int64_t)bh * (n_groups + 1) * kMomEntry + e] = 0.f;
+}
+
+__global__ __launch_bounds__(256) void moments_scan_kernel(float* __restrict__ mom, int n_bh, int n_groups) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)n_bh * kMomEntry) return;
+  const int bh = (int)(t / kMomEntry), e = (int)(t % kMomEntry);
+  float* col = mom + (int64_t)bh * (n_groups + 1) * kMomEntry + e;
+  constexpr int CH = 32;  // entries loaded together
+  float run = 0.f;
+  for (int g0 = 1; g0 <= n_groups; g0 += CH) {
+    float v[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) v[k] = g0 + k <= n_groups ? col[(int64_t)(g0 + k) * kMomEntry] : 0.f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      run += v[k];
+      if (g0 + k <= n_groups) col[(int64_t)(g0 + k) * kMomEntry] = run;
+    }
+  }
 }
 
 __device__ __forceinline__ int wave_count(bool pred) { return __builtin_popcountll(__ballot(pred)); }
@@ -240,68 +295,47 @@ __global__ __launch_bounds__(kWaves * 64) void select_kernel(IndexerArgs a) {
     c.sd = 0.f;
   }
 
-  // Threshold estimate for rows with more candidates than the buffer holds.
+  // Threshold estimate for rows with more candidates than the buffer holds: the mean and
+  // deviation of the row's importances over the keys of the block's moment prefix, from the
+  // prefix sums of K' and of K' K'^T (mean = q.K1 / N, second moment = q^T K2 q / N).
   if (n_max > kCap) {
-    float s1 = 0.f, s2 = 0.f, s0 = 0.f;
-    const int n_fl = min(n_max, max(kFirstLook, n_max / 4));
-    const int nfl_kb = (n_fl + 31) / 32;
-    const int my_n = i < a.S ? min(causal ? i + 1 : a.S, n_fl) : 0;
-    // key blocks below this bound lie inside every row's sample (no per-key test)
-    const int n_full = i0 + kRows > a.S ? 0 : min(causal ? i0 + 1 : a.S, n_fl);
-    // the same ring of K' loads as the counting pass below
-    KFrag ring[kPrefetch];
+    const int n_groups = (a.S + kMomGroup - 1) / kMomGroup;
+    const int gsel = causal ? (i0 + 1) / kMomGroup : n_groups;  // keys [0, min(kMomGroup gsel, S))
+    const float n_mom = (float)min(gsel * kMomGroup, a.S);
+    const float* me = a.mom + ((int64_t)bh * (n_groups + 1) + gsel) * kMomEntry;
+    // wave w takes rows 2w (lanes 0-31) and 2w + 1 (lanes 32-63); lane l32 holds rank l32
+    const int row = 2 * wave + h2;
+    const int ir = min(i0 + row, a.S - 1);
+    float q[kRank];
 #pragma unroll
-    for (int p = 0; p < kPrefetch; ++p) {
-      ring[p] = load_kfrag(kp, min(wave + p * kWaves, nfl_kb - 1), a.S, lane);
-      __builtin_amdgcn_sched_barrier(0);  // issue order = use order
+    for (int v = 0; v < kRank / 8; ++v) {
+      const bf16x8 x = *(const bf16x8*)(qp + (int64_t)ir * kRank + 8 * v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[8 * v + e] = (float)x[e];
     }
-    for (int kb0 = wave; kb0 < nfl_kb; kb0 += kPrefetch * kWaves) {
+    float y = 0.f;  // (K2 q)[l32]
 #pragma unroll
-      for (int p = 0; p < kPrefetch; ++p) {
-        const int kb = kb0 + p * kWaves;
-        const f32x16 sc = tile_scores(ring[p], qf, kb, a.S, i, causal, kb >= first_edge_kb, lane);
-        ring[p] = load_kfrag(kp, min(kb + kPrefetch * kWaves, nfl_kb - 1), a.S, lane);
-        if (kb >= nfl_kb) continue;
-        if (kb * 32 + 32 <= n_full) {
-          s0 += 16.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s1 += sc[r];
-            s2 = fmaf(sc[r], sc[r], s2);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            if (j < my_n) {
-              s0 += 1.f;
-              s1 += sc[r];
-              s2 = fmaf(sc[r], sc[r], s2);
-            }
-          }
-        }
-      }
+    for (int v = 0; v < kRank / 4; ++v) {
+      const float4 k2 = *(const float4*)(me + kRank + l32 * kRank + 4 * v);
+      y = fmaf(k2.x, q[4 * v], y);
+      y = fmaf(k2.y, q[4 * v + 1], y);
+      y = fmaf(k2.z, q[4 * v + 2], y);
+      y = fmaf(k2.w, q[4 * v + 3], y);
     }
-    // fold the two half-waves (same query, different keys)
-    s0 += __shfl_xor(s0, 32);
-    s1 += __shfl_xor(s1, 32);
-    s2 += __shfl_xor(s2, 32);
-    if (h2 == 0) {
-      sh.red[wave][l32][0] = s0;
-      sh.red[wave][l32][1] = s1;
-      sh.red[wave][l32][2] = s2;
+    float qr = q[0];
+#pragma unroll
+    for (int r = 1; r < kRank; ++r) qr = l32 == r ? q[r] : qr;  // q[l32]
+    float s1 = qr * me[l32], s2 = qr * y;
+#pragma unroll
+    for (int w = 16; w >= 1; w >>= 1) {
+      s1 += __shfl_xor(s1, w);
+      s2 += __shfl_xor(s2, w);
     }
-    __syncthreads();
-    if (tid < kRows) {
-      RowCtl& c = sh.ctl[tid];
-      float t0 = 0.f, t1 = 0.f, t2 = 0.f;
-      for (int w = 0; w < kWaves; ++w) {
-        t0 += sh.red[w][tid][0];
-        t1 += sh.red[w][tid][1];
-        t2 += sh.red[w][tid][2];
-      }
-      c.mean = t0 > 0.f ? t1 / t0 : 0.f;
-      c.sd = t0 > 0.f ? sqrtf(fmaxf(t2 / t0 - c.mean * c.mean, 0.f)) : 0.f;
+    __syncthreads();  // the rows' control entries are initialised
+    if (l32 == 0 && i0 + row < a.S) {
+      RowCtl& c = sh.ctl[row];
+      c.mean = n_mom > 0.f ? s1 / n_mom : 0.f;
+      c.sd = n_mom > 0.f ? sqrtf(fmaxf(s2 / n_mom - c.mean * c.mean, 0.f)) : 0.f;
       if (c.n > kCap) {
         const float target = 0.5f * (float)(c.need + kCap);
         c.K = key_above(c.mean + c.sd * normal_upper_quantile(target / (float)c.n));
@@ -616,6 +650,12 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
   };
   proj(a.q, a.wq, a.qp);
   proj(a.k, a.wk, a.kp);
+  const int n_groups = (a.S + kMomGroup - 1) / kMomGroup;
+  const int n_bh = a.B * a.H;
+  hipLaunchKernelGGL(moments_group_kernel, dim3((unsigned)(n_bh * n_groups)), dim3(256), 0, stream, a.kp, a.mom, a.S,
+                     n_groups);
+  hipLaunchKernelGGL(moments_scan_kernel, dim3((unsigned)((n_bh * kMomEntry + 255) / 256)), dim3(256), 0, stream,
+                     a.mom, n_bh, n_groups);
   const int blocks = a.B * a.H * ((a.S + kRows - 1) / kRows);
   hipLaunchKernelGGL(select_kernel, dim3(blocks), dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();

@@ -61,6 +61,10 @@ struct GatherArgs {
 
 // The indexer's per-row candidate buffer leaves room above the selection size.
 constexpr int kIndexerMaxTopK = 512;
+// Keys per group of the indexer's prefix moments, and floats per moment entry (rank 32: the
+// sum of K' and the sum of K' K'^T).
+constexpr int kMomGroup = 128;
+constexpr int kMomEntry = 32 + 32 * 32;
 
 struct IndexerArgs {
   const void* q;
@@ -69,6 +73,7 @@ struct IndexerArgs {
   const void* wk;
   __bf16* qp;      // [B][H][S][rank] projections (plan scratch)
   __bf16* kp;
+  float* mom;      // [B][H][S/128 + 1][rank + rank*rank] prefix moments of K' (plan scratch)
   int32_t* idx;    // [B][H][S][top_k]
   int32_t* count;  // [B][H][S]
   int32_t B, H, S, D, rank, top_k, causal;
