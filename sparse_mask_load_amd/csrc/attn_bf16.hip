@@ -545,6 +545,7 @@ void attn_bf16_kernel(FwdArgs a) {
     RowState<ND> st;
     reset(st);
     int cur_chunk = a.c0;
+    bool acc_live = false;  // the accumulation in progress has taken a tile (uniform)
 
     // Merges the two key halves and writes chunk `chunk`'s partial (O in the
     // true-max basis, m in natural-log units, l), then resets the state.
@@ -594,6 +595,32 @@ void attn_bf16_kernel(FwdArgs a) {
       }
       __syncthreads();  // the staging buffers are free again (tile loads go there next)
       reset(st);
+    };
+    // An empty accumulation's partial, (0, -inf, 0), is written by every wave for its own
+    // rows, with no merge of the key halves and no staging (nor their barriers).
+    auto flush_empty = [&](int chunk) {
+      constexpr int RPW = BLK / SH::NW;  // rows per wave
+      const int ln = opaque(lane);
+      const int64_t prow0 = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      static_assert(RPW * (D / 4) % 64 == 0, "the wave's rows split evenly over its lanes");
+#pragma unroll
+      for (int k = 0; k < RPW * (D / 4) / 64; ++k) {
+        const int idx = ln + 64 * k;
+        const int r = wave * RPW + idx / (D / 4), c = idx % (D / 4);
+        if (qb * BLK + r < a.S) *(f32x4*)(a.o_part + (prow0 + r) * D + 4 * c) = z;
+      }
+      if (ln < RPW && qb * BLK + wave * RPW + ln < a.S) {
+        a.m_part[prow0 + wave * RPW + ln] = kNegInf;
+        a.l_part[prow0 + wave * RPW + ln] = 0.f;
+      }
+    };
+    auto flush_chunk = [&](int chunk, float* kscr, float* mscr) {
+      if (acc_live)
+        flush_partial(chunk, kscr, mscr);
+      else
+        flush_empty(chunk);
+      acc_live = false;
     };
     // live bits of this wave's key blocks of a tile
     auto live_of = [&](int desc) {
@@ -655,7 +682,8 @@ void attn_bf16_kernel(FwdArgs a) {
       __syncthreads();
       if (!full) {
         const int tchunk = (desc >> kDescChunkShift) & 63;
-        while (cur_chunk < tchunk) flush_partial(cur_chunk++, (float*)kfree, (float*)vfree);
+        while (cur_chunk < tchunk) flush_chunk(cur_chunk++, (float*)kfree, (float*)vfree);
+        acc_live = true;  // this tile belongs to the accumulation of chunk tchunk
       }
       // K of tile t+2 and V of tile t+1 are loaded in slices, one per key block,
       // so that no wave stalls on a full memory-request queue.  Near the end of
@@ -711,7 +739,7 @@ void attn_bf16_kernel(FwdArgs a) {
     wait_vm();  // no tile load may still be in flight when the merge buffers are used
     __syncthreads();
     if (!full) {
-      while (cur_chunk < a.c1) flush_partial(cur_chunk++, (float*)sK0, (float*)sV0);
+      while (cur_chunk < a.c1) flush_chunk(cur_chunk++, (float*)sK0, (float*)sV0);
     } else {
       const int ln = opaque(lane), h2 = ln >> 5;
       float m, l_row;
@@ -839,6 +867,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
     RowState<ND> st;  // acc and l relative to st.m_ref (the reference of the last consumed block)
     reset(st);
     int cur_chunk = a.c0;
+    bool acc_live = false;  // the accumulation in progress has taken a tile (uniform)
     // Row maxima are kept per lane, over the lane's own keys and in raw score units (the
     // scale is positive): lmax for the accumulation in progress, lmax_next for one that starts
     // with the next tile (partial mode).  The wave's row max (both half-waves) is formed when
@@ -891,6 +920,33 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       __syncthreads();
       reset(st);
       lmax = kNegInf;
+    };
+    // An empty accumulation's partial, (0, -inf, 0), is written by every wave for its own
+    // rows, with no merge of the key halves and no staging (nor their barriers).
+    auto flush_empty = [&](int chunk) {
+      constexpr int RPW = BLK / SH::NW;  // rows per wave
+      const int ln = opaque(lane);
+      const int64_t prow0 = ((int64_t)(chunk - a.c0) * a.B * a.H + bh) * a.S + (int64_t)qb * BLK;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      static_assert(RPW * (D / 4) % 64 == 0, "the wave's rows split evenly over its lanes");
+#pragma unroll
+      for (int k = 0; k < RPW * (D / 4) / 64; ++k) {
+        const int idx = ln + 64 * k;
+        const int r = wave * RPW + idx / (D / 4), c = idx % (D / 4);
+        *(f32x4*)(a.o_part + (prow0 + r) * D + 4 * c) = z;
+      }
+      if (ln < RPW) {
+        a.m_part[prow0 + wave * RPW + ln] = kNegInf;
+        a.l_part[prow0 + wave * RPW + ln] = 0.f;
+      }
+      lmax = kNegInf;
+    };
+    auto flush_chunk = [&](int chunk, float* kscr, float* mscr) {
+      if (acc_live)
+        flush_partial(chunk, kscr, mscr);
+      else
+        flush_empty(chunk);
+      acc_live = false;
     };
     auto src_of = [&](int desc) { return tile_source(desc, bh_base, a.ss, a.S, LAYOUT, a.n_chunks, BLK); };
     auto chunk_of = [&](int desc) { return (desc >> kDescChunkShift) & 63; };
@@ -986,10 +1042,11 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       __syncthreads();
       bool fresh = t == 0;  // block 0 of this tile opens an accumulation
       if (!full && cur_chunk < chunk_of(desc)) {
-        while (cur_chunk < chunk_of(desc)) flush_partial(cur_chunk++, (float*)kfree, (float*)vfree);
+        while (cur_chunk < chunk_of(desc)) flush_chunk(cur_chunk++, (float*)kfree, (float*)vfree);
         fresh = true;
       }
       if (fresh) lmax = lmax_next;
+      acc_live = true;  // this tile belongs to the accumulation in progress
       const TileSrc srcK = src_of(__builtin_amdgcn_readfirstlane(sList[min(t + 2, n_tiles - 1)]));
       const TileSrc srcV = src_of(desc1);
 
@@ -1109,7 +1166,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
     wait_vm();
     __syncthreads();
     if (!full) {
-      while (cur_chunk < a.c1) flush_partial(cur_chunk++, (float*)sK0, (float*)sV0);
+      while (cur_chunk < a.c1) flush_chunk(cur_chunk++, (float*)sK0, (float*)sV0);
     } else {
       const int ln = opaque(lane), h2 = ln >> 5;
       float m, l_row;
