@@ -414,9 +414,9 @@ def main() -> int:
                     help="KV chunk layout: contiguous blocks, or striped (token i in chunk i mod C)")
     ap.add_argument("--mode", choices=["merged", "fused"], default="merged",
                     help="merged: partial chunks + chunk_merge (default); fused: chunks folded in-kernel")
-    ap.add_argument("--order", choices=["lpt_xcd", "lpt", "naive", "lpt_device"], default="lpt_device",
+    ap.add_argument("--order", choices=["lpt_xcd", "lpt", "naive", "lpt_device", "lpt_dynamic"], default="lpt_device",
                     help="work order: two-level LPT (heads to XCDs, then Q-blocks), one-level LPT, round-robin, "
-                         "round-based LPT made on the GPU")
+                         "round-based LPT made on the GPU, or the GPU-made LPT queue taken at run time")
     ap.add_argument("--bins", type=int, default=0, help="persistent workgroups (0: one per resident slot)")
     ap.add_argument("--q-pairs", choices=["auto", "on", "off"], default="auto",
                     help="work items of two adjacent Q-blocks (auto: where their union tiles exceed the live "
@@ -526,7 +526,7 @@ def main() -> int:
         "config": {"workload": f"{w.name} block-sparse MHA B{B} H{H} S{S} d{D} block {w.block}, "
                                f"{C} {args.layout} KV chunks {'merged by chunk_merge' if args.mode == 'merged' else 'folded in-kernel'}, "
                                f"work items: {'Q-block pairs' if run.q_pairs else 'Q-blocks'}, "
-                               f"{ {'lpt_xcd': 'two-level LPT (heads to XCDs, then Q-blocks)', 'lpt': 'LPT', 'naive': 'round-robin', 'lpt_device': 'round-based LPT made on the GPU'}[args.order]} over {info['num_bins']} bins",
+                               f"{ {'lpt_xcd': 'two-level LPT (heads to XCDs, then Q-blocks)', 'lpt': 'LPT', 'naive': 'round-robin', 'lpt_device': 'round-based LPT made on the GPU', 'lpt_dynamic': 'LPT queue made on the GPU, taken at run time'}[args.order]} over {info['num_bins']} bins",
                    "B": B, "H": H, "S": S, "D": D, "block": w.block, "n_chunks": C, "layout": args.layout,
                    "mask": {"tiny": "Bernoulli(0.5)+diag", "video": "frame band / Bernoulli",
                             "causal": "block lower-triangular", "skewed": "Zipf(1.2) rows"}[args.workload],
@@ -580,7 +580,7 @@ def main() -> int:
         # and in LPT order
         alt_ms = {}
         n_items = info["n_items"]
-        alts = [(o_, o_, 0) for o_ in ("naive", "lpt", "lpt_xcd", "lpt_device")]
+        alts = [(o_, o_, 0) for o_ in ("naive", "lpt", "lpt_xcd", "lpt_device", "lpt_dynamic")]
         alts += [("grid_id_order", "naive", n_items), ("grid_lpt_order", "lpt", n_items)]
         for alt, alt_order, alt_bins in alts:
             p_alt = run.plan(alt_order, alt_bins)

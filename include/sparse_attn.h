@@ -68,8 +68,27 @@ typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  *                    1024 bins (else SA_ERR_UNSUPPORTED).  The plan call then
  *                    never waits for the device: popcount and every list
  *                    (full range and each chunk) are made on `stream`, and
- *                    sparse_attn_plan_info waits for them to read the statistics. */
-typedef enum { SA_ORDER_LPT = 0, SA_ORDER_NAIVE = 1, SA_ORDER_LPT_XCD = 2, SA_ORDER_LPT_DEVICE = 3 } sa_order;
+ *                    sparse_attn_plan_info waits for them to read the statistics.
+ *  SA_ORDER_LPT_DYNAMIC: the LPT rule in its list-scheduling form: the items in
+ *                    LPT order (load descending, id ascending) form a queue, and
+ *                    each persistent workgroup takes the next item whenever it is
+ *                    free, so work goes to the compute unit that becomes free first
+ *                    at run time rather than by the loads alone.  The plan is made
+ *                    on the GPU as for SA_ORDER_LPT_DEVICE (same limits; its bin
+ *                    lists are also made and exported) plus the queue of each list
+ *                    (SA_PLAN_LPT_ORDER) and two counters per list, which the
+ *                    forward's last workgroup returns to zero.  bf16 block-128
+ *                    kernels (single Q-blocks without a partial last block, and
+ *                    Q-block pairs) take the queue; the other kernels use the bin
+ *                    lists.  Forward calls with one such plan are serialised (each
+ *                    waits for the plan's earlier calls on other streams). */
+typedef enum {
+  SA_ORDER_LPT = 0,
+  SA_ORDER_NAIVE = 1,
+  SA_ORDER_LPT_XCD = 2,
+  SA_ORDER_LPT_DEVICE = 3,
+  SA_ORDER_LPT_DYNAMIC = 4
+} sa_order;
 typedef enum { SA_LAYOUT_CONTIGUOUS = 0, SA_LAYOUT_STRIPED = 1 } sa_layout;
 typedef enum { SA_KIND_BLOCK = 0, SA_KIND_TOPK = 1, SA_KIND_INDEX = 2 } sa_kind;
 
@@ -161,7 +180,8 @@ typedef enum {
   SA_PLAN_TOPK_IDX = 6, /* int32 [B][H][S][top_k] selected keys (TOPK/INDEX)              */
   SA_PLAN_TOPK_COUNT = 7, /* int32 [B][H][S]  number of selected keys                     */
   SA_PLAN_PAIR_ROW = 8,   /* int32 [B][H][nP]  q_pairs: live tiles of the union of rows 2p, 2p+1 */
-  SA_PLAN_PAIR_CROW = 9   /* int32 [B][H][C][nP] q_pairs: the same per chunk (striped: = PAIR_ROW) */
+  SA_PLAN_PAIR_CROW = 9,  /* int32 [B][H][C][nP] q_pairs: the same per chunk (striped: = PAIR_ROW) */
+  SA_PLAN_LPT_ORDER = 10  /* int32 [n_items] SA_ORDER_LPT_DYNAMIC: the queue, items in LPT order      */
 } sa_plan_array;
 
 /* Build a plan.
@@ -240,8 +260,9 @@ sa_status chunk_merge(int32_t n_parts, const float* const* o_parts, const float*
 sa_status sparse_attn_plan_info(const sa_plan* plan, sa_plan_info* out);
 
 /* Copy one of the plan's arrays to host memory dst (n_elems elements of the
- * array's type).  chunk selects the list for ITEMS / BIN_PTR / BIN_LOAD: -1 is
- * the full-range list, c in [0, C) the list of chunk c.  Synchronous. */
+ * array's type).  chunk selects the list for ITEMS / BIN_PTR / BIN_LOAD /
+ * LPT_ORDER: -1 is the full-range list, c in [0, C) the list of chunk c.
+ * Synchronous. */
 sa_status sparse_attn_plan_copy(const sa_plan* plan, int32_t what, int32_t chunk, void* dst,
                                 int64_t n_elems);
 

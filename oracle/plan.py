@@ -158,6 +158,32 @@ def lpt_rounds(loads: Sequence[int], m: int) -> Tuple[List[List[int]], List[int]
     return bins, bin_load
 
 
+def lpt_order(loads: Sequence[int]) -> List[int]:
+    """The jobs in LPT order: load descending, then job id ascending (reading (i) above).
+
+    The queue of the LPT paragraph's greedy in its list-scheduling form: whenever a machine
+    becomes free it takes the next job of this list.  With run times equal to the loads,
+    the machine that becomes free first is the least-loaded one, so the form gives ``lpt``'s
+    assignment (``list_schedule`` below shows it on given run times).
+    """
+    return sorted(range(len(loads)), key=lambda i: (-int(loads[i]), i))
+
+
+def list_schedule(order: Sequence[int], times: Sequence[float], m: int) -> List[List[int]]:
+    """Runs the jobs of ``order`` on m machines, each free machine taking the next job.
+
+    ``times[j]`` is job j's run time.  Among machines free at the same moment the lowest
+    index takes the job first (reading (ii) above).  Returns each machine's jobs in order.
+    """
+    free_at = [0.0] * m
+    bins: List[List[int]] = [[] for _ in range(m)]
+    for job in order:
+        b = min(range(m), key=lambda k: (free_at[k], k))
+        bins[b].append(job)
+        free_at[b] += float(times[job])
+    return bins
+
+
 def naive(loads: Sequence[int], m: int) -> Tuple[List[List[int]], List[int]]:
     """Round-robin in job-id order: job i runs on machine i mod m."""
     bins: List[List[int]] = [[] for _ in range(m)]
@@ -186,7 +212,8 @@ def plan_items(row_loads: np.ndarray, m: int, order: str = "lpt", groups: int = 
 
     ``order``: "lpt", "naive", "lpt_device" (``lpt_rounds``) or "lpt_xcd"
     (``lpt_grouped`` with the heads of ``row_loads`` [B, H, nQ] and ``groups``
-    bin groups).  Returns ``items`` (all
+    bin groups); "lpt_dynamic" makes the bins of "lpt_device" and adds ``queue``,
+    the items in LPT order.  Returns ``items`` (all
     bins' lists concatenated), ``bin_ptr`` (m + 1 offsets), ``bin_load`` and
     ``makespan``.
     """
@@ -195,13 +222,17 @@ def plan_items(row_loads: np.ndarray, m: int, order: str = "lpt", groups: int = 
     if order == "lpt_xcd":
         bins, bin_load = lpt_grouped(loads, row_loads.shape[-1], m, groups)
     else:
-        bins, bin_load = {"lpt": lpt, "naive": naive, "lpt_device": lpt_rounds}[order](loads, m)
+        bins, bin_load = {"lpt": lpt, "naive": naive, "lpt_device": lpt_rounds,
+                          "lpt_dynamic": lpt_rounds}[order](loads, m)
     items, ptr = [], [0]
     for b in bins:
         items.extend(b)
         ptr.append(len(items))
-    return {"items": np.array(items, dtype=np.int64), "bin_ptr": np.array(ptr, dtype=np.int64),
-            "bin_load": np.array(bin_load, dtype=np.int64), "makespan": int(max(bin_load))}
+    out = {"items": np.array(items, dtype=np.int64), "bin_ptr": np.array(ptr, dtype=np.int64),
+           "bin_load": np.array(bin_load, dtype=np.int64), "makespan": int(max(bin_load))}
+    if order == "lpt_dynamic":
+        out["queue"] = np.array(lpt_order(loads), dtype=np.int64)
+    return out
 
 
 def _tokens_per_block_in_part(S: int, block: int, n_parts: int, layout: str) -> np.ndarray:

@@ -18,15 +18,15 @@ LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 
 SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_NOMEM = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
-SA_ORDER_LPT, SA_ORDER_NAIVE, SA_ORDER_LPT_XCD, SA_ORDER_LPT_DEVICE = 0, 1, 2, 3
+SA_ORDER_LPT, SA_ORDER_NAIVE, SA_ORDER_LPT_XCD, SA_ORDER_LPT_DEVICE, SA_ORDER_LPT_DYNAMIC = 0, 1, 2, 3, 4
 SA_LAYOUT_CONTIGUOUS, SA_LAYOUT_STRIPED = 0, 1
 SA_KIND_BLOCK, SA_KIND_TOPK, SA_KIND_INDEX = 0, 1, 2
 (SA_PLAN_ROW, SA_PLAN_COL, SA_PLAN_CROW, SA_PLAN_ITEMS, SA_PLAN_BIN_PTR, SA_PLAN_BIN_LOAD,
- SA_PLAN_TOPK_IDX, SA_PLAN_TOPK_COUNT, SA_PLAN_PAIR_ROW, SA_PLAN_PAIR_CROW) = range(10)
+ SA_PLAN_TOPK_IDX, SA_PLAN_TOPK_COUNT, SA_PLAN_PAIR_ROW, SA_PLAN_PAIR_CROW, SA_PLAN_LPT_ORDER) = range(11)
 
 _DTYPES = {"f32": SA_F32, "bf16": SA_BF16}
 _ORDERS = {"lpt": SA_ORDER_LPT, "naive": SA_ORDER_NAIVE, "lpt_xcd": SA_ORDER_LPT_XCD,
-           "lpt_device": SA_ORDER_LPT_DEVICE}
+           "lpt_device": SA_ORDER_LPT_DEVICE, "lpt_dynamic": SA_ORDER_LPT_DYNAMIC}
 _LAYOUTS = {"contiguous": SA_LAYOUT_CONTIGUOUS, "striped": SA_LAYOUT_STRIPED}
 
 

@@ -50,6 +50,9 @@ struct sa_plan {
   std::mutex upload_mutex;
   int64_t total_live = 0, load_sum = 0, makespan = 0, lower_bound = 0;
   // TOPK / INDEX
+  // SA_ORDER_LPT_DYNAMIC: each list's queue (items in LPT order) and its two counters
+  int32_t* d_lpt_order = nullptr;    // [(C+1)][n_items]
+  int32_t* d_dyn_ctr = nullptr;      // [(C+1)][2]
   int32_t* d_idx = nullptr;          // [B][H][S][top_k]
   int32_t* d_count = nullptr;        // [B][H][S]
   __bf16* d_qp = nullptr;            // [B][H][S][rank]
@@ -290,13 +293,17 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
   // item loads: mask row counts, or the union counts of Q-block pairs
   const int32_t* d_load = P->q_pairs ? P->d_prow : P->d_row;
   const int32_t* d_cload = P->q_pairs ? P->d_pcrow : P->d_crow;
-  if (P->order == SA_ORDER_LPT_DEVICE) {
+  if (P->order == SA_ORDER_LPT_DEVICE || P->order == SA_ORDER_LPT_DYNAMIC) {
     // every list on the device, right behind the popcount: nothing waits for the host
     if ((st = dalloc(P, &P->d_bin_load, (size_t)(C + 1) * P->num_bins, stream)) ||
         (st = dalloc(P, &P->d_stats, (size_t)(C + 1) * 4, stream)))
       return st;
+    const bool dyn = P->order == SA_ORDER_LPT_DYNAMIC;
+    if (dyn && ((st = dalloc(P, &P->d_lpt_order, (size_t)(C + 1) * P->n_items, stream)) ||
+                (st = dalloc(P, &P->d_dyn_ctr, (size_t)(C + 1) * 2, stream))))
+      return st;
     SA_HIP(sa::launch_plan_rounds(d_load, d_cload, BH, nI, C, P->num_bins, P->d_items, P->d_bin_ptr,
-                                  P->d_bin_load, P->d_stats, stream));
+                                  P->d_bin_load, P->d_stats, stream, 0, -1, P->d_lpt_order, P->d_dyn_ctr));
     P->device_lists = true;
     return SA_OK;
   }
@@ -469,10 +476,14 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
     return fail(SA_ERR_INVALID, "unknown sparsity kind %d", sp->kind);
   sa_status st = validate_problem(prob, sp->kind == SA_KIND_BLOCK);
   if (st) return st;
-  if (order != SA_ORDER_LPT && order != SA_ORDER_NAIVE && order != SA_ORDER_LPT_XCD && order != SA_ORDER_LPT_DEVICE)
+  if (order != SA_ORDER_LPT && order != SA_ORDER_NAIVE && order != SA_ORDER_LPT_XCD && order != SA_ORDER_LPT_DEVICE &&
+      order != SA_ORDER_LPT_DYNAMIC)
     return fail(SA_ERR_INVALID, "unknown order %d", order);
+  const bool device_order = order == SA_ORDER_LPT_DEVICE || order == SA_ORDER_LPT_DYNAMIC;
+  if (order == SA_ORDER_LPT_DYNAMIC && sp->kind != SA_KIND_BLOCK)
+    return fail(SA_ERR_INVALID, "the run-time order exists only for block plans");
   if (num_bins < 0) return fail(SA_ERR_INVALID, "num_bins %d < 0", num_bins);
-  if (order == SA_ORDER_LPT_DEVICE && sp->kind == SA_KIND_BLOCK) {
+  if (device_order && sp->kind == SA_KIND_BLOCK) {
     const int64_t nQ = (prob->S + prob->block - 1) / prob->block;
     const int64_t n_items = (int64_t)prob->B * prob->H * (prob->q_pairs ? (nQ + 1) / 2 : nQ);
     if (n_items > sa::kDevicePlanMaxItems || num_bins > sa::kDevicePlanMaxBins)
@@ -490,7 +501,7 @@ sa_status sparse_attn_plan(const sa_problem* prob, const sa_sparsity* sp, int32_
   }
   P->num_bins = num_bins ? num_bins : default_bins(*prob, P->device);
   P->n_xcd = xcd_count(P->device);
-  if (order == SA_ORDER_LPT_DEVICE && sp->kind == SA_KIND_BLOCK && P->num_bins > sa::kDevicePlanMaxBins) {
+  if (device_order && sp->kind == SA_KIND_BLOCK && P->num_bins > sa::kDevicePlanMaxBins) {
     delete P;  // the default bin count of this device is above the planner's limit
     return fail(SA_ERR_UNSUPPORTED, "device planning takes at most %d bins (default here: %d)",
                 sa::kDevicePlanMaxBins, P->num_bins);
@@ -550,6 +561,15 @@ sa_status sparse_attn_fwd(const sa_plan* P, const void* q, const void* k, const 
   a.mask = P->d_mask;
   a.items = P->d_items + (size_t)list * P->n_items;
   a.bin_ptr = P->d_bin_ptr + (size_t)list * (P->num_bins + 1);
+  if (P->order == SA_ORDER_LPT_DYNAMIC) {
+    // the queue's counters are shared by every call with this plan: calls on other streams
+    // finish first (a call on this stream follows the previous one anyway)
+    std::lock_guard<std::mutex> lock(const_cast<sa_plan*>(P)->use_mutex);
+    for (const auto& u : P->uses)
+      if (u.first != stream) SA_HIP(hipStreamWaitEvent(stream, u.second, 0));
+    a.dyn_items = P->d_lpt_order + (size_t)list * P->n_items;
+    a.dyn_ctr = P->d_dyn_ctr + 2 * list;
+  }
   a.trace = trace;
   a.B = pr.B; a.H = pr.H; a.S = pr.S; a.nQ = P->nQ; a.nK = P->nK; a.n_chunks = pr.n_chunks;
   a.layout = pr.layout; a.c0 = chunk_begin; a.c1 = chunk_end; a.num_bins = P->num_bins;
@@ -665,6 +685,11 @@ sa_status sparse_attn_plan_copy(const sa_plan* P, int32_t what, int32_t chunk, v
                    : (const void*)(P->h_bin_load.data() + (size_t)list * P->num_bins);
       count = P->num_bins;
       esize = 8;
+      break;
+    case SA_PLAN_LPT_ORDER:
+      if (chunk < -1 || chunk >= C) return fail(SA_ERR_INVALID, "chunk %d outside [-1, %d)", chunk, C);
+      src = P->d_lpt_order ? (const void*)(P->d_lpt_order + (size_t)list * P->n_items) : nullptr;
+      count = P->d_lpt_order ? P->n_items : 0;
       break;
     case SA_PLAN_TOPK_IDX: src = P->d_idx; count = block ? 0 : BH * pr.S * P->top_k; break;
     case SA_PLAN_TOPK_COUNT: src = P->d_count; count = block ? 0 : BH * pr.S; break;

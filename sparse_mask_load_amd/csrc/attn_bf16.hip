@@ -138,6 +138,19 @@ __device__ __forceinline__ void barrier_only() {
   asm volatile("" ::: "memory");
 }
 
+// Run-time work queue (the list-scheduling form of LPT): one thread of a workgroup takes
+// the next position with a device-scope atomic add; the last workgroup to finish returns the
+// queue's two counters (next position, finished workgroups) to zero for the next launch.
+__device__ __forceinline__ int queue_take(int32_t* ctr) {
+  return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void queue_finish(int32_t* ctr) {
+  if (__hip_atomic_fetch_add(ctr + 1, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+    __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Where the rows of one K/V tile live in global memory: row r of the tile is
 // element base + r * row_stride; rows at or beyond `rows` repeat the last
 // valid row (the partial last block of a ragged sequence).
@@ -839,13 +852,25 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
   const bf16* __restrict__ gK = (const bf16*)a.k;
   const bf16* __restrict__ gV = (const bf16*)a.v;
   const int bin = blockIdx.x;
-  const int p_begin = a.bin_ptr[bin], p_end = a.bin_ptr[bin + 1];
   const float sl2 = a.scale_log2;   // > 0
   const float inv_sl2 = 1.f / sl2;
+  // the workgroup's items: its bin's list, or positions taken from the run-time queue
+  const bool dyn = a.dyn_items != nullptr;
+  __shared__ int sQueuePos;
+  int pos = 0, p_end = 0, next_pos = 0;
+  if (dyn) {
+    p_end = a.bin_ptr[a.num_bins];
+    if (tid == 0) sQueuePos = queue_take(a.dyn_ctr);
+    __syncthreads();
+    pos = __builtin_amdgcn_readfirstlane(sQueuePos);
+  } else {
+    pos = a.bin_ptr[bin];
+    p_end = a.bin_ptr[bin + 1];
+  }
 
-  for (int pos = p_begin; pos < p_end; ++pos) {
+  while (pos < p_end) {
     const int64_t t_start = realtime_now();
-    const int item = a.items[pos];
+    const int item = dyn ? a.dyn_items[pos] : a.items[pos];
     const int qb = item % a.nQ;
     const int bh = item / a.nQ;
     const int b = bh / a.H, h = bh % a.H;
@@ -1040,6 +1065,9 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
 
       wait_vm();
       __syncthreads();
+      // (thread 0) the position of the workgroup's next item, taken from the run-time queue
+      // here, right after a wait for every load in flight: the next such wait is a tile away
+      if (dyn && t == 0 && tid == 0) next_pos = queue_take(a.dyn_ctr);
       bool fresh = t == 0;  // block 0 of this tile opens an accumulation
       if (!full && cur_chunk < chunk_of(desc)) {
         while (cur_chunk < chunk_of(desc)) flush_chunk(cur_chunk++, (float*)kfree, (float*)vfree);
@@ -1192,7 +1220,18 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       tr[2] = hw_location();
       tr[3] = ((int64_t)bin << 32) | (int64_t)(uint32_t)item;
     }
+    if (dyn) {
+      if (tid == 0) {
+        if (n_tiles == 0) next_pos = queue_take(a.dyn_ctr);  // (else taken during the first tile)
+        sQueuePos = next_pos;
+      }
+      __syncthreads();  // (every wave read the previous position before this item's barriers)
+      pos = __builtin_amdgcn_readfirstlane(sQueuePos);
+    } else {
+      ++pos;
+    }
   }
+  if (dyn && tid == 0) queue_finish(a.dyn_ctr);
 }
 
 // Q-block pairs (S a multiple of 128): an item is the two Q-blocks 2p and 2p+1
@@ -1250,13 +1289,25 @@ void attn_bf16_pair_kernel(FwdArgs a) {
   const bf16* __restrict__ gK = (const bf16*)a.k;
   const bf16* __restrict__ gV = (const bf16*)a.v;
   const int bin = blockIdx.x;
-  const int p_begin = a.bin_ptr[bin], p_end = a.bin_ptr[bin + 1];
   const float sl2 = a.scale_log2;   // > 0
   const float inv_sl2 = 1.f / sl2;
+  // the workgroup's items: its bin's list, or positions taken from the run-time queue
+  const bool dyn = a.dyn_items != nullptr;
+  __shared__ int sQueuePos;
+  int pos = 0, p_end = 0, next_pos = 0;
+  if (dyn) {
+    p_end = a.bin_ptr[a.num_bins];
+    if (tid == 0) sQueuePos = queue_take(a.dyn_ctr);
+    __syncthreads();
+    pos = __builtin_amdgcn_readfirstlane(sQueuePos);
+  } else {
+    pos = a.bin_ptr[bin];
+    p_end = a.bin_ptr[bin + 1];
+  }
 
-  for (int pos = p_begin; pos < p_end; ++pos) {
+  while (pos < p_end) {
     const int64_t t_start = realtime_now();
-    const int item = a.items[pos];
+    const int item = dyn ? a.dyn_items[pos] : a.items[pos];
     const int pr = item % a.nI;
     const int bh = item / a.nI;
     const int b = bh / a.H, h = bh % a.H;
@@ -1447,6 +1498,9 @@ void attn_bf16_pair_kernel(FwdArgs a) {
       if constexpr (H == 0) {
         wait_vm();
         __syncthreads();
+        // (thread 0) the position of the workgroup's next item, taken from the run-time queue
+        // here, right after a wait for every load in flight: the next such wait is a tile away
+        if (dyn && t == 0 && tid == 0) next_pos = queue_take(a.dyn_ctr);
       } else {
         barrier_only();
       }
@@ -1612,7 +1666,18 @@ void attn_bf16_pair_kernel(FwdArgs a) {
       tr[2] = hw_location();
       tr[3] = ((int64_t)bin << 32) | (int64_t)(uint32_t)item;
     }
+    if (dyn) {
+      if (tid == 0) {
+        if (n_tiles == 0) next_pos = queue_take(a.dyn_ctr);  // (else taken during the first tile)
+        sQueuePos = next_pos;
+      }
+      __syncthreads();  // (every wave read the previous position before this item's barriers)
+      pos = __builtin_amdgcn_readfirstlane(sQueuePos);
+    } else {
+      ++pos;
+    }
   }
+  if (dyn && tid == 0) queue_finish(a.dyn_ctr);
 }
 
 template <int D, int BLK>

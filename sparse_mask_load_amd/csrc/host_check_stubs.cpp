@@ -11,7 +11,7 @@ hipError_t launch_popcount(const uint8_t*, int, int, int, int, int, int32_t*, in
   return hipErrorNotSupported;
 }
 hipError_t launch_plan_rounds(const int32_t*, const int32_t*, int, int, int, int, int32_t*, int32_t*, int64_t*,
-                              int64_t*, hipStream_t, int, int) {
+                              int64_t*, hipStream_t, int, int, int32_t*, int32_t*) {
   return hipErrorNotSupported;
 }
 hipError_t launch_attn_bf16(const FwdArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }

@@ -36,6 +36,10 @@ struct FwdArgs {
   const uint8_t* mask;    // [B][H][nQ][nK]
   const int32_t* items;   // work list of this launch
   const int32_t* bin_ptr; // [num_bins + 1]
+  // run-time queue (SA_ORDER_LPT_DYNAMIC), null otherwise: items in LPT order and two
+  // counters (next position, finished workgroups) that the last workgroup resets
+  const int32_t* dyn_items;
+  int32_t* dyn_ctr;
   int64_t* trace;         // nullable
   int32_t B, H, S, nQ, nK, n_chunks, layout, c0, c1;
   int32_t num_bins;
@@ -101,9 +105,12 @@ hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_ch
 // from chunk c of crow.  Lists [list0, list0 + n_lists) are made (n_lists < 0: through list
 // C), list list0 + s written to slot s of items [.][BH*nQ], bin_ptr [.][m+1], bin_load [.][m]
 // and stats [.][4] = (load sum, max item load, makespan, lower bound).
+// order (nullable): each list's items in LPT order; dyn_ctr (nullable): two counters per list,
+// zeroed (the run-time queue of SA_ORDER_LPT_DYNAMIC)
 hipError_t launch_plan_rounds(const int32_t* row, const int32_t* crow, int BH, int nQ, int C, int m, int32_t* items,
                               int32_t* bin_ptr, int64_t* bin_load, int64_t* stats, hipStream_t stream,
-                              int list0 = 0, int n_lists = -1);
+                              int list0 = 0, int n_lists = -1, int32_t* order = nullptr,
+                              int32_t* dyn_ctr = nullptr);
 hipError_t launch_attn_bf16(const FwdArgs& a, int D, int block, hipStream_t stream);
 int attn_bf16_wg_per_cu(int block);  // workgroups the bf16 kernel keeps resident per CU
 hipError_t launch_attn_f32(const FwdArgs& a, int D, int block, hipStream_t stream);

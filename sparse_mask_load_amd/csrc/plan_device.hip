@@ -41,7 +41,9 @@ __global__ __launch_bounds__(kThreads) void plan_rounds_kernel(const int32_t* __
                                                                int C, int m, int32_t* __restrict__ items,
                                                                int32_t* __restrict__ bin_ptr,
                                                                int64_t* __restrict__ bin_load,
-                                                               int64_t* __restrict__ stats, int list0) {
+                                                               int64_t* __restrict__ stats, int list0,
+                                                               int32_t* __restrict__ order,
+                                                               int32_t* __restrict__ dyn_ctr) {
   __shared__ uint32_t key[kDevicePlanMaxItems];   // sort keys; after the sort, items in LPT order
   __shared__ uint16_t bin_at[kDevicePlanMaxItems];  // bin of the item at each LPT position
   __shared__ uint64_t xch[kThreads];               // bitonic exchange across waves / scan buffer
@@ -91,6 +93,11 @@ __global__ __launch_bounds__(kThreads) void plan_rounds_kernel(const int32_t* __
       }
       __syncthreads();
     }
+
+  // the queue of the run-time order: the items in LPT order, and its counters at zero
+  if (order)
+    for (int p = tid; p < n; p += kThreads) order[(int64_t)slot * n + p] = (int32_t)(key[p] & ((1u << kIdBits) - 1));
+  if (dyn_ctr && tid < 2) dyn_ctr[2 * slot + tid] = 0;
 
   // 2. rounds; thread t holds one bin key (load << 16 | bin), sentinels beyond m
   uint64_t bkey = tid < m ? (uint64_t)tid : ~0ull;
@@ -169,13 +176,13 @@ __global__ __launch_bounds__(kThreads) void plan_rounds_kernel(const int32_t* __
 
 hipError_t launch_plan_rounds(const int32_t* row, const int32_t* crow, int BH, int nQ, int C, int m, int32_t* items,
                               int32_t* bin_ptr, int64_t* bin_load, int64_t* stats, hipStream_t stream, int list0,
-                              int n_lists) {
+                              int n_lists, int32_t* order, int32_t* dyn_ctr) {
   if (n_lists < 0) n_lists = C + 1 - list0;
   if (BH * nQ > kDevicePlanMaxItems || m > kDevicePlanMaxBins || m < 1 || list0 < 0 || n_lists < 1 ||
       list0 + n_lists > C + 1)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(plan_rounds_kernel, dim3(n_lists), dim3(kThreads), 0, stream, row, crow, BH, nQ, C, m, items,
-                     bin_ptr, bin_load, stats, list0);
+                     bin_ptr, bin_load, stats, list0, order, dyn_ctr);
   return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ T.test_problem_fields_are_the_declared_ones()
 T.test_token_causal_only_for_block_plans()
 T.test_q_pairs_only_for_block_plans()
 T.test_hip_errors_surface_as_sa_err_hip()
-T.test_device_order_limits_checked_before_the_gpu()
+for order in (bd.SA_ORDER_LPT_DEVICE, bd.SA_ORDER_LPT_DYNAMIC):
+    T.test_device_order_limits_checked_before_the_gpu(order)
 T.test_fwd_and_merge_argument_errors()
 print("SANITIZED HOST CHECKS OK", flush=True)

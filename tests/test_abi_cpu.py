@@ -181,17 +181,21 @@ def test_q_pairs_only_for_block_plans():
     assert "q_pairs" in bd.sa_last_error()
 
 
-def test_device_order_limits_checked_before_the_gpu():
+@pytest.mark.parametrize("order", [bd.SA_ORDER_LPT_DEVICE, bd.SA_ORDER_LPT_DYNAMIC], ids=["device", "dynamic"])
+def test_device_order_limits_checked_before_the_gpu(order):
     # 65 heads of 256 Q-blocks = 16640 items, above the device planner's 16384
     big = _problem(H=65, S=16384, sb=65 * 16384 * 64, sh=16384 * 64, n_chunks=1)
-    assert _plan_status(big, order=bd.SA_ORDER_LPT_DEVICE) == bd.SA_ERR_UNSUPPORTED
+    assert _plan_status(big, order=order) == bd.SA_ERR_UNSUPPORTED
     assert "16384" in bd.sa_last_error()
-    assert _plan_status(_problem(), order=bd.SA_ORDER_LPT_DEVICE, num_bins=1025) == bd.SA_ERR_UNSUPPORTED
+    assert _plan_status(_problem(), order=order, num_bins=1025) == bd.SA_ERR_UNSUPPORTED
     # with Q-block pairs the limit counts pairs: 129 heads of 128 pairs = 16512 items
     pairs = _problem(H=129, S=32768, block=128, q_pairs=1, sb=129 * 32768 * 64, sh=32768 * 64, n_chunks=1)
-    assert _plan_status(pairs, order=bd.SA_ORDER_LPT_DEVICE) == bd.SA_ERR_UNSUPPORTED
+    assert _plan_status(pairs, order=order) == bd.SA_ERR_UNSUPPORTED
     assert "16384" in bd.sa_last_error()
-    assert _plan_status(_problem(), order=4) == bd.SA_ERR_INVALID
+    assert _plan_status(_problem(), order=5) == bd.SA_ERR_INVALID
+    # the run-time queue exists only for block plans
+    assert _plan_status(_problem(), kind=bd.SA_KIND_TOPK, order=bd.SA_ORDER_LPT_DYNAMIC) == bd.SA_ERR_INVALID
+    assert "block plans" in bd.sa_last_error()
 
 
 def test_fwd_and_merge_argument_errors():

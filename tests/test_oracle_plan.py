@@ -87,6 +87,25 @@ def test_lpt_is_list_scheduling_of_sorted_jobs():
     assert sorted(j for lst in bins for j in lst) == list(range(len(loads)))
 
 
+def test_lpt_order_and_list_scheduling():
+    # the queue of the run-time order: loads descending, ids ascending on ties (hand example)
+    assert P.lpt_order([3, 7, 3, 0, 7]) == [1, 4, 0, 2, 3]
+    # list scheduling of that queue with run times equal to the loads is the LPT greedy
+    rng = np.random.default_rng(11)
+    for m in (1, 2, 5, 17):
+        loads = rng.integers(0, 60, size=200).tolist()
+        assert P.list_schedule(P.lpt_order(loads), loads, m) == P.lpt(loads, m)[0]
+    # page example: [8,7,6,5,4] on two machines -> 8+5+4 | 7+6
+    assert P.list_schedule(P.lpt_order([8, 7, 6, 5, 4]), [8, 7, 6, 5, 4], 2) == [[0, 3, 4], [1, 2]]
+    # with other run times a machine that finishes early takes more of the queue
+    times = [10, 10, 1, 1, 1, 1]
+    assert P.list_schedule([0, 1, 2, 3, 4, 5], [20, 10, 1, 1, 1, 1], 2) == [[0], [1, 2, 3, 4, 5]]
+    assert P.list_schedule([0, 1, 2, 3, 4, 5], times, 2) == [[0, 2, 4], [1, 3, 5]]
+    q = P.plan_items(np.array([[3, 7, 3, 0, 7]]), 2, "lpt_dynamic")
+    assert q["queue"].tolist() == [1, 4, 0, 2, 3]
+    assert np.array_equal(q["items"], P.plan_items(np.array([[3, 7, 3, 0, 7]]), 2, "lpt_device")["items"])
+
+
 def test_naive_round_robin():
     bins, bl = P.naive([1, 2, 3, 4, 5, 6, 7], 3)
     assert bins == [[0, 3, 6], [1, 4], [2, 5]] and bl == [12, 7, 9]
