@@ -5,8 +5,9 @@ workload (B1 H16 S16384 d128, block 128, lower-triangular block mask, KV in 4 co
 chunks, one bin per compute unit):
 
   1. sparse_attn_plan: GPU popcount of the mask and the work lists, by default with the
-     device planner (round-based LPT made on the GPU; --order lpt_xcd / lpt / naive plan
-     on the host instead).  The mask is a runtime input, so every step re-plans, on a
+     device planner (round-based LPT made on the GPU; --order lpt_dynamic: the same plan's
+     LPT queue, taken by the attention kernel's workgroups at run time, one counter per XCD;
+     lpt_xcd / lpt / naive plan on the host instead).  The mask is a runtime input, so every step re-plans, on a
      side stream; the forward call waits for the plan's event;
   2. sparse_attn_fwd in partial mode over chunks [0, 4): one (O, m, l) partial per chunk;
   3. chunk_merge: online-softmax merge of the 4 partials into O (bf16).
@@ -394,7 +395,7 @@ def workload_summary(bd, W, torch, dev, cfg, layout="contiguous", steps=10, reps
            "step_pct_bf16_peak": round(100 * flop / step_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
            "fwd_partial_ms": round(fwd_ms, 4), "fwd_partial_tflops": round(flop / fwd_ms / 1e9, 2),
            "merge_ms": round(merge_ms, 4), "merge_gbs": round(run.merge_bytes() / merge_ms / 1e6, 1),
-           "by_order": {o: run.order_summary(o, reps) for o in ("lpt_device", "lpt", "naive")}}
+           "by_order": {o: run.order_summary(o, reps) for o in ("lpt_dynamic", "lpt_device", "lpt", "naive")}}
     if ring:
         out["ring_steps"] = run.ring_steps("lpt_device", reps)
     del run

@@ -71,13 +71,16 @@ typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  *                    sparse_attn_plan_info waits for them to read the statistics.
  *  SA_ORDER_LPT_DYNAMIC: the LPT rule in its list-scheduling form: the items in
  *                    LPT order (load descending, id ascending) form a queue, and
- *                    each persistent workgroup takes the next item whenever it is
+ *                    each persistent workgroup takes a new item whenever it is
  *                    free, so work goes to the compute unit that becomes free first
- *                    at run time rather than by the loads alone.  The plan is made
- *                    on the GPU as for SA_ORDER_LPT_DEVICE (same limits; its bin
- *                    lists are also made and exported) plus the queue of each list
- *                    (SA_PLAN_LPT_ORDER) and two counters per list, which the
- *                    forward's last workgroup returns to zero.  bf16 block-128
+ *                    at run time rather than by the loads alone.  Queue position i
+ *                    belongs to XCD i mod 8 (workgroup b runs on XCD b mod 8): a
+ *                    workgroup takes its XCD's next position, and another XCD's once
+ *                    its own are all taken.  The plan is made on the GPU as for
+ *                    SA_ORDER_LPT_DEVICE (same limits; its bin lists are also made
+ *                    and exported) plus the queue of each list (SA_PLAN_LPT_ORDER)
+ *                    and 16 counters per list, which the forward's last workgroup
+ *                    returns to zero.  bf16 block-128
  *                    kernels (single Q-blocks without a partial last block, and
  *                    Q-block pairs) take the queue; the other kernels use the bin
  *                    lists.  Forward calls with one such plan are serialised (each

@@ -52,7 +52,7 @@ struct sa_plan {
   // TOPK / INDEX
   // SA_ORDER_LPT_DYNAMIC: each list's queue (items in LPT order) and its two counters
   int32_t* d_lpt_order = nullptr;    // [(C+1)][n_items]
-  int32_t* d_dyn_ctr = nullptr;      // [(C+1)][2]
+  int32_t* d_dyn_ctr = nullptr;      // [(C+1)][sa::kQueueCtrs]
   int32_t* d_idx = nullptr;          // [B][H][S][top_k]
   int32_t* d_count = nullptr;        // [B][H][S]
   __bf16* d_qp = nullptr;            // [B][H][S][rank]
@@ -300,7 +300,7 @@ sa_status plan_block(sa_plan* P, const sa_sparsity* sp, hipStream_t stream) {
       return st;
     const bool dyn = P->order == SA_ORDER_LPT_DYNAMIC;
     if (dyn && ((st = dalloc(P, &P->d_lpt_order, (size_t)(C + 1) * P->n_items, stream)) ||
-                (st = dalloc(P, &P->d_dyn_ctr, (size_t)(C + 1) * 2, stream))))
+                (st = dalloc(P, &P->d_dyn_ctr, (size_t)(C + 1) * sa::kQueueCtrs, stream))))
       return st;
     SA_HIP(sa::launch_plan_rounds(d_load, d_cload, BH, nI, C, P->num_bins, P->d_items, P->d_bin_ptr,
                                   P->d_bin_load, P->d_stats, stream, 0, -1, P->d_lpt_order, P->d_dyn_ctr));
@@ -568,7 +568,7 @@ sa_status sparse_attn_fwd(const sa_plan* P, const void* q, const void* k, const 
     for (const auto& u : P->uses)
       if (u.first != stream) SA_HIP(hipStreamWaitEvent(stream, u.second, 0));
     a.dyn_items = P->d_lpt_order + (size_t)list * P->n_items;
-    a.dyn_ctr = P->d_dyn_ctr + 2 * list;
+    a.dyn_ctr = P->d_dyn_ctr + sa::kQueueCtrs * list;
   }
   a.trace = trace;
   a.B = pr.B; a.H = pr.H; a.S = pr.S; a.nQ = P->nQ; a.nK = P->nK; a.n_chunks = pr.n_chunks;

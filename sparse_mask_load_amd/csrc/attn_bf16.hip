@@ -138,16 +138,31 @@ __device__ __forceinline__ void barrier_only() {
   asm volatile("" ::: "memory");
 }
 
-// Run-time work queue (the list-scheduling form of LPT): one thread of a workgroup takes
-// the next position with a device-scope atomic add; the last workgroup to finish returns the
-// queue's two counters (next position, finished workgroups) to zero for the next launch.
-__device__ __forceinline__ int queue_take(int32_t* ctr) {
-  return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Run-time work queue (the list-scheduling form of LPT).  The queue holds the items in LPT
+// order; its positions are dealt to the 8 XCDs in turn (position i belongs to XCD i mod 8, as
+// workgroup b runs on XCD b mod 8), one counter per XCD.  One thread of a workgroup takes its
+// XCD's next position with a device-scope atomic add, so the items that share a head's K/V
+// in one LPT round stay on one XCD's L2; once its XCD's positions are all taken it takes
+// another XCD's next one.  Every position below n is returned exactly once (each comes from
+// one counter value), n means the queue is empty.  The last workgroup to finish returns the
+// counters (ctr[0..7] next positions, ctr[8] finished workgroups) to zero for the next launch.
+__device__ __forceinline__ int queue_take(int32_t* ctr, int n) {
+  const int home = blockIdx.x & 7;
+  const int c = __hip_atomic_fetch_add(ctr + home, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (c * 8 + home < n) return c * 8 + home;
+  for (int k = 1; k < 8; ++k) {
+    const int x = (home + k) & 7;
+    // (a counter only grows: one read as exhausted stays exhausted)
+    if (__hip_atomic_load(ctr + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * 8 + x >= n) continue;
+    const int cx = __hip_atomic_fetch_add(ctr + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (cx * 8 + x < n) return cx * 8 + x;
+  }
+  return n;
 }
 __device__ __forceinline__ void queue_finish(int32_t* ctr) {
-  if (__hip_atomic_fetch_add(ctr + 1, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
-    __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__hip_atomic_fetch_add(ctr + 8, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+#pragma unroll
+    for (int x = 0; x < 9; ++x) __hip_atomic_store(ctr + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -860,7 +875,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
   int pos = 0, p_end = 0, next_pos = 0;
   if (dyn) {
     p_end = a.bin_ptr[a.num_bins];
-    if (tid == 0) sQueuePos = queue_take(a.dyn_ctr);
+    if (tid == 0) sQueuePos = queue_take(a.dyn_ctr, p_end);
     __syncthreads();
     pos = __builtin_amdgcn_readfirstlane(sQueuePos);
   } else {
@@ -1067,7 +1082,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
       __syncthreads();
       // (thread 0) the position of the workgroup's next item, taken from the run-time queue
       // here, right after a wait for every load in flight: the next such wait is a tile away
-      if (dyn && t == 0 && tid == 0) next_pos = queue_take(a.dyn_ctr);
+      if (dyn && t == 0 && tid == 0) next_pos = queue_take(a.dyn_ctr, p_end);
       bool fresh = t == 0;  // block 0 of this tile opens an accumulation
       if (!full && cur_chunk < chunk_of(desc)) {
         while (cur_chunk < chunk_of(desc)) flush_chunk(cur_chunk++, (float*)kfree, (float*)vfree);
@@ -1222,7 +1237,7 @@ void attn_bf16_pipe_kernel(FwdArgs a) {
     }
     if (dyn) {
       if (tid == 0) {
-        if (n_tiles == 0) next_pos = queue_take(a.dyn_ctr);  // (else taken during the first tile)
+        if (n_tiles == 0) next_pos = queue_take(a.dyn_ctr, p_end);  // (else taken during the first tile)
         sQueuePos = next_pos;
       }
       __syncthreads();  // (every wave read the previous position before this item's barriers)
@@ -1297,7 +1312,7 @@ void attn_bf16_pair_kernel(FwdArgs a) {
   int pos = 0, p_end = 0, next_pos = 0;
   if (dyn) {
     p_end = a.bin_ptr[a.num_bins];
-    if (tid == 0) sQueuePos = queue_take(a.dyn_ctr);
+    if (tid == 0) sQueuePos = queue_take(a.dyn_ctr, p_end);
     __syncthreads();
     pos = __builtin_amdgcn_readfirstlane(sQueuePos);
   } else {
@@ -1500,7 +1515,7 @@ void attn_bf16_pair_kernel(FwdArgs a) {
         __syncthreads();
         // (thread 0) the position of the workgroup's next item, taken from the run-time queue
         // here, right after a wait for every load in flight: the next such wait is a tile away
-        if (dyn && t == 0 && tid == 0) next_pos = queue_take(a.dyn_ctr);
+        if (dyn && t == 0 && tid == 0) next_pos = queue_take(a.dyn_ctr, p_end);
       } else {
         barrier_only();
       }
@@ -1668,7 +1683,7 @@ void attn_bf16_pair_kernel(FwdArgs a) {
     }
     if (dyn) {
       if (tid == 0) {
-        if (n_tiles == 0) next_pos = queue_take(a.dyn_ctr);  // (else taken during the first tile)
+        if (n_tiles == 0) next_pos = queue_take(a.dyn_ctr, p_end);  // (else taken during the first tile)
         sQueuePos = next_pos;
       }
       __syncthreads();  // (every wave read the previous position before this item's barriers)

@@ -67,6 +67,8 @@ struct GatherArgs {
 constexpr int kIndexerMaxTopK = 512;
 // Keys per group of the indexer's prefix moments, and floats per moment entry (rank 32: the
 // sum of K' and the sum of K' K'^T).
+// counters per list of the run-time queue: one next position per XCD, finished workgroups
+constexpr int kQueueCtrs = 16;
 constexpr int kMomGroup = 128;
 constexpr int kMomEntry = 32 + 32 * 32;
 
@@ -105,8 +107,8 @@ hipError_t launch_popcount(const uint8_t* mask, int BH, int nQ, int nK, int n_ch
 // from chunk c of crow.  Lists [list0, list0 + n_lists) are made (n_lists < 0: through list
 // C), list list0 + s written to slot s of items [.][BH*nQ], bin_ptr [.][m+1], bin_load [.][m]
 // and stats [.][4] = (load sum, max item load, makespan, lower bound).
-// order (nullable): each list's items in LPT order; dyn_ctr (nullable): two counters per list,
-// zeroed (the run-time queue of SA_ORDER_LPT_DYNAMIC)
+// order (nullable): each list's items in LPT order; dyn_ctr (nullable): kQueueCtrs counters
+// per list, zeroed (the run-time queue of SA_ORDER_LPT_DYNAMIC)
 hipError_t launch_plan_rounds(const int32_t* row, const int32_t* crow, int BH, int nQ, int C, int m, int32_t* items,
                               int32_t* bin_ptr, int64_t* bin_load, int64_t* stats, hipStream_t stream,
                               int list0 = 0, int n_lists = -1, int32_t* order = nullptr,

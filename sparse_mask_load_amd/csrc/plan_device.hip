@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void plan_rounds_kernel(const int32_t* __
   // the queue of the run-time order: the items in LPT order, and its counters at zero
   if (order)
     for (int p = tid; p < n; p += kThreads) order[(int64_t)slot * n + p] = (int32_t)(key[p] & ((1u << kIdBits) - 1));
-  if (dyn_ctr && tid < 2) dyn_ctr[2 * slot + tid] = 0;
+  if (dyn_ctr && tid < kQueueCtrs) dyn_ctr[kQueueCtrs * slot + tid] = 0;
 
   // 2. rounds; thread t holds one bin key (load << 16 | bin), sentinels beyond m
   uint64_t bkey = tid < m ? (uint64_t)tid : ~0ull;
