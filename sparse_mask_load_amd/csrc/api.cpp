@@ -65,6 +65,7 @@ struct sa_plan {
   std::vector<std::pair<void*, size_t>> allocs;
   // one event per stream that ran a forward call with the plan, re-recorded after each call
   std::mutex use_mutex;
+  std::mutex queue_mutex;  // SA_ORDER_LPT_DYNAMIC: held by a forward call from its waits to its use record
   std::vector<std::pair<hipStream_t, hipEvent_t>> uses;
 };
 
@@ -561,9 +562,13 @@ sa_status sparse_attn_fwd(const sa_plan* P, const void* q, const void* k, const 
   a.mask = P->d_mask;
   a.items = P->d_items + (size_t)list * P->n_items;
   a.bin_ptr = P->d_bin_ptr + (size_t)list * (P->num_bins + 1);
+  std::unique_lock<std::mutex> queue_lock;
   if (P->order == SA_ORDER_LPT_DYNAMIC) {
     // the queue's counters are shared by every call with this plan: calls on other streams
-    // finish first (a call on this stream follows the previous one anyway)
+    // finish first (a call on this stream follows the previous one anyway).  The queue lock is
+    // held until this call's use is recorded, so that two host threads cannot both launch
+    // before either has recorded its use
+    queue_lock = std::unique_lock<std::mutex>(const_cast<sa_plan*>(P)->queue_mutex);
     std::lock_guard<std::mutex> lock(const_cast<sa_plan*>(P)->use_mutex);
     for (const auto& u : P->uses)
       if (u.first != stream) SA_HIP(hipStreamWaitEvent(stream, u.second, 0));

@@ -7,6 +7,8 @@ the queue must give the same output bits as the device planner's static lists: a
 computed the same way whichever workgroup takes it.  Launches are repeated, since each one's
 last workgroup returns the queue's counters to zero for the next.
 """
+import threading
+
 import numpy as np
 import pytest
 import torch
@@ -103,5 +105,41 @@ def test_dynamic_queue_causal_workload(q_pairs):
         assert torch.equal(G.run_full(plan_d, q, k, v), o_ref), f"full mode, launch {rep}"
         for got, ref in zip(G.run_partial(plan_d, q, k, v, 0, w.n_chunks), part_ref):
             assert torch.equal(got, ref), f"partial mode, launch {rep}"
+    plan_s.close()
+    plan_d.close()
+
+
+def test_dynamic_queue_two_host_threads():
+    """Forward calls on one run-time-order plan from two host threads, each on a stream of its
+    own, share the queue's counters, so the library runs them one after another: every output
+    equals the static order's bit for bit."""
+    w = W.make_custom(1, 4, 2048, 128, block=128, n_chunks=4, dtype="bf16", pattern="causal", density=0.0,
+                      seed=790)
+    q, k, v = G.upload(w)
+    plan_s = G.plan_block(w, q, order="lpt_device", q_pairs=True)
+    plan_d = G.plan_block(w, q, order="lpt_dynamic", q_pairs=True)
+    o_ref = G.run_full(plan_s, q, k, v)
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs = [[G.empty_like_qkv(q) for _ in range(8)] for _ in range(2)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            for o in outs[i]:
+                bd.sparse_attn_fwd(plan_d, q, k, v, o=o, stream=streams[i])
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        for j, o in enumerate(outs[i]):
+            assert torch.equal(o, o_ref), f"thread {i}, call {j}"
     plan_s.close()
     plan_d.close()
